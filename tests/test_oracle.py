@@ -1,0 +1,346 @@
+"""Pins for the float64 oracle: checks against things other than itself.
+
+Each test fixes the oracle to something the pages or the mathematics fix:
+brute force with a materialised mask (tests/bruteforce.py), torch's float64
+scaled_dot_product_attention as a library routine, closed forms (running
+means), invariants (row sums, isolation of requests and heads, chunked equals
+one-shot, decode row equals prefill row) and the cache-size figures the pages
+print (tests/golden/pages_worked_examples.json).  A dropped term, a wrong sign,
+a transposed operand or a shifted index in oracle.c fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from prefill_self_attention_amd import inputs as I
+from tests import bruteforce as BF
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "pages_worked_examples.json")))
+
+
+def bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def rand_varlen(lengths, H, D, seed):
+    w = I.Varlen("t", lengths, H, D, seed=seed)
+    q, k, v = w.tensors()
+    return w, bits(q), bits(k), bits(v)
+
+
+def f64(b):
+    return BF.bf16_to_f64(b)
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("lengths,H,D,seed", [
+    ([3], 4, 32, 11),            # toy: 3 tokens, 4 heads, head_dim 32
+    ([64], 4, 32, 1),            # single T=64 workload
+    ([5, 2, 3], 2, 32, 12),      # cu_seqlens [0,5,7,10]
+    ([1, 17, 0, 40], 3, 64, 13),  # includes an empty sequence
+])
+def test_matches_bruteforce(lengths, H, D, seed):
+    w, q, k, v = rand_varlen(lengths, H, D, seed)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    ref = BF.varlen(q, k, v, w.cu_seqlens, w.scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_matches_torch_sdpa_float64():
+    """A library routine: torch's float64 CPU attention with is_causal."""
+    w, q, k, v = rand_varlen([96], 4, 128, 21)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    Q = torch.from_numpy(f64(q)).permute(1, 0, 2)
+    K = torch.from_numpy(f64(k)).permute(1, 0, 2)
+    V = torch.from_numpy(f64(v)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, is_causal=True, scale=w.scale).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_chunked_matches_torch_sdpa_with_prefix_mask():
+    """Bottom-right alignment: query i at absolute prefix+i sees keys 0..prefix+i."""
+    H, D, pre, n, cap = 2, 64, 37, 20, 64
+    g = I.generator(31)
+    q = I.randn_bf16(g, (n, H, D))
+    k = I.randn_bf16(g, (n, H, D))
+    v = I.randn_bf16(g, (n, H, D))
+    kc = I.randn_bf16(g, (1, H, cap, D))
+    vc = I.randn_bf16(g, (1, H, cap, D))
+    scale = I.default_scale(D)
+    out, kimg, vimg, _ = oracle.prefill_chunked(bits(q), bits(k), bits(v), [0, n], [pre],
+                                                bits(kc), bits(vc), scale)
+    Kall = torch.cat([kc[0, :, :pre].double(), k.double().permute(1, 0, 2)], dim=1)
+    Vall = torch.cat([vc[0, :, :pre].double(), v.double().permute(1, 0, 2)], dim=1)
+    mask = torch.arange(pre + n)[None, :] <= (pre + torch.arange(n))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.double().permute(1, 0, 2), Kall, Vall, attn_mask=mask, scale=scale)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+    # own K/V appended at prefix..prefix+n-1, nothing else touched
+    np.testing.assert_array_equal(kimg[0, :, pre:pre + n], bits(k).transpose(1, 0, 2))
+    np.testing.assert_array_equal(vimg[0, :, pre:pre + n], bits(v).transpose(1, 0, 2))
+    np.testing.assert_array_equal(kimg[0, :, :pre], bits(kc)[0, :, :pre])
+    np.testing.assert_array_equal(kimg[0, :, pre + n:], bits(kc)[0, :, pre + n:])
+    np.testing.assert_array_equal(vimg[0, :, pre + n:], bits(vc)[0, :, pre + n:])
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_first_row_and_length_one_return_own_v_exactly():
+    w, q, k, v = rand_varlen([1, 9, 1, 33], 4, 32, 41)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    for b in range(len(w.lengths)):
+        s = w.cu_seqlens[b]
+        np.testing.assert_array_equal(out[s], f64(v)[s])
+
+
+def test_v_ones_gives_ones_and_rows_sum_to_one():
+    w, q, k, v = rand_varlen([50], 3, 32, 42)
+    ones = bits(torch.ones(50, 3, 32, dtype=torch.bfloat16))
+    out, _, _, probs = oracle.prefill_varlen(q, k, ones, w.cu_seqlens, w.scale, want_probs=True)
+    np.testing.assert_array_equal(out, np.ones_like(out))
+    np.testing.assert_allclose(probs.sum(axis=2), 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", ["identical_keys", "zero_scale"])
+def test_running_mean_closed_form(mode):
+    """All scores of a row equal -> weights uniform over keys 0..i -> causal running mean of V."""
+    w, q, k, v = rand_varlen([7, 60], 2, 64, 43)
+    scale = w.scale
+    if mode == "identical_keys":
+        k = np.broadcast_to(k[:1], k.shape).copy()  # one key for every position
+        for b in range(2):
+            s = w.cu_seqlens[b]
+            k[s:w.cu_seqlens[b + 1]] = k[s]
+    else:
+        scale = 0.0
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, scale)
+    V = f64(v)
+    for b in range(2):
+        s, e = w.cu_seqlens[b], w.cu_seqlens[b + 1]
+        mean = np.cumsum(V[s:e], axis=0) / np.arange(1, e - s + 1)[:, None, None]
+        np.testing.assert_allclose(out[s:e], mean, rtol=1e-13, atol=1e-14)
+
+
+def test_chunked_running_mean_counts_prefix():
+    """scale 0 in a chunk with prefix p: out_i = mean of prefix V and own V_0..i."""
+    H, D, pre, n, cap = 2, 32, 10, 6, 16
+    g = I.generator(44)
+    q, k, v = (I.randn_bf16(g, (n, H, D)) for _ in range(3))
+    kc = I.randn_bf16(g, (1, H, cap, D))
+    vc = I.randn_bf16(g, (1, H, cap, D))
+    out, _, _, _ = oracle.prefill_chunked(bits(q), bits(k), bits(v), [0, n], [pre],
+                                          bits(kc), bits(vc), 0.0)
+    Vall = np.concatenate([f64(bits(vc))[0, :, :pre], f64(bits(v)).transpose(1, 0, 2)], axis=1)
+    for i in range(n):
+        np.testing.assert_allclose(out[i], Vall[:, :pre + i + 1].mean(axis=1),
+                                   rtol=1e-13, atol=1e-14)
+
+
+def test_one_hot_v_exposes_probabilities():
+    """V[j] = e_j (T <= D): out[i, j] = P[i, j]; zero above the diagonal, rows sum to 1."""
+    T, H, D = 24, 2, 32
+    w, q, k, _ = rand_varlen([T], H, D, 45)
+    eye = np.zeros((T, H, D), dtype=np.float32)
+    for j in range(T):
+        eye[j, :, j] = 1.0
+    v = bits(torch.from_numpy(eye).to(torch.bfloat16))
+    out, _, _, probs = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale, want_probs=True)
+    for h in range(H):
+        P = out[:, h, :T]
+        assert np.all(np.triu(P, 1) == 0.0)
+        np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-14)
+        _, pref = BF.attention_one(f64(q)[:, h], f64(k)[:, h], f64(v)[:, h], w.scale)
+        np.testing.assert_allclose(P, pref, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(probs[h], pref, rtol=1e-12, atol=1e-15)
+
+
+def test_two_keys_logistic_form():
+    """Row 1 of a 2-token sequence: weight on key 1 is the logistic of the score gap."""
+    w, q, k, v = rand_varlen([2], 1, 32, 46)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    Q, K, V = f64(q)[:, 0], f64(k)[:, 0], f64(v)[:, 0]
+    gap = w.scale * (float(np.dot(Q[1], K[1])) - float(np.dot(Q[1], K[0])))
+    a = 1.0 / (1.0 + np.exp(-gap))
+    np.testing.assert_allclose(out[1, 0], (1 - a) * V[0] + a * V[1], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_varlen_equals_separate_runs_exactly():
+    w, q, k, v = rand_varlen([5, 2, 3], 4, 32, 47)
+    assert w.cu_seqlens == GOLDEN["varlen_metadata"]["cu_seqlens"]
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    for b in range(3):
+        s, e = w.cu_seqlens[b], w.cu_seqlens[b + 1]
+        sep, _, _, _ = oracle.prefill_varlen(q[s:e], k[s:e], v[s:e], [0, e - s], w.scale)
+        np.testing.assert_array_equal(out[s:e], sep)
+
+
+def test_requests_and_heads_do_not_interfere():
+    w, q, k, v = rand_varlen([12, 20], 3, 32, 48)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    k2 = k.copy()
+    k2[12:, 1] ^= 0x0101  # perturb sequence 1, head 1
+    out2, _, _, _ = oracle.prefill_varlen(q, k2, v, w.cu_seqlens, w.scale)
+    np.testing.assert_array_equal(out2[:12], out[:12])
+    np.testing.assert_array_equal(out2[12:, 0], out[12:, 0])
+    np.testing.assert_array_equal(out2[12:, 2], out[12:, 2])
+    assert not np.array_equal(out2[13:, 1], out[13:, 1])
+
+
+def test_chunked_equals_one_shot():
+    """A prompt processed in chunks through the cache reproduces the one-shot call."""
+    T, C, H, D = 96, 32, 2, 32
+    w, q, k, v = rand_varlen([T], H, D, 49)
+    one, kimg1, vimg1, _ = oracle.prefill_varlen(
+        q, k, v, w.cu_seqlens, w.scale,
+        k_cache=np.zeros(T * H * D, np.uint16), v_cache=np.zeros(T * H * D, np.uint16))
+    kc = np.zeros((1, H, T, D), np.uint16)
+    vc = np.zeros((1, H, T, D), np.uint16)
+    outs = []
+    for c in range(T // C):
+        sl = slice(c * C, (c + 1) * C)
+        o, kc, vc, _ = oracle.prefill_chunked(q[sl], k[sl], v[sl], [0, C], [c * C], kc, vc, w.scale)
+        outs.append(o)
+    np.testing.assert_allclose(np.concatenate(outs), one, rtol=1e-12, atol=1e-14)
+    # [1, H, cap=T, D] chunked layout is byte-identical to the varlen [H, T, D] block
+    np.testing.assert_array_equal(kc.reshape(-1), kimg1)
+    np.testing.assert_array_equal(vc.reshape(-1), vimg1)
+
+
+def test_decode_row_equals_prefill_row():
+    """A length-1 row with prefix p equals row p of a prefill over the same p+1 tokens."""
+    p, H, D = 30, 2, 32
+    w, q, k, v = rand_varlen([p + 1], H, D, 50)
+    one, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    kc = np.zeros((1, H, p + 8, D), np.uint16)
+    vc = np.zeros((1, H, p + 8, D), np.uint16)
+    kc[0, :, :p] = k[:p].transpose(1, 0, 2)
+    vc[0, :, :p] = v[:p].transpose(1, 0, 2)
+    o, kimg, vimg, _ = oracle.prefill_chunked(q[p:], k[p:], v[p:], [0, 1], [p], kc, vc, w.scale)
+    np.testing.assert_allclose(o[0], one[p], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(kimg[0, :, p], k[p])
+    np.testing.assert_array_equal(vimg[0, :, p], v[p])
+
+
+def test_sampled_rows_equal_full_run():
+    w, q, k, v = rand_varlen([33, 1, 70], 2, 64, 51)
+    out, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    rows = [0, 32, 33, 34, 60, 103]
+    sub = oracle.prefill_rows(q, k, v, w.cu_seqlens, w.scale, rows)
+    np.testing.assert_array_equal(sub, out[rows])
+
+
+def test_sampled_rows_chunked_equal_full_run():
+    H, D, cap = 2, 32, 40
+    g = I.generator(52)
+    n = [5, 1, 1]
+    pre = [12, 30, 0]
+    N = sum(n)
+    q, k, v = (I.randn_bf16(g, (N, H, D)) for _ in range(3))
+    kc = I.randn_bf16(g, (3, H, cap, D))
+    vc = I.randn_bf16(g, (3, H, cap, D))
+    cu = I.cu_from_lengths(n)
+    out, _, _, _ = oracle.prefill_chunked(bits(q), bits(k), bits(v), cu, pre, bits(kc), bits(vc), 0.3)
+    sub = oracle.prefill_rows(bits(q), bits(k), bits(v), cu, 0.3, list(range(N)),
+                              prefix_lens=pre, k_cache=bits(kc), v_cache=bits(vc))
+    np.testing.assert_array_equal(sub, out)
+
+
+def test_thread_count_does_not_change_result():
+    w, q, k, v = rand_varlen([40, 23], 4, 32, 53)
+    a, _, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    b = np.zeros_like(a)
+    for h in range(4):  # one head at a time: a different work split
+        bh, _, _, _ = oracle.prefill_varlen(q[:, h:h + 1].copy(), k[:, h:h + 1].copy(),
+                                            v[:, h:h + 1].copy(), w.cu_seqlens, w.scale)
+        b[:, h] = bh[:, 0]
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rejects_bad_metadata():
+    w, q, k, v = rand_varlen([4, 4], 1, 32, 54)
+    with pytest.raises(ValueError):
+        oracle.prefill_varlen(q, k, v, [0, 5, 3, 8], w.scale)  # cu not monotonic
+    with pytest.raises(ValueError):
+        oracle.prefill_chunked(q, k, v, [0, 4, 8], [0, 6], np.zeros((2, 1, 8, 32), np.uint16),
+                               np.zeros((2, 1, 8, 32), np.uint16), w.scale)  # 6 + 4 > cap 8
+
+
+# ---------------------------------------------------------------- the pages' figures
+
+def test_cache_bytes_match_pages_T512():
+    """Per-layer K+V bytes for 32 heads x 512 tokens x 128 in bf16 (printed on the pages)."""
+    fx = GOLDEN["kv_bytes_per_layer_T512"]
+    T, H, D = fx["seq_len"], fx["num_heads"], fx["head_dim"]
+    w, q, k, v = rand_varlen([T], H, D, 55)
+    sentinel = np.full(T * H * D + 64, 0x7FC1, np.uint16)  # bf16 NaN pattern, extra guard
+    _, kimg, vimg, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale,
+                                             k_cache=sentinel, v_cache=sentinel)
+    written = (np.count_nonzero(kimg != sentinel) + np.count_nonzero(vimg != sentinel))
+    # every element of k/v is copied once; N(0,1) bf16 never equals the sentinel bits
+    assert written * fx["bytes_per_element"] == fx["bytes"]
+    assert np.all(kimg[T * H * D:] == 0x7FC1)
+    # head-major: element (h, t, d) of the image is k[t, h, d]
+    np.testing.assert_array_equal(kimg[:T * H * D].reshape(H, T, D), k.transpose(1, 0, 2))
+
+
+def test_cache_bytes_closed_forms_from_pages():
+    fx = GOLDEN["kv_bytes_per_layer_T4096"]
+    b = 2 * fx["num_heads"] * fx["seq_len"] * fx["head_dim"] * fx["bytes_per_element"]
+    assert b == fx["approx_mib"] * 2 ** 20
+    fx = GOLDEN["kv_bytes_per_token_model"]
+    per_layer = 2 * fx["num_heads"] * fx["head_dim"] * fx["bytes_per_element"]
+    assert per_layer * fx["num_layers"] == fx["bytes"]
+    assert per_layer == 16384
+    fx = GOLDEN["score_matrix_bytes_T8192"]
+    assert fx["seq_len"] ** 2 * fx["bytes_per_element"] == fx["approx_mib"] * 2 ** 20
+
+
+def test_toy_shapes_from_pages():
+    """3 tokens, 4 heads of 32: the layer's K cache is [4, 3, 32]; decode grows it to 4."""
+    fx = GOLDEN["toy_prefill_shapes"]
+    T, H, D = fx["tokens"], fx["num_heads"], fx["head_dim"]
+    assert H * D == fx["hidden"]
+    w, q, k, v = rand_varlen([T], H, D, 56)
+    _, kimg, _, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale,
+                                          k_cache=np.zeros(T * H * D, np.uint16),
+                                          v_cache=np.zeros(T * H * D, np.uint16))
+    assert list(kimg.reshape(H, T, D).shape) == fx["k_cache_layer_shape"]
+    dg = GOLDEN["toy_decode_growth"]
+    kc = np.zeros((1, H, dg["cache_len_after"], D), np.uint16)
+    vc = np.zeros_like(kc)
+    kc[0, :, :T] = k.transpose(1, 0, 2)
+    vc[0, :, :T] = v.transpose(1, 0, 2)
+    g = I.generator(57)
+    nq, nk, nv = (bits(I.randn_bf16(g, (1, H, D))) for _ in range(3))
+    _, _, _, probs = oracle.prefill_chunked(nq, nk, nv, [0, 1], [dg["cache_len_before"]],
+                                            kc, vc, w.scale, want_probs=True)
+    assert probs.shape == (H, 1, dg["cache_len_after"])  # scores over 3 cached + itself
+
+
+def test_decode_token_sees_prefix_and_itself():
+    fx = GOLDEN["decode_visible_positions"]
+    p, H, D = fx["prompt_tokens"], 1, 32
+    g = I.generator(58)
+    kc = bits(I.randn_bf16(g, (1, H, p + 1, D)))
+    vc = bits(I.randn_bf16(g, (1, H, p + 1, D)))
+    q, k, v = (bits(I.randn_bf16(g, (1, H, D))) for _ in range(3))
+    _, _, _, probs = oracle.prefill_chunked(q, k, v, [0, 1], [p], kc, vc, 0.2, want_probs=True)
+    assert probs.shape[2] == fx["positions_attended_by_next_token"]
+    assert np.all(probs > 0)
+
+
+def test_causal_pair_count():
+    """Non-zero weights of a T-token row block = T(T+1)/2 causal pairs (half the full square)."""
+    T = 48
+    w, q, k, v = rand_varlen([T], 1, 32, 59)
+    _, _, _, probs = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale, want_probs=True)
+    assert np.count_nonzero(probs) == T * (T + 1) // 2
