@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark: causal prefill attention + KV-cache write on one MI355X.
+
+One step = one call of prefill_attn_varlen (C ABI, one fused kernel launch)
+over the Llama-2-7B-shaped layer: one sequence of T=2048 tokens, 32 heads x
+128, bf16 q/k/v ~ N(0,1) from a seed, scale 1/sqrt(128), K/V cache
+[1, 32, 2048, 128] written in the same launch.  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
+
+  value     = algorithmic FLOPs per step / mean step time (TFLOP/s); the
+              algorithmic FLOPs count 4*D per causal (query, key) pair per head
+              (QK^T and PV, 2*D each), the masked half excluded.
+  roofline  = the same FLOPs / the mean kernel duration from HIP events on the
+              launch stream, against the dense bf16 MFMA peak (2.5 PFLOP/s);
+              traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE and
+              WRITE_SIZE counters (profiles/), scaled by a copy-kernel
+              calibration, or null if the kernel source changed since.
+  cpu_baseline = the float64 oracle on the host cores over the same workload.
+
+Options: --gpus N (only 1 is supported: the path runs on one GPU),
+--steps K, --warmup W, --workload NAME, --no-cpu-baseline, --copy-calib
+(runs only a 1 GiB device copy, for the counter calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "prefill_self_attention_amd", "csrc", "prefill_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_fwd_T2048_H32_D128.txt")
+METRIC = "prefill attention TFLOP/s + % bf16 MFMA peak (T=2048,H=32,D=128); KV GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="single_T2048_H32_D128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    return ap.parse_args()
+
+
+def causal_pairs(lengths, prefixes=None):
+    prefixes = prefixes or [0] * len(lengths)
+    return sum(n * p + n * (n + 1) // 2 for n, p in zip(lengths, prefixes))
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256") != kernel_sha():
+        return None, "kernel changed since the counters were taken"
+    try:
+        f = float(kv["fetch_kib_per_dispatch"]) * float(kv["copy_fetch_factor"])
+        w = float(kv["write_kib_per_dispatch"]) * float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None, "incomplete counter summary"
+    return (f + w) * 1024.0, "ok"
+
+
+def copy_calib():
+    import torch
+    n = 1 << 29  # 2^29 bf16 = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_each_way": 2 * n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, q, k, v, flops):
+    """Time the float64 oracle on the host cores over the same workload."""
+    import oracle
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "the whole workload (%d tokens x %d heads x %d), float64, one run"
+                      % (w.num_tokens, w.num_heads, w.head_dim)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (no sharding or collectives); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calib:
+        copy_calib()
+        return
+
+    import prefill_self_attention_amd as P
+    from prefill_self_attention_amd import inputs as I
+    P.load()
+
+    w = I.workload(args.workload)
+    if not isinstance(w, I.Varlen):
+        raise SystemExit("bench.py times varlen workloads; chunked steps are covered by tests")
+    q, k, v = w.tensors()
+    N, H, D = q.shape
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    kc = torch.empty_like(qd)
+    vc = torch.empty_like(qd)
+    max_seqlen = w.max_seqlen
+    torch.cuda.synchronize()
+
+    pairs = causal_pairs(w.lengths)
+    flops = 4.0 * D * H * pairs
+    kv_bytes = 2.0 * N * H * D * 2
+    alg_bytes = 6.0 * N * H * D * 2  # read q, k, v; write out, k_cache, v_cache
+
+    def step():
+        P.prefill_attn_varlen(qd, kd, vd, cu, kc, vc, out, scale=w.scale, max_seqlen=max_seqlen)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = total_ms / args.steps
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    traffic, traffic_note = read_traffic() if args.workload == "single_T2048_H32_D128" else (None, "n/a")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_lens": w.lengths if len(w.lengths) <= 8 else
+                   "%d sequences" % len(w.lengths), "tokens": N, "num_heads": H, "head_dim": D,
+                   "causal": True, "kv_cache_write": True, "scale": w.scale},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kv_write_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "algorithmic_hbm_gbps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "launch_us": {"mean": round(mean_launch_ms * 1e3, 2),
+                      "median": round(launch_ms[len(launch_ms) // 2] * 1e3, 2),
+                      "p99": round(launch_ms[min(len(launch_ms) - 1,
+                                                 int(math.ceil(0.99 * len(launch_ms))) - 1)] * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, flops)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+/*
+ * prefill_attn.h -- C ABI of the MI355X (gfx950) prefill-attention library.
+ *
+ * One call computes causal scaled-dot-product self-attention over a batch of
+ * variable-length prompts flattened into one token stream and, in the same
+ * launch, writes every new token's K and V into a head-major KV cache.
+ *
+ * Sources (the pages that define the operation):
+ *   [P1] "Prefill不是热身：大模型推理的真正瓶颈与优化核心" (www.mhpn.cn/news/2373630)
+ *   [P2] "大模型推理优化：Prefill、Decode与KV Cache的工程实践" (www.zskr.cn/news/2334369)
+ *   [P3] "大模型 Prompt Prefill 阶段的高效 Batching 与算子排布" (www.nxmr.cn/news/92962)
+ *   [P4] "大语言模型推理核心：Prefill与Decode原理及工程优化" (www.yfxerp.com/news/184489)
+ *   [P5] untitled page at www.zwxr.cn/news/300951
+ *
+ * Common conventions
+ *   - bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+ *   - q, k, v, out: [N, H, D] contiguous, token-major, N = cu_seqlens[B].  The
+ *     flattened [total_tokens, hidden] stream with hidden = H * D [P3 §2].
+ *   - cu_seqlens: int32 [B + 1] in DEVICE memory, cu[0] = 0, non-decreasing;
+ *     sequence b owns tokens cu[b] .. cu[b+1]-1 [P3 figure and §2].
+ *   - Attention of sequence b, head h, query i (absolute position p_b + i,
+ *     p_b = 0 for varlen):  out = sum_{j <= p_b + i} softmax_j(scale q.k_j) v_j
+ *     over keys of sequence b only [P1 §3 and P4 §2.2 formula; P5 §1.1 causal
+ *     visibility; P3 §2 no attention across requests].
+ *   - head_dim D in {32, 64, 128}.  scale: any finite float (0 allowed); the
+ *     usual value is 1/sqrt(D).
+ *   - All pointers are caller-owned device memory aligned to 16 bytes.  The
+ *     library keeps no pointer after returning, allocates no memory, creates
+ *     no stream and never synchronises the device (except in check mode,
+ *     below).  Work is enqueued on `stream` (NULL = default stream); inputs
+ *     must stay valid until it completes.  Calls are re-entrant.
+ *   - Outputs (out, k_cache, v_cache) must not overlap q, k, v, cu_seqlens,
+ *     prefix_lens or each other.
+ *   - Errors detectable on the host are reported before anything is enqueued
+ *     and leave every buffer untouched.  B == 0 or max_seqlen == 0 enqueues
+ *     nothing and returns PA_OK.  Device faults surface at the caller's next
+ *     synchronisation, as for any HIP launch.
+ *   - Device-resident metadata (cu_seqlens, prefix_lens) is trusted in the
+ *     default mode: a violated precondition (non-monotonic cu_seqlens, a
+ *     length above max_seqlen, prefix + length above the cache capacity) is
+ *     undefined behaviour.  In check mode (pa_set_check_mode(1) or the
+ *     environment variable PA_CHECK=1 at load time) the library copies the
+ *     metadata to the host on `stream`, waits for it, and returns
+ *     PA_ERR_SEQLENS / PA_ERR_CAPACITY instead of launching.
+ */
+#ifndef PREFILL_ATTN_H
+#define PREFILL_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,      /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,     /* num_seqs < 0, num_heads < 1, max_seqlen < 0, cache_capacity < 1, or a grid limit exceeded */
+    PA_ERR_HEAD_DIM = 3,  /* head_dim not in {32, 64, 128} */
+    PA_ERR_SCALE = 4,     /* scale is NaN or infinite */
+    PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
+    PA_ERR_ALIAS = 6,     /* an output pointer equals an input or another output pointer */
+    PA_ERR_SEQLENS = 7,   /* check mode: cu_seqlens[0] != 0, decreasing, or a length > max_seqlen */
+    PA_ERR_CAPACITY = 8,  /* check mode: a prefix length < 0 or prefix + length > cache_capacity */
+    PA_ERR_HIP = 9        /* a HIP runtime call failed; see pa_last_hip_error() */
+} pa_status;
+
+/*
+ * Varlen causal prefill with KV-cache write.
+ *
+ *   q, k, v      bf16 [N, H, D] device, read only.
+ *   cu_seqlens   int32 [num_seqs + 1] device.
+ *   num_seqs     B >= 0 (host).
+ *   max_seqlen   host upper bound on every cu[b+1] - cu[b]; sizes the grid.
+ *   num_heads    H >= 1; head_dim D in {32, 64, 128}.
+ *   k_cache,     bf16 device, written only: sequence b's cache block is
+ *   v_cache      [H, len_b, D] starting at element cu[b] * H * D, so the
+ *                buffers hold N * H * D elements in total.  This is the
+ *                per-layer cache layout [batch, heads, seq, head_dim] of
+ *                [P2 §1.3] and [P4 §3.2], head-major as [P1 §3] advises,
+ *                with one sequence per batch entry packed back to back.
+ *                Prefill produces K and V of every prompt position
+ *                [P5 §1.1]; Q is not cached [P2 §1.3].
+ *   out          bf16 [N, H, D] device, written only (rounded to nearest even).
+ *   scale        softmax scale applied to q.k.
+ *   stream       HIP stream (NULL = default stream).
+ */
+pa_status prefill_attn_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *cu_seqlens, int32_t num_seqs,
+                              int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                              uint16_t *k_cache, uint16_t *v_cache, uint16_t *out,
+                              float scale, hipStream_t stream);
+
+/*
+ * Chunked prefill: each sequence already has prefix_lens[b] tokens in the
+ * cache, and its new tokens (a prompt chunk, or a single decode token) attend
+ * to that cached prefix and causally to each other [P3 §3 chunked prefill
+ * co-scheduled with decode; P2 §2.2; P5 §1.2: the decoded token attends to
+ * every cached position and to itself].  Query i of sequence b sits at
+ * absolute position prefix_lens[b] + i and sees keys 0 .. prefix_lens[b] + i.
+ *
+ *   q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, out,
+ *   scale, stream      as for prefill_attn_varlen (new tokens only).
+ *   k_cache, v_cache   bf16 [num_seqs, H, cache_capacity, D] device.  Positions
+ *                      0 .. prefix_lens[b]-1 of sequence b are read; the new
+ *                      tokens' K/V are written at positions prefix_lens[b] ..
+ *                      prefix_lens[b] + len_b - 1; nothing else is touched.
+ *                      With B = 1, prefix 0 and capacity = len, this layout is
+ *                      byte-identical to the varlen cache block.
+ *   cache_capacity     positions per (sequence, head) in the cache, >= 1.
+ *   prefix_lens        int32 [num_seqs] device, 0 <= prefix_lens[b] and
+ *                      prefix_lens[b] + len_b <= cache_capacity.
+ *
+ * The new tokens' own K/V are read from k and v, never from the cache, so no
+ * work-group reads a cache position the same call writes, and repeating the
+ * call with the same arguments writes identical bytes.
+ */
+pa_status prefill_attn_chunked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const int32_t *cu_seqlens, int32_t num_seqs,
+                               int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                               uint16_t *k_cache, uint16_t *v_cache,
+                               int32_t cache_capacity, uint16_t *out, float scale,
+                               hipStream_t stream, const int32_t *prefix_lens);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *pa_status_string(int status);
+
+/* Turn check mode on (1) or off (0); returns the previous setting.  Process-wide. */
+int pa_set_check_mode(int on);
+
+/* hipError_t of the last PA_ERR_HIP returned on the calling thread (0 if none). */
+int pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFILL_ATTN_H */

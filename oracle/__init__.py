@@ -53,6 +53,8 @@ def _load():
     lib.oracle_prefill_rows.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, p,
                                         ctypes.c_float, p, ctypes.c_int64, p]
     lib.oracle_prefill_rows.restype = ctypes.c_int
+    lib.oracle_cache_image.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
+    lib.oracle_cache_image.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -183,3 +185,29 @@ def prefill_rows(q, k, v, cu_seqlens, scale, rows, prefix_lens=None,
         ctypes.c_float(scale), _ptr(rows), rows.shape[0], _ptr(out))
     _check(rc, "prefill_rows")
     return out
+
+
+def cache_image(k, v, cu_seqlens, k_cache, v_cache, prefix_lens=None):
+    """The cache image only (no attention): copies of k_cache / v_cache with
+    the new tokens' K/V placed.  Varlen layout if prefix_lens is None (flat
+    buffers of >= N*H*D elements), else chunked [B, H, cap, D]."""
+    k, v = _u16(k), _u16(v)
+    cu = _i32(cu_seqlens)
+    N, H, D = k.shape
+    B = cu.shape[0] - 1
+    kc = _u16(k_cache).copy()
+    vc = _u16(v_cache).copy()
+    pre = None
+    cap = 0
+    if prefix_lens is not None:
+        pre = _i32(prefix_lens)
+        cap = kc.shape[2]
+        if kc.shape != (B, H, cap, D) or vc.shape != kc.shape:
+            raise ValueError("cache must be [B, H, cap, D]")
+    elif kc.size < N * H * D or vc.size < N * H * D:
+        raise ValueError("varlen cache needs N*H*D elements")
+    rc = _load().oracle_cache_image(_ptr(k), _ptr(v), _ptr(cu), B, H, D, cap,
+                                    _ptr(pre) if pre is not None else None,
+                                    _ptr(kc), _ptr(vc))
+    _check(rc, "cache_image")
+    return kc, vc

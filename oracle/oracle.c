@@ -324,6 +324,25 @@ int oracle_prefill_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return failed ? -1 : 0;
 }
 
+/*
+ * The cache image alone (no attention), for bit-exact cache checks at sizes
+ * where computing every output row would take too long.  prefix_lens NULL
+ * selects the varlen layout, otherwise the chunked [B, H, cap, D] layout;
+ * same placement rule as write_cache above.
+ */
+int oracle_cache_image(const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
+                       int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t cache_capacity, const int32_t *prefix_lens,
+                       uint16_t *k_cache, uint16_t *v_cache)
+{
+    problem_t P = {NULL, k, v, cu_seqlens, prefix_lens, NULL, NULL,
+                   num_seqs, num_heads, head_dim, cache_capacity, 0.0};
+    int rc = check_meta(&P);
+    if (rc) return rc;
+    write_cache(&P, k_cache, v_cache);
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -1,0 +1,157 @@
+"""Thin ctypes binding over libprefill_attn.so (include/prefill_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprefill_attn.so")
+
+PA_OK = 0
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libprefill_attn.so is not built (%s); run `python -m prefill_self_attention_amd.build`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.prefill_attn_varlen.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, p,
+                                        ctypes.c_float, p]
+    lib.prefill_attn_varlen.restype = ctypes.c_int
+    lib.prefill_attn_chunked.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, i32, p,
+                                         ctypes.c_float, p, p]
+    lib.prefill_attn_chunked.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_set_check_mode.argtypes = [ctypes.c_int]
+    lib.pa_set_check_mode.restype = ctypes.c_int
+    lib.pa_last_hip_error.argtypes = []
+    lib.pa_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def pa_set_check_mode(on: bool) -> bool:
+    return bool(load().pa_set_check_mode(1 if on else 0))
+
+
+def pa_last_hip_error() -> int:
+    return int(load().pa_last_hip_error())
+
+
+class PrefillAttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = int(status)
+        msg = pa_status_string(status)
+        if status == 9:
+            msg += " (hipError_t %d)" % pa_last_hip_error()
+        super().__init__(msg)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_tensor(name, t, dtype):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def _max_seqlen(cu_seqlens) -> int:
+    """max(cu[b+1]-cu[b]) from a host copy (synchronises the stream)."""
+    c = cu_seqlens.cpu().tolist()
+    return max([c[i + 1] - c[i] for i in range(len(c) - 1)] or [0])
+
+
+def prefill_attn_varlen(q, k, v, cu_seqlens, k_cache, v_cache, out, scale=None,
+                        max_seqlen=None, stream=None):
+    """Varlen causal prefill + KV-cache write (see prefill_attn.h).
+
+    q, k, v, out: bf16 [N, H, D] device tensors; cu_seqlens: int32 [B + 1]
+    device; k_cache, v_cache: bf16 device tensors of N*H*D elements (sequence
+    b's [H, len_b, D] block starts at element cu[b]*H*D).  scale defaults to
+    1/sqrt(D).  max_seqlen: host int; computed from cu_seqlens (a sync) if
+    omitted.  Returns out.
+    """
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    N, H, D = q.shape
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    st = load().prefill_attn_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, D,
+        _ptr(k_cache), _ptr(v_cache), _ptr(out), ctypes.c_float(scale), _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out
+
+
+def prefill_attn_chunked(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens,
+                         scale=None, max_seqlen=None, stream=None):
+    """Chunked prefill: new tokens attend to a cached prefix and to each other.
+
+    k_cache, v_cache: bf16 [B, H, cap, D] device; prefix_lens: int32 [B]
+    device.  New tokens' K/V are written at positions prefix_b .. prefix_b +
+    len_b - 1.  Other arguments as for prefill_attn_varlen.  Returns out.
+    """
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    _check_tensor("prefix_lens", prefix_lens, torch.int32)
+    N, H, D = q.shape
+    B = cu_seqlens.shape[0] - 1
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != H or \
+            k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [B, H, cap, D]")
+    cap = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    st = load().prefill_attn_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, D,
+        _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
+        _stream(stream), _ptr(prefix_lens))
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out

@@ -1,0 +1,184 @@
+// api.hip -- the C ABI declared in include/prefill_attn.h: argument checks,
+// optional metadata checks (check mode), grid sizing and the launch.
+// Every step of the computation runs in the kernels of prefill_fwd.hip.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "launch.h"
+#include "prefill_attn.h"
+
+namespace {
+
+std::atomic<int> g_check_mode{-1};  // -1: not yet read from the environment
+thread_local int t_last_hip_error = 0;
+
+bool check_mode() {
+  int m = g_check_mode.load(std::memory_order_relaxed);
+  if (m < 0) {
+    const char* e = std::getenv("PA_CHECK");
+    m = (e && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    g_check_mode.compare_exchange_strong(expected, m);
+    m = g_check_mode.load(std::memory_order_relaxed);
+  }
+  return m == 1;
+}
+
+pa_status hip_fail(hipError_t e) {
+  t_last_hip_error = (int)e;
+  return PA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Host-side checks shared by both entry points.
+pa_status check_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int32_t* cu, int32_t num_seqs, int32_t max_seqlen,
+                       int32_t num_heads, int32_t head_dim, const uint16_t* kc,
+                       const uint16_t* vc, const uint16_t* out, float scale) {
+  if (!q || !k || !v || !cu || !kc || !vc || !out) return PA_ERR_NULL;
+  if (num_seqs < 0 || max_seqlen < 0 || num_heads < 1) return PA_ERR_SHAPE;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return PA_ERR_HEAD_DIM;
+  if (!std::isfinite(scale)) return PA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc) ||
+      !aligned16(out))
+    return PA_ERR_ALIGN;
+  const void* outs[3] = {kc, vc, out};
+  const void* ins[4] = {q, k, v, cu};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (outs[i] == ins[j]) return PA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[i] == outs[j]) return PA_ERR_ALIAS;
+  }
+  return PA_OK;
+}
+
+// Grid limits: x = heads, y = sequences, z = query blocks.
+pa_status check_grid(int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int* nqb) {
+  const int bm = pa::fwd_block_rows();
+  const int64_t q_blocks = ((int64_t)max_seqlen + bm - 1) / bm;
+  if (num_seqs > 65535 || q_blocks > 65535 || num_heads > 65535) return PA_ERR_SHAPE;
+  *nqb = (int)q_blocks;
+  return PA_OK;
+}
+
+// Check mode: copy metadata to the host on `stream`, wait, validate.
+pa_status check_metadata(const int32_t* cu, int32_t num_seqs, int32_t max_seqlen,
+                         const int32_t* prefix, int32_t cap, hipStream_t stream) {
+  std::vector<int32_t> hcu(num_seqs + 1), hpre(prefix ? num_seqs : 0);
+  hipError_t e = hipMemcpyAsync(hcu.data(), cu, sizeof(int32_t) * (num_seqs + 1),
+                                hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (prefix) {
+    e = hipMemcpyAsync(hpre.data(), prefix, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost,
+                       stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (hcu[0] != 0) return PA_ERR_SEQLENS;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t n = (int64_t)hcu[b + 1] - hcu[b];
+    if (n < 0 || n > max_seqlen) return PA_ERR_SEQLENS;
+    if (prefix) {
+      if (hpre[b] < 0 || (int64_t)hpre[b] + n > cap) return PA_ERR_CAPACITY;
+    }
+  }
+  return PA_OK;
+}
+
+pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+              int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+              uint16_t* kc, uint16_t* vc, int32_t cap, uint16_t* out, float scale,
+              hipStream_t stream, const int32_t* prefix) {
+  int nqb = 0;
+  pa_status st = check_grid(num_seqs, max_seqlen, num_heads, &nqb);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || max_seqlen == 0) return PA_OK;
+  if (check_mode()) {
+    st = check_metadata(cu, num_seqs, max_seqlen, prefix, cap, stream);
+    if (st != PA_OK) return st;
+  }
+  pa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.cu = cu;
+  p.prefix = prefix;
+  p.kc = kc;
+  p.vc = vc;
+  p.out = out;
+  p.num_heads = num_heads;
+  p.cap = cap;
+  p.nqb = nqb;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  hipError_t e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status prefill_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                              int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
+                              uint16_t* v_cache, uint16_t* out, float scale,
+                              hipStream_t stream) {
+  pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
+                              k_cache, v_cache, out, scale);
+  if (st != PA_OK) return st;
+  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, k_cache, v_cache,
+             0, out, scale, stream, nullptr);
+}
+
+pa_status prefill_attn_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                               int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
+                               uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
+                               float scale, hipStream_t stream, const int32_t* prefix_lens) {
+  pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
+                              k_cache, v_cache, out, scale);
+  if (st != PA_OK) return st;
+  if (!prefix_lens) return PA_ERR_NULL;
+  if ((const void*)prefix_lens == (const void*)k_cache ||
+      (const void*)prefix_lens == (const void*)v_cache || (const void*)prefix_lens == (const void*)out)
+    return PA_ERR_ALIAS;
+  if (cache_capacity < 1) return PA_ERR_SHAPE;
+  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, k_cache, v_cache,
+             cache_capacity, out, scale, stream, prefix_lens);
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid count or size (num_seqs, max_seqlen, num_heads, cache_capacity or grid limit)";
+    case PA_ERR_HEAD_DIM: return "PA_ERR_HEAD_DIM: head_dim must be 32, 64 or 128";
+    case PA_ERR_SCALE: return "PA_ERR_SCALE: scale must be finite";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
+    case PA_ERR_ALIAS: return "PA_ERR_ALIAS: an output aliases an input or another output";
+    case PA_ERR_SEQLENS: return "PA_ERR_SEQLENS: cu_seqlens must start at 0, be non-decreasing and have lengths <= max_seqlen";
+    case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: prefix_lens must be >= 0 with prefix + length <= cache_capacity";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP runtime call failed (see pa_last_hip_error)";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_set_check_mode(int on) {
+  int prev = check_mode() ? 1 : 0;
+  g_check_mode.store(on ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
+
+int pa_last_hip_error(void) { return t_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// launch.h -- internal interface between the C-ABI layer (api.hip) and the
+// gfx950 kernels (prefill_fwd.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct FwdParams {
+  const uint16_t* q;        // [N, H, D] bf16
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cu;        // [B + 1]
+  const int32_t* prefix;    // [B] (chunked) or nullptr (varlen)
+  uint16_t* kc;             // varlen: packed [H, len_b, D] blocks; chunked: [B, H, cap, D]
+  uint16_t* vc;
+  uint16_t* out;            // [N, H, D] bf16
+  int32_t num_heads;
+  int32_t cap;              // chunked cache capacity (0 for varlen)
+  int32_t nqb;              // query blocks per sequence in the grid
+  float scale_log2;         // scale * log2(e)
+};
+
+// Query rows handled by one work-group.
+int fwd_block_rows();
+
+// Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
+hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
+                              hipStream_t stream);
+
+}  // namespace pa

@@ -344,3 +344,23 @@ def test_causal_pair_count():
     w, q, k, v = rand_varlen([T], 1, 32, 59)
     _, _, _, probs = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale, want_probs=True)
     assert np.count_nonzero(probs) == T * (T + 1) // 2
+
+
+def test_cache_image_only_matches_full_oracle():
+    w, q, k, v = rand_varlen([7, 1, 30], 2, 32, 60)
+    sent = np.full(w.num_tokens * 2 * 32 + 16, 0x7FC1, np.uint16)
+    _, kimg, vimg, _ = oracle.prefill_varlen(q, k, v, w.cu_seqlens, w.scale,
+                                             k_cache=sent, v_cache=sent)
+    kc, vc = oracle.cache_image(k, v, w.cu_seqlens, sent, sent)
+    np.testing.assert_array_equal(kc, kimg)
+    np.testing.assert_array_equal(vc, vimg)
+    g = I.generator(61)
+    n, pre = [4, 1], [9, 3]
+    cu = I.cu_from_lengths(n)
+    kq, kk, kv = (bits(I.randn_bf16(g, (5, 2, 32))) for _ in range(3))
+    kc0 = bits(I.randn_bf16(g, (2, 2, 16, 32)))
+    vc0 = bits(I.randn_bf16(g, (2, 2, 16, 32)))
+    _, kimg, vimg, _ = oracle.prefill_chunked(kq, kk, kv, cu, pre, kc0, vc0, 0.1)
+    kc, vc = oracle.cache_image(kk, kv, cu, kc0, vc0, prefix_lens=pre)
+    np.testing.assert_array_equal(kc, kimg)
+    np.testing.assert_array_equal(vc, vimg)
