@@ -61,11 +61,10 @@ pa_status check_common(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 }
 
 // Grid limits: x = heads, y = sequences, z = query blocks.
-pa_status check_grid(int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int* nqb) {
-  const int bm = pa::fwd_block_rows();
-  const int64_t q_blocks = ((int64_t)max_seqlen + bm - 1) / bm;
-  if (num_seqs > 65535 || q_blocks > 65535 || num_heads > 65535) return PA_ERR_SHAPE;
-  *nqb = (int)q_blocks;
+pa_status check_grid(int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int* grid_z) {
+  const int z = pa::fwd_grid_blocks(max_seqlen);
+  if (num_seqs > 65535 || z > 65535 || num_heads > 65535) return PA_ERR_SHAPE;
+  *grid_z = z;
   return PA_OK;
 }
 
@@ -117,8 +116,11 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   p.out = out;
   p.num_heads = num_heads;
   p.cap = cap;
-  p.nqb = nqb;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  p.grid_z = nqb;
+  // scale * q.k == |scale| * (sign(scale) q).k : keep the exp2-domain factor
+  // non-negative so the kernel can take the row max before scaling
+  p.scale_log2 = (float)(std::fabs((double)scale) * 1.4426950408889634);  // log2(e)
+  p.neg_q = scale < 0.f ? 1 : 0;
   hipError_t e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;

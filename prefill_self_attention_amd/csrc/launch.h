@@ -17,12 +17,14 @@ struct FwdParams {
   uint16_t* out;            // [N, H, D] bf16
   int32_t num_heads;
   int32_t cap;              // chunked cache capacity (0 for varlen)
-  int32_t nqb;              // query blocks per sequence in the grid
-  float scale_log2;         // scale * log2(e)
+  int32_t grid_z;           // work-groups per (head, sequence): pairs of query blocks
+  float scale_log2;         // |scale| * log2(e)
+  int32_t neg_q;            // 1 if scale < 0: q's sign is flipped in the kernel
 };
 
-// Query rows handled by one work-group.
+// Query rows per block, and work-groups per (head, sequence) for a maximum length.
 int fwd_block_rows();
+int fwd_grid_blocks(int max_seqlen);
 
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,

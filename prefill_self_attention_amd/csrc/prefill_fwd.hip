@@ -16,41 +16,53 @@
 // How it is computed (blockwise, never materialising the T x T scores, and
 // skipping tiles above the diagonal: www.zwxr.cn/news/300951 §3.3):
 //
-//  * Work-group = (sequence b, head h, block of BM = 128 query rows); four
-//    wave64s, each owning 32 consecutive query rows.  The grid is laid out
-//    (head, sequence, q-block) with the q-block index reversed, so the
-//    hardware dispatches the longest (highest) q-blocks first; with H a
-//    multiple of 8 every q-block of one head lands on the same XCD (the
-//    dispatcher deals work-groups round-robin over the 8 XCDs), which keeps
-//    that head's K/V in one L2.
-//  * Key tiles of BN = 64 absolute key positions.  The work-group stages
-//    K[64][D] row-major and V^T[D][64] (keys permuted inside each group of 16,
-//    see below) in LDS; the next tile's global loads are issued before the
-//    current tile's MFMAs, so HBM latency hides behind compute.
+//  * Query blocks of 128 rows, key tiles of 64 absolute key positions.  A
+//    query block whose last key is e needs ceil(e / 64) tiles, so block i of
+//    a causal sequence costs about i+1 units.  One work-group takes the pair
+//    of blocks (z, n-1-z) of one (sequence, head): their costs sum to the same
+//    total for every z, so all work-groups of a sequence carry equal work.
+//  * The work-group has 8 wave64s, two per SIMD, in two groups of four.  The
+//    tile list of the pair (light block's tiles, then the heavy block's) is
+//    split in half: the upper group walks the heavy block's tiles from 0, the
+//    lower group does the light block and then the heavy block's remaining
+//    (highest) tiles.  Each wave owns 32 query rows of the block it is on.
+//    The heavy block's rows thus hold two partial online-softmax states (one
+//    per group), merged through LDS at the end.  Every wave of the launch does
+//    the same number of tiles (17 at T = 2048), and each SIMD runs two waves,
+//    so one wave's softmax VALU work can overlap the other's MFMAs.
+//  * Each group stages its own tile per iteration in LDS: K[64][D] row-major
+//    and V^T[D][64] (keys permuted inside each group of 16, see below), rows
+//    padded by 16 B so 8-lane 16-byte reads fall on distinct banks.  The next
+//    tile's global loads are issued before the current tile's MFMAs.
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in VGPRs for the
-//    whole loop).  In the 32x32 accumulator layout lane l holds query column
-//    l%32 and 16 key rows 8*(r/4) + 4*(l/32) + r%4, so a query's whole score
-//    row lives in two lanes (l and l^32): the online-softmax max needs one
-//    cross-half exchange per tile, the running sum none until the end, and
-//    the O rescale is a per-lane multiply.
-//  * Online softmax in the exp2 domain: s2 = s * scale * log2(e);
-//    m' = max(m, rowmax), alpha = 2^(m - m'), p = 2^(s2 - m'),
-//    l = alpha l + sum p, O = alpha O.  This streams the row normaliser that
-//    the definition takes over the whole row.
-//  * O^T = V^T P^T, again 32x32x16 MFMA: the B operand is P^T converted to
-//    bf16 straight from the score accumulator (registers 8s..8s+7 of a
-//    32-key block are keys {16s + 8*(i/4) + 4*(l/32) + i%4}); V^T in LDS
-//    stores keys of each 16-group in the order [0..3, 8..11, 4..7, 12..15] so
-//    the matching A operand is one 16-byte LDS read.
-//  * Causal masking is applied only on tiles that cross the wave's diagonal or
-//    the end of the keys; tiles wholly above a wave's diagonal are skipped by
-//    that wave, and never loaded by a work-group none of whose rows sees them.
-//  * KV-cache write: the work-group that owns query rows [q0, q0+BM) copies
-//    K/V of exactly those tokens from the registers it staged them through,
-//    with full-row coalesced stores.  Prefix keys of chunked prefill are read
-//    from the cache, new keys always from k/v, so no work-group reads a cache
-//    position this launch writes.
+//    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in VGPRs).  In the
+//    32x32 accumulator layout lane l holds query column l%32 and 16 key rows
+//    8*(r/4) + 4*(l/32) + r%4, so a query's score row lives in two lanes
+//    (l and l^32): the online-softmax max needs one v_permlane32_swap per
+//    tile, the running sum none until the end, and the O rescale is a
+//    per-lane multiply.
+//  * Online softmax in the exp2 domain with c = |scale| log2(e) >= 0 (a
+//    negative scale flips q's sign instead): the row max is taken over raw
+//    scores, p = 2^(s c - m) is one FMA and one v_exp_f32.  The running max m
+//    only moves when a tile's max exceeds it by more than 8 (lazy rescale:
+//    p stays below 2^8, O and l are rescaled when m moves), which is exact in
+//    real arithmetic because the final O / l uses one consistent m.
+//  * O^T = V^T P^T, 32x32x16 MFMA: the B operand is P^T converted to bf16
+//    straight from the score accumulator (registers 8s..8s+7 of a 32-key block
+//    are keys 16s + 8*(i/4) + 4*(l/32) + i%4); V^T stores keys of each 16-group
+//    in the order [0..3, 8..11, 4..7, 12..15], so the matching A operand is one
+//    16-byte LDS read.
+//  * Causal masking runs only on tiles that cross a wave's diagonal or the end
+//    of the keys; a wave skips tiles wholly above its rows.
+//  * KV-cache write: the group that stages a tile holding keys of the block's
+//    own new tokens copies exactly those rows to the cache from its staging
+//    registers, with full-row coalesced stores; every new token is written
+//    once.  Prefix keys of chunked prefill are read from the cache, new keys
+//    always from k/v, so no work-group reads a cache position this launch
+//    writes.
+//  * The grid is (head, sequence, pair); with H a multiple of 8 all pairs of
+//    one head land on one XCD (work-groups are dealt round-robin over the 8
+//    XCDs), which keeps that head's K/V in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,286 +78,396 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;  // query rows per work-group
-constexpr int kBN = 64;           // keys per tile
-constexpr int kKPad = 8;          // bf16 elements of padding per K row in LDS
-constexpr int kVPad = 8;          // bf16 elements of padding per V^T row in LDS
+constexpr int kGroupThreads = 256;  // one group = 4 waves
+constexpr int kBM = 128;            // query rows per block (4 waves x 32)
+constexpr int kBN = 64;             // keys per tile
+constexpr int kPad = 8;             // bf16 elements of padding per LDS row
+constexpr float kRescale = 8.0f;    // lazy-rescale headroom, log2 units
+constexpr float kNegInf = -__builtin_huge_valf();
+// Initial running max: finite, so a first tile in which every key of a row is
+// masked (possible when a group starts mid-sequence) keeps alpha = 2^0 = 1
+// instead of 2^(-inf - -inf); any real score replaces it (alpha = 0 then).
+constexpr float kMInit = -1.0e30f;
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+// max / sum of x over lanes l and l^32 (the two halves of one query's scores)
+__device__ __forceinline__ float row_max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
-// Key (relative to its 16-group) stored at position i (0..7) of half `hh`
-// of the group: the order matches the 32x32 accumulator's row mapping.
-__device__ __forceinline__ int vt_key(int hh, int i) {
-  return 8 * (i >> 2) + 4 * hh + (i & 3);
+__device__ __forceinline__ float row_sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool kChunked>
-struct Tile {
-  // K chunks of 8 bf16 (16 B) per thread, and V dword columns for 8 keys.
-  static constexpr int kKChunks = kBN * D / 8;                 // 16-B chunks per K tile
-  static constexpr int kKPerThread = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVItems = (D / 2) * (kBN / 8);           // (d pair, key octet)
-  static constexpr int kVPerThread = (kVItems + kThreads - 1) / kThreads;
-  static constexpr int kKStride = D + kKPad;                   // LDS row stride (elements)
-  static constexpr int kVStride = kBN + kVPad;
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t two = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
+}
+
+// Key (within its 16-group) stored at position i (0..7) of half hh of the
+// group's V^T row: matches the 32x32 accumulator's row order.
+__device__ __forceinline__ int vt_key(int hh, int i) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+template <int D>
+struct Cfg {
+  static constexpr int kKStride = D + kPad;           // K row stride in LDS (elements)
+  static constexpr int kVStride = kBN + kPad;         // V^T row stride
+  static constexpr int kKElems = kBN * kKStride;
+  static constexpr int kSlotElems = kKElems + D * kVStride;
+  static constexpr int kKChunks = kBN * D / 8;         // 16-B chunks per K tile
+  static constexpr int kKPer = (kKChunks + kGroupThreads - 1) / kGroupThreads;
+  static constexpr int kVItems = (D / 2) * (kBN / 8);  // (d pair, key octet) items
+  static constexpr int kVPer = (kVItems + kGroupThreads - 1) / kGroupThreads;
+  // merge buffer: per upper wave, per lane: m, l and D/32 x 16 accumulators
+  static constexpr int kMergeFloats = 4 * (2 + D / 2) * 64;
+  static constexpr int kLdsElems =
+      (2 * kSlotElems > 2 * kMergeFloats) ? 2 * kSlotElems : 2 * kMergeFloats;
 };
 
+// One query block of one (sequence, head).
+struct Block {
+  int q0;       // first local row
+  int qend;     // one past the last local row (<= len)
+  int key_end;  // keys needed: absolute positions [0, key_end)
+  int own_lo;   // absolute positions [own_lo, key_end) are this block's new tokens
+  int ntiles;
+};
+
+__device__ __forceinline__ Block make_block(int qb, int len, int pre) {
+  Block k;
+  k.q0 = qb * kBM;
+  k.qend = min(k.q0 + kBM, len);
+  k.key_end = pre + k.qend;
+  k.own_lo = pre + k.q0;
+  k.ntiles = (k.key_end + kBN - 1) / kBN;
+  return k;
+}
+
 template <int D, bool kChunked>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_fwd_kernel(FwdParams p) {
-  using T = Tile<D, kChunked>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * T::kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * T::kVStride];
+__global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int qb = p.nqb - 1 - (int)blockIdx.z;
+  const int z = blockIdx.z;
   const int64_t H = p.num_heads;
 
   const int seq_start = p.cu[b];
   const int len = p.cu[b + 1] - seq_start;
-  const int q0 = qb * kBM;
-  if (q0 >= len) return;
+  const int nqb = (len + kBM - 1) / kBM;
+  const int qb_hi = nqb - 1 - z;
+  if (z > qb_hi) return;                 // no block pair left for this work-group
   const int pre = kChunked ? p.prefix[b] : 0;
-  const int qend = min(q0 + kBM, len);
-  const int key_end = pre + qend;             // keys this work-group needs: [0, key_end)
-  const int own_lo = pre + q0;                // cache rows this work-group writes
-  const int ntiles = (key_end + kBN - 1) / kBN;
+  const bool has_lo = z < qb_hi;
+  const Block blo = make_block(z, len, pre);
+  const Block bhi = make_block(qb_hi, len, pre);
+  const int e_lo = has_lo ? blo.ntiles : 0;
+  const int e_hi = bhi.ntiles;
+  const int n_iter = (e_lo + e_hi + 1) / 2;  // tiles of the upper group
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int ql = lane & 31;
   const int hh = lane >> 5;
+  const bool upper = wave >= 4;
+  const int gw = wave & 3;               // wave within its group
+  const int gtid = tid & (kGroupThreads - 1);
 
-  const int64_t row_stride = H * D;           // elements between consecutive tokens
+  uint16_t* const k_lds = lds + (upper ? C::kSlotElems : 0);
+  uint16_t* const vt_lds = k_lds + C::kKElems;
+
+  const int64_t row_stride = H * D;      // elements between consecutive tokens
   const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
   const uint16_t* __restrict__ vin = p.v + (int64_t)h * D;
-  // cache base for this (b, h): element of absolute key position 0
-  int64_t cache_base;
-  if (kChunked) {
-    cache_base = ((int64_t)b * H + h) * p.cap * D;
-  } else {
-    cache_base = (int64_t)seq_start * H * D + (int64_t)h * len * D;
-  }
+  // cache element of absolute key position 0 for this (b, h)
+  const int64_t cache_base = kChunked ? ((int64_t)b * H + h) * p.cap * D
+                                      : (int64_t)seq_start * H * D + (int64_t)h * len * D;
+  const float c = p.scale_log2;          // |scale| * log2(e) >= 0
 
-  // ---------------------------------------------------------- Q operand (B)
-  const int qrow0 = q0 + 32 * wave;           // first local row of this wave
-  const bool wave_active = qrow0 < len;
-  const int qa0 = pre + qrow0;                // its absolute position
-  const int qa = qa0 + ql;                    // this lane's query position
-  bf16x8_t qop[D / 16];
-  {
-    const int row = qrow0 + ql;
-    const bool ok = row < len;
-    const uint16_t* src = p.q + ((int64_t)(seq_start + (ok ? row : 0)) * H + h) * D + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4_t x = ok ? *(const u32x4_t*)(src + 16 * ks) : u32x4_t{0, 0, 0, 0};
-      qop[ks] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
+  // ---------------------------------------------------------------- schedule
+  // Tile of this group at iteration `it`: (block, tile index), or none.
+  auto my_tile = [&](int it, bool& on_hi, int& t) -> bool {
+    if (upper) { on_hi = true; t = it; return it < n_iter; }
+    if (it < e_lo) { on_hi = false; t = it; return true; }
+    on_hi = true;
+    t = n_iter + (it - e_lo);
+    return t < e_hi;
+  };
 
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = f32x16_t{};
-  float m_run = -__builtin_huge_valf();
-  float l_run = 0.f;
+  // ---------------------------------------------------------------- staging
+  u32x4_t kreg[C::kKPer];
+  uint32_t vreg[C::kVPer][8];
 
-  // ---------------------------------------------------------- staging regs
-  u32x4_t kreg[T::kKPerThread];
-  uint32_t vreg[T::kVPerThread][8];
-
-  // Source row of absolute key position kp (valid keys only).
-  auto key_src = [&](const uint16_t* __restrict__ in, const uint16_t* __restrict__ cache,
-                     int kp) -> const uint16_t* {
+  auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) {
     if (kChunked && kp < pre) return cache + cache_base + (int64_t)kp * D;
     return in + (int64_t)(seq_start + kp - pre) * row_stride;
   };
 
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](const Block& blk, int t) {
     const int t0 = t * kBN;
+    const bool full = t0 + kBN <= blk.key_end;
 #pragma unroll
-    for (int i = 0; i < T::kKPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      kreg[i] = u32x4_t{0, 0, 0, 0};
-      if (c < T::kKChunks) {
-        const int kp = t0 + c / (D / 8);
-        if (kp < key_end)
-          kreg[i] = *(const u32x4_t*)(key_src(kin, p.kc, kp) + 8 * (c % (D / 8)));
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int cidx = gtid + kGroupThreads * i;
+      kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (cidx < C::kKChunks) {
+        const int kp = t0 + cidx / (D / 8);
+        if (full || kp < blk.key_end)
+          kreg[i] = *(const u32x4_t*)(row_ptr(kin, p.kc, kp) + 8 * (cidx % (D / 8)));
       }
     }
 #pragma unroll
-    for (int i = 0; i < T::kVPerThread; ++i) {
-      const int item = tid + kThreads * i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vreg[i][e] = 0u;
-      if (item < T::kVItems) {
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int item = gtid + kGroupThreads * i;
+      if (item < C::kVItems) {
         const int dp = item % (D / 2);
         const int oct = item / (D / 2);
+        const int kbase = t0 + 16 * (oct >> 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int kp = t0 + 16 * (oct >> 1) + vt_key(oct & 1, e);
-          if (kp < key_end)
-            vreg[i][e] = *(const uint32_t*)(key_src(vin, p.vc, kp) + 2 * dp);
+          const int kp = kbase + vt_key(oct & 1, e);
+          vreg[i][e] = 0u;
+          if (full || kp < blk.key_end)
+            vreg[i][e] = *(const uint32_t*)(row_ptr(vin, p.vc, kp) + 2 * dp);
         }
       }
     }
   };
 
-  auto store_tile = [&](int t) {
+  auto store_tile = [&](const Block& blk, int t) {
     const int t0 = t * kBN;
+    const bool writes_cache = t0 + kBN > blk.own_lo;  // tile holds new tokens of blk
 #pragma unroll
-    for (int i = 0; i < T::kKPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < T::kKChunks) {
-        const int r = c / (D / 8), c8 = c % (D / 8);
-        *(u32x4_t*)(k_lds + r * T::kKStride + 8 * c8) = kreg[i];
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int cidx = gtid + kGroupThreads * i;
+      if (cidx < C::kKChunks) {
+        const int r = cidx / (D / 8), c8 = cidx % (D / 8);
+        *(u32x4_t*)(k_lds + r * C::kKStride + 8 * c8) = kreg[i];
         const int kp = t0 + r;
-        if (kp >= own_lo && kp < key_end)
+        if (writes_cache && kp >= blk.own_lo && kp < blk.key_end)
           *(u32x4_t*)(p.kc + cache_base + (int64_t)kp * D + 8 * c8) = kreg[i];
       }
     }
 #pragma unroll
-    for (int i = 0; i < T::kVPerThread; ++i) {
-      const int item = tid + kThreads * i;
-      if (item < T::kVItems) {
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int item = gtid + kGroupThreads * i;
+      if (item < C::kVItems) {
         const int dp = item % (D / 2);
         const int oct = item / (D / 2);
+        const uint32_t* x = vreg[i];
         u32x4_t lo, hi;
-        lo[0] = pack_lo(vreg[i][0], vreg[i][1]);
-        lo[1] = pack_lo(vreg[i][2], vreg[i][3]);
-        lo[2] = pack_lo(vreg[i][4], vreg[i][5]);
-        lo[3] = pack_lo(vreg[i][6], vreg[i][7]);
-        hi[0] = pack_hi(vreg[i][0], vreg[i][1]);
-        hi[1] = pack_hi(vreg[i][2], vreg[i][3]);
-        hi[2] = pack_hi(vreg[i][4], vreg[i][5]);
-        hi[3] = pack_hi(vreg[i][6], vreg[i][7]);
-        *(u32x4_t*)(vt_lds + (2 * dp) * T::kVStride + 8 * oct) = lo;
-        *(u32x4_t*)(vt_lds + (2 * dp + 1) * T::kVStride + 8 * oct) = hi;
+        lo[0] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
+        lo[1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
+        lo[2] = __builtin_amdgcn_perm(x[5], x[4], 0x05040100u);
+        lo[3] = __builtin_amdgcn_perm(x[7], x[6], 0x05040100u);
+        hi[0] = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
+        hi[1] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);
+        hi[2] = __builtin_amdgcn_perm(x[5], x[4], 0x07060302u);
+        hi[3] = __builtin_amdgcn_perm(x[7], x[6], 0x07060302u);
+        *(u32x4_t*)(vt_lds + (2 * dp) * C::kVStride + 8 * oct) = lo;
+        *(u32x4_t*)(vt_lds + (2 * dp + 1) * C::kVStride + 8 * oct) = hi;
+        if (writes_cache) {
+          const int kbase = t0 + 16 * (oct >> 1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kp = t0 + 16 * (oct >> 1) + vt_key(oct & 1, e);
-          if (kp >= own_lo && kp < key_end)
-            *(uint32_t*)(p.vc + cache_base + (int64_t)kp * D + 2 * dp) = vreg[i][e];
+          for (int e = 0; e < 8; ++e) {
+            const int kp = kbase + vt_key(oct & 1, e);
+            if (kp >= blk.own_lo && kp < blk.key_end)
+              *(uint32_t*)(p.vc + cache_base + (int64_t)kp * D + 2 * dp) = x[e];
+          }
         }
       }
     }
   };
 
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // all waves are done reading the previous tile
-    store_tile(t);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+  // ---------------------------------------------------------------- wave state
+  bf16x8_t qop[D / 16];
+  f32x16_t o[D / 32];
+  float m_run, l_run;
+  int qrow0, len_rows;  // this wave's first local row; rows of its block are < len_rows
 
+  auto begin_rows = [&](const Block& blk) {
+    qrow0 = blk.q0 + 32 * gw;
+    len_rows = blk.qend;
+    const int row = qrow0 + ql;
+    const bool ok = row < len_rows;
+    const uint16_t* src = p.q + ((int64_t)(seq_start + (ok ? row : 0)) * H + h) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4_t x = ok ? *(const u32x4_t*)(src + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      if (p.neg_q) x ^= 0x80008000u;  // negative scale: flip the sign of q instead
+      qop[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = f32x16_t{};
+    m_run = kMInit;
+    l_run = 0.f;
+  };
+
+  // normalise and store this wave's rows
+  auto store_rows = [&](float l_part) {
+    const int row = qrow0 + ql;
+    const float inv = 1.f / row_sum_halves(l_part);
+    if (row >= len_rows) return;
+    uint16_t* dst = p.out + ((int64_t)(seq_start + row) * H + h) * D + 4 * hh;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        u32x2_t w = {pack_bf16x2(o[mb][4 * cc + 0] * inv, o[mb][4 * cc + 1] * inv),
+                     pack_bf16x2(o[mb][4 * cc + 2] * inv, o[mb][4 * cc + 3] * inv)};
+        *(u32x2_t*)(dst + 32 * mb + 8 * cc) = w;
+      }
+  };
+
+  // one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto compute_tile = [&](const Block& blk, int t, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     const int t0 = t * kBN;
-    if (!wave_active || t0 > qa0 + 31) continue;  // tile wholly above this wave's rows
-
-    // S^T = K Q^T for two 32-key blocks
+    const int qa = pre + qrow0 + ql;  // this lane's absolute query position
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
-      const uint16_t* kr = k_lds + (32 * kb + ql) * T::kKStride + 8 * hh;
+      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kKStride + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr + 16 * ks));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s[kb], 0, 0, 0);
       }
     }
-
-    // scale, mask, row max
-    const bool need_mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > key_end);
-    float mx = -__builtin_huge_valf();
+    if constexpr (kMask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * p.scale_log2;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int kp = t0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (kp > qa || kp >= key_end) x = -__builtin_huge_valf();
+          if (kp > qa || kp >= blk.key_end) s[kb][r] = kNegInf;
         }
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // p = 2^(s2 - m), row sum (per lane), P^T -> bf16 B operands
-    float ls = 0.f;
+    float mx4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float m8 = s[j >> 1][8 * (j & 1)];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, s[j >> 1][8 * (j & 1) + i]);
+      mx4[j] = m8;
+    }
+    float mx = row_max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    const float mt = (mx == kNegInf) ? mx : mx * c;
+    if (__any(mt > m_run + kRescale)) {  // wave-uniform; always taken on the first tile
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) o[mb] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
     bf16x8_t pb[4];
+    float ls[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int g = 0; g < 4; ++g) {
+      float e[8];
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = __builtin_amdgcn_exp2f(s[kb][8 * sh + i] - m_new);
-          ls += e[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x2_t two = {e[2 * i], e[2 * i + 1]};
-          bf16x2_t c = __builtin_convertvector(two, bf16x2_t);
-          pb[2 * kb + sh][2 * i] = c[0];
-          pb[2 * kb + sh][2 * i + 1] = c[1];
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float sv = s[g >> 1][8 * (g & 1) + i];
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, neg_m));
+        if constexpr (kMask) x = (sv == kNegInf) ? 0.f : x;  // also right for c == 0
+        e[i] = x;
       }
+      ls[g] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      u32x4_t w = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                   pack_bf16x2(e[6], e[7])};
+      pb[g] = __builtin_bit_cast(bf16x8_t, w);
     }
-    l_run = alpha * l_run + ls;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) o[mb] *= alpha;
-
-    // O^T += V^T P^T
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      const uint16_t* vr = vt_lds + (32 * mb + ql) * T::kVStride + 8 * hh;
+      const uint16_t* vr = vt_lds + (32 * mb + ql) * C::kVStride + 8 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vr + 16 * g));
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], o[mb], 0, 0, 0);
       }
     }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  bool on_hi_rows = upper || !has_lo;  // which block's rows this wave holds
+  begin_rows(on_hi_rows ? bhi : blo);
+
+  {
+    bool oh;
+    int t;
+    if (my_tile(0, oh, t)) load_tile(oh ? bhi : blo, t);
+  }
+  for (int it = 0; it < n_iter; ++it) {
+    bool oh;
+    int t;
+    const bool have = my_tile(it, oh, t);
+    const Block& blk = oh ? bhi : blo;
+    __syncthreads();  // both groups are done reading their previous tiles
+    if (have) store_tile(blk, t);
+    __syncthreads();
+    {
+      bool oh2;
+      int t2;
+      if (it + 1 < n_iter && my_tile(it + 1, oh2, t2)) load_tile(oh2 ? bhi : blo, t2);
+    }
+    if (!have) continue;
+    if (oh && !on_hi_rows) {  // lower group moves from the light block to the heavy one
+      if (qrow0 < len_rows) store_rows(l_run);
+      on_hi_rows = true;
+      begin_rows(bhi);
+    }
+    const int t0 = t * kBN;
+    const int qa0 = pre + qrow0;
+    if (qrow0 >= len_rows || t0 > qa0 + 31) continue;  // no rows, or tile above them
+    const bool need_mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > blk.key_end);
+    if (need_mask)
+      compute_tile(blk, t, std::true_type{});
+    else
+      compute_tile(blk, t, std::false_type{});
   }
 
-  // ---------------------------------------------------------- epilogue
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  const int row = qrow0 + ql;
-  if (row >= len) return;
-  uint16_t* dst = p.out + ((int64_t)(seq_start + row) * H + h) * D + 4 * hh;
+  // ---------------------------------------------------------------- merge
+  if (!on_hi_rows) {  // lower group never reached the heavy block: finish the light one
+    if (qrow0 < len_rows) store_rows(l_run);
+    on_hi_rows = true;
+    begin_rows(bhi);   // empty partial state for the heavy block's rows
+  }
+  __syncthreads();     // tile buffers are free
+  float* mbuf = reinterpret_cast<float*>(lds) + gw * (2 + D / 2) * 64;
+  if (upper) {
+    mbuf[lane] = m_run;
+    mbuf[64 + lane] = l_run;
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x2_t a = {o[mb][4 * c + 0] * inv, o[mb][4 * c + 1] * inv};
-      f32x2_t bb = {o[mb][4 * c + 2] * inv, o[mb][4 * c + 3] * inv};
-      bf16x2_t ca = __builtin_convertvector(a, bf16x2_t);
-      bf16x2_t cb = __builtin_convertvector(bb, bf16x2_t);
-      u32x2_t w = {__builtin_bit_cast(uint32_t, ca), __builtin_bit_cast(uint32_t, cb)};
-      *(u32x2_t*)(dst + 32 * mb + 8 * c) = w;
-    }
+      for (int r = 0; r < 16; ++r) mbuf[(2 + 16 * mb + r) * 64 + lane] = o[mb][r];
+  }
+  __syncthreads();
+  if (!upper && qrow0 < len_rows) {
+    const float mb_ = mbuf[lane];
+    const float lb = mbuf[64 + lane];
+    const float m = fmaxf(m_run, mb_);
+    const float fa = __builtin_amdgcn_exp2f(m_run - m);  // 0 if this group saw no tile
+    const float fb = __builtin_amdgcn_exp2f(mb_ - m);
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] = o[mb][r] * fa + mbuf[(2 + 16 * mb + r) * 64 + lane] * fb;
+    store_rows(l_run * fa + lb * fb);
   }
 }
 
 template <int D, bool kChunked>
 hipError_t launch_d(const FwdParams& p, int num_seqs, hipStream_t stream) {
-  dim3 grid(p.num_heads, num_seqs, p.nqb);
+  dim3 grid(p.num_heads, num_seqs, p.grid_z);
   hipLaunchKernelGGL((prefill_fwd_kernel<D, kChunked>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -353,6 +475,11 @@ hipError_t launch_d(const FwdParams& p, int num_seqs, hipStream_t stream) {
 }  // namespace
 
 int fwd_block_rows() { return kBM; }
+
+int fwd_grid_blocks(int max_seqlen) {
+  const int nqb = (max_seqlen + kBM - 1) / kBM;
+  return (nqb + 1) / 2;  // one work-group per pair of query blocks
+}
 
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream) {
