@@ -106,20 +106,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
 }
 
-// Key (within its 16-group) stored at position i (0..7) of half hh of the
-// group's V^T row: matches the 32x32 accumulator's row order.
-__device__ __forceinline__ int vt_key(int hh, int i) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
-
 template <int D>
 struct Cfg {
-  static constexpr int kKStride = D + kPad;           // K row stride in LDS (elements)
-  static constexpr int kVStride = kBN + kPad;         // V^T row stride
-  static constexpr int kKElems = kBN * kKStride;
-  static constexpr int kSlotElems = kKElems + D * kVStride;
-  static constexpr int kKChunks = kBN * D / 8;         // 16-B chunks per K tile
-  static constexpr int kKPer = (kKChunks + kGroupThreads - 1) / kGroupThreads;
-  static constexpr int kVItems = (D / 2) * (kBN / 8);  // (d pair, key octet) items
-  static constexpr int kVPer = (kVItems + kGroupThreads - 1) / kGroupThreads;
+  static constexpr int kStride = D + kPad;             // K and V row stride in LDS (elements)
+  static constexpr int kTileElems = kBN * kStride;
+  static constexpr int kSlotElems = 2 * kTileElems;     // K tile then V tile
+  static constexpr int kChunksPerRow = D / 8;           // 16-B chunks per row
+  static constexpr int kRowsPerPass = kGroupThreads / kChunksPerRow;
+  static constexpr int kPer = kBN / kRowsPerPass;       // 16-B chunks per thread per tile
   // merge buffer: per upper wave, per lane: m, l and D/32 x 16 accumulators
   static constexpr int kMergeFloats = 4 * (2 + D / 2) * 64;
   static constexpr int kLdsElems =
@@ -178,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   const int gtid = tid & (kGroupThreads - 1);
 
   uint16_t* const k_lds = lds + (upper ? C::kSlotElems : 0);
-  uint16_t* const vt_lds = k_lds + C::kKElems;
+  uint16_t* const v_lds = k_lds + C::kTileElems;
 
   const int64_t row_stride = H * D;      // elements between consecutive tokens
   const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
@@ -199,8 +193,14 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   };
 
   // ---------------------------------------------------------------- staging
-  u32x4_t kreg[C::kKPer];
-  uint32_t vreg[C::kVPer][8];
+  // Thread gtid of a group moves 16-B chunk (gtid % (D/8)) of tile rows
+  // gtid / (D/8) + i * kRowsPerPass, i < kPer, for K and for V.  Row pointers
+  // are formed per tile from uniform (scalar) bases; per-lane offsets are
+  // 32-bit.  Full tiles that lie wholly in the new tokens or wholly in the
+  // cached prefix take the unguarded path; the few edge tiles check each row.
+  u32x4_t kreg[C::kPer], vreg[C::kPer];
+  const int srow = gtid / C::kChunksPerRow;
+  const int scol = 8 * (gtid % C::kChunksPerRow);
 
   auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) {
     if (kChunked && kp < pre) return cache + cache_base + (int64_t)kp * D;
@@ -210,29 +210,31 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   auto load_tile = [&](const Block& blk, int t) {
     const int t0 = t * kBN;
     const bool full = t0 + kBN <= blk.key_end;
+    const bool all_new = !kChunked || t0 >= pre;
+    const bool all_cached = kChunked && t0 + kBN <= pre;
+    if (full && (all_new || all_cached)) {
+      // uniform tile base and row step (elements)
+      const int64_t step = all_new ? row_stride : (int64_t)D;
+      const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                   : p.kc + cache_base + (int64_t)t0 * D;
+      const uint16_t* vt = all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                   : p.vc + cache_base + (int64_t)t0 * D;
+      const uint32_t off = (uint32_t)(srow * step + scol);
 #pragma unroll
-    for (int i = 0; i < C::kKPer; ++i) {
-      const int cidx = gtid + kGroupThreads * i;
-      kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (cidx < C::kKChunks) {
-        const int kp = t0 + cidx / (D / 8);
-        if (full || kp < blk.key_end)
-          kreg[i] = *(const u32x4_t*)(row_ptr(kin, p.kc, kp) + 8 * (cidx % (D / 8)));
+      for (int i = 0; i < C::kPer; ++i) {
+        const int64_t pass = (int64_t)(i * C::kRowsPerPass) * step;
+        kreg[i] = *(const u32x4_t*)(kt + pass + off);
+        vreg[i] = *(const u32x4_t*)(vt + pass + off);
       }
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < C::kVPer; ++i) {
-      const int item = gtid + kGroupThreads * i;
-      if (item < C::kVItems) {
-        const int dp = item % (D / 2);
-        const int oct = item / (D / 2);
-        const int kbase = t0 + 16 * (oct >> 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kp = kbase + vt_key(oct & 1, e);
-          vreg[i][e] = 0u;
-          if (full || kp < blk.key_end)
-            vreg[i][e] = *(const uint32_t*)(row_ptr(vin, p.vc, kp) + 2 * dp);
+      for (int i = 0; i < C::kPer; ++i) {
+        const int kp = t0 + srow + i * C::kRowsPerPass;
+        kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
+        vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (kp < blk.key_end) {
+          kreg[i] = *(const u32x4_t*)(row_ptr(kin, p.kc, kp) + scol);
+          vreg[i] = *(const u32x4_t*)(row_ptr(vin, p.vc, kp) + scol);
         }
       }
     }
@@ -240,44 +242,20 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
 
   auto store_tile = [&](const Block& blk, int t) {
     const int t0 = t * kBN;
-    const bool writes_cache = t0 + kBN > blk.own_lo;  // tile holds new tokens of blk
 #pragma unroll
-    for (int i = 0; i < C::kKPer; ++i) {
-      const int cidx = gtid + kGroupThreads * i;
-      if (cidx < C::kKChunks) {
-        const int r = cidx / (D / 8), c8 = cidx % (D / 8);
-        *(u32x4_t*)(k_lds + r * C::kKStride + 8 * c8) = kreg[i];
-        const int kp = t0 + r;
-        if (writes_cache && kp >= blk.own_lo && kp < blk.key_end)
-          *(u32x4_t*)(p.kc + cache_base + (int64_t)kp * D + 8 * c8) = kreg[i];
-      }
+    for (int i = 0; i < C::kPer; ++i) {
+      const int r = srow + i * C::kRowsPerPass;
+      *(u32x4_t*)(k_lds + r * C::kStride + scol) = kreg[i];
+      *(u32x4_t*)(v_lds + r * C::kStride + scol) = vreg[i];
     }
+    if (t0 + kBN > blk.own_lo) {  // the tile holds new tokens of blk: copy them to the cache
 #pragma unroll
-    for (int i = 0; i < C::kVPer; ++i) {
-      const int item = gtid + kGroupThreads * i;
-      if (item < C::kVItems) {
-        const int dp = item % (D / 2);
-        const int oct = item / (D / 2);
-        const uint32_t* x = vreg[i];
-        u32x4_t lo, hi;
-        lo[0] = __builtin_amdgcn_perm(x[1], x[0], 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(x[3], x[2], 0x05040100u);
-        lo[2] = __builtin_amdgcn_perm(x[5], x[4], 0x05040100u);
-        lo[3] = __builtin_amdgcn_perm(x[7], x[6], 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(x[1], x[0], 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(x[3], x[2], 0x07060302u);
-        hi[2] = __builtin_amdgcn_perm(x[5], x[4], 0x07060302u);
-        hi[3] = __builtin_amdgcn_perm(x[7], x[6], 0x07060302u);
-        *(u32x4_t*)(vt_lds + (2 * dp) * C::kVStride + 8 * oct) = lo;
-        *(u32x4_t*)(vt_lds + (2 * dp + 1) * C::kVStride + 8 * oct) = hi;
-        if (writes_cache) {
-          const int kbase = t0 + 16 * (oct >> 1);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kp = kbase + vt_key(oct & 1, e);
-            if (kp >= blk.own_lo && kp < blk.key_end)
-              *(uint32_t*)(p.vc + cache_base + (int64_t)kp * D + 2 * dp) = x[e];
-          }
+      for (int i = 0; i < C::kPer; ++i) {
+        const int kp = t0 + srow + i * C::kRowsPerPass;
+        if (kp >= blk.own_lo && kp < blk.key_end) {
+          const int64_t dst = cache_base + (int64_t)kp * D + scol;
+          *(u32x4_t*)(p.kc + dst) = kreg[i];
+          *(u32x4_t*)(p.vc + dst) = vreg[i];
         }
       }
     }
@@ -332,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
-      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kKStride + 8 * hh;
+      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kStride + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr + 16 * ks));
@@ -385,12 +363,26 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
       pb[g] = __builtin_bit_cast(bf16x8_t, w);
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // PV A operand with the LDS transpose read: lane L of 16-lane group G
+    // points at 4 consecutive d of key row 16g + 8r + 4*(G/2) + (L%16)/4,
+    // d = 32 mb + 16*(G%2) + 4*(L%4); the read hands lane L the 4 keys
+    // {16g + 8r + 4*(G/2) + j} at its own d = 32 mb + L%32, i.e. elements
+    // 4r..4r+3 of V^T in the accumulator's key order.
+    const int tg = lane >> 4, tl = lane & 15;
+    const uint16_t* vr = v_lds + (4 * (tg >> 1) + (tl >> 2)) * C::kStride + 16 * (tg & 1) + 4 * (tl & 3);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-      const uint16_t* vr = vt_lds + (32 * mb + ql) * C::kVStride + 8 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vr + 16 * g));
+        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+        const uint16_t* a0 = vr + (16 * g) * C::kStride + 32 * mb;
+        const uint16_t* a1 = a0 + 8 * C::kStride;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
+        typedef short s16x8_t __attribute__((ext_vector_type(8)));
+        s16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], o[mb], 0, 0, 0);
       }
     }
