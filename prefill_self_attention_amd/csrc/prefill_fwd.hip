@@ -108,16 +108,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 template <int D>
 struct Cfg {
-  static constexpr int kStride = D + kPad;             // K and V row stride in LDS (elements)
-  static constexpr int kTileElems = kBN * kStride;
-  static constexpr int kSlotElems = 2 * kTileElems;     // K tile then V tile
+  // LDS row strides (elements): K rows 4 banks apart for the 8-lane 16-byte
+  // reads of the score operand, V rows 8 banks apart for the 4-row, 32-byte
+  // footprint of each 16-lane transpose read.
+  static constexpr int kKStride = D + kPad;
+  static constexpr int kVStride = D + 2 * kPad;
+  static constexpr int kKElems = kBN * kKStride;
+  static constexpr int kSlotElems = kKElems + kBN * kVStride;  // K tile then V tile
   static constexpr int kChunksPerRow = D / 8;           // 16-B chunks per row
   static constexpr int kRowsPerPass = kGroupThreads / kChunksPerRow;
   static constexpr int kPer = kBN / kRowsPerPass;       // 16-B chunks per thread per tile
   // merge buffer: per upper wave, per lane: m, l and D/32 x 16 accumulators
   static constexpr int kMergeFloats = 4 * (2 + D / 2) * 64;
   static constexpr int kLdsElems =
-      (2 * kSlotElems > 2 * kMergeFloats) ? 2 * kSlotElems : 2 * kMergeFloats;
+      (4 * kSlotElems > 2 * kMergeFloats) ? 4 * kSlotElems : 2 * kMergeFloats;
 };
 
 // One query block of one (sequence, head).
@@ -171,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   const int gw = wave & 3;               // wave within its group
   const int gtid = tid & (kGroupThreads - 1);
 
-  uint16_t* const k_lds = lds + (upper ? C::kSlotElems : 0);
-  uint16_t* const v_lds = k_lds + C::kTileElems;
+  // two LDS slots per group (double buffer): slot s of group g at (2g + s)
+  uint16_t* const grp_lds = lds + (upper ? 2 * C::kSlotElems : 0);
 
   const int64_t row_stride = H * D;      // elements between consecutive tokens
   const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
@@ -240,13 +244,15 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
     }
   };
 
-  auto store_tile = [&](const Block& blk, int t) {
+  auto store_tile = [&](const Block& blk, int t, int slot) {
     const int t0 = t * kBN;
+    uint16_t* const k_lds = grp_lds + slot * C::kSlotElems;
+    uint16_t* const v_lds = k_lds + C::kKElems;
 #pragma unroll
     for (int i = 0; i < C::kPer; ++i) {
       const int r = srow + i * C::kRowsPerPass;
-      *(u32x4_t*)(k_lds + r * C::kStride + scol) = kreg[i];
-      *(u32x4_t*)(v_lds + r * C::kStride + scol) = vreg[i];
+      *(u32x4_t*)(k_lds + r * C::kKStride + scol) = kreg[i];
+      *(u32x4_t*)(v_lds + r * C::kVStride + scol) = vreg[i];
     }
     if (t0 + kBN > blk.own_lo) {  // the tile holds new tokens of blk: copy them to the cache
 #pragma unroll
@@ -302,15 +308,17 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   };
 
   // one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto compute_tile = [&](const Block& blk, int t, auto mask_tag) {
+  auto compute_tile = [&](const Block& blk, int t, int slot, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
+    const uint16_t* const k_lds = grp_lds + slot * C::kSlotElems;
+    const uint16_t* const v_lds = k_lds + C::kKElems;
     const int t0 = t * kBN;
     const int qa = pre + qrow0 + ql;  // this lane's absolute query position
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
-      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kStride + 8 * hh;
+      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kKStride + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr + 16 * ks));
@@ -369,15 +377,15 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
     // {16g + 8r + 4*(G/2) + j} at its own d = 32 mb + L%32, i.e. elements
     // 4r..4r+3 of V^T in the accumulator's key order.
     const int tg = lane >> 4, tl = lane & 15;
-    const uint16_t* vr = v_lds + (4 * (tg >> 1) + (tl >> 2)) * C::kStride + 16 * (tg & 1) + 4 * (tl & 3);
+    const uint16_t* vr = v_lds + (4 * (tg >> 1) + (tl >> 2)) * C::kVStride + 16 * (tg & 1) + 4 * (tl & 3);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         typedef short s16x4_t __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-        const uint16_t* a0 = vr + (16 * g) * C::kStride + 32 * mb;
-        const uint16_t* a1 = a0 + 8 * C::kStride;
+        const uint16_t* a0 = vr + (16 * g) * C::kVStride + 32 * mb;
+        const uint16_t* a1 = a0 + 8 * C::kVStride;
         s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0));
         s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
         typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -392,38 +400,43 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   bool on_hi_rows = upper || !has_lo;  // which block's rows this wave holds
   begin_rows(on_hi_rows ? bhi : blo);
 
+  // Double-buffered LDS, one barrier per iteration: iteration `it` computes
+  // from slot it%2, then stores the next tile (loaded into registers during
+  // the previous iteration) into the other slot, whose last readers finished
+  // before the previous barrier, then issues the loads for the tile after.
   {
     bool oh;
     int t;
-    if (my_tile(0, oh, t)) load_tile(oh ? bhi : blo, t);
+    if (my_tile(0, oh, t)) {
+      load_tile(oh ? bhi : blo, t);
+      store_tile(oh ? bhi : blo, t, 0);
+    }
+    if (n_iter > 1 && my_tile(1, oh, t)) load_tile(oh ? bhi : blo, t);
   }
+  __syncthreads();
   for (int it = 0; it < n_iter; ++it) {
     bool oh;
     int t;
-    const bool have = my_tile(it, oh, t);
-    const Block& blk = oh ? bhi : blo;
-    __syncthreads();  // both groups are done reading their previous tiles
-    if (have) store_tile(blk, t);
+    if (my_tile(it, oh, t)) {
+      const Block& blk = oh ? bhi : blo;
+      if (oh && !on_hi_rows) {  // lower group moves from the light block to the heavy one
+        if (qrow0 < len_rows) store_rows(l_run);
+        on_hi_rows = true;
+        begin_rows(bhi);
+      }
+      const int t0 = t * kBN;
+      const int qa0 = pre + qrow0;
+      if (qrow0 < len_rows && t0 <= qa0 + 31) {  // rows present and not all above the tile
+        const bool need_mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > blk.key_end);
+        if (need_mask)
+          compute_tile(blk, t, it & 1, std::true_type{});
+        else
+          compute_tile(blk, t, it & 1, std::false_type{});
+      }
+    }
+    if (it + 1 < n_iter && my_tile(it + 1, oh, t)) store_tile(oh ? bhi : blo, t, (it + 1) & 1);
+    if (it + 2 < n_iter && my_tile(it + 2, oh, t)) load_tile(oh ? bhi : blo, t);
     __syncthreads();
-    {
-      bool oh2;
-      int t2;
-      if (it + 1 < n_iter && my_tile(it + 1, oh2, t2)) load_tile(oh2 ? bhi : blo, t2);
-    }
-    if (!have) continue;
-    if (oh && !on_hi_rows) {  // lower group moves from the light block to the heavy one
-      if (qrow0 < len_rows) store_rows(l_run);
-      on_hi_rows = true;
-      begin_rows(bhi);
-    }
-    const int t0 = t * kBN;
-    const int qa0 = pre + qrow0;
-    if (qrow0 >= len_rows || t0 > qa0 + 31) continue;  // no rows, or tile above them
-    const bool need_mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > blk.key_end);
-    if (need_mask)
-      compute_tile(blk, t, std::true_type{});
-    else
-      compute_tile(blk, t, std::false_type{});
   }
 
   // ---------------------------------------------------------------- merge
@@ -432,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
     on_hi_rows = true;
     begin_rows(bhi);   // empty partial state for the heavy block's rows
   }
-  __syncthreads();     // tile buffers are free
+  // the loop's last barrier has freed the tile buffers
   float* mbuf = reinterpret_cast<float*>(lds) + gw * (2 + D / 2) * 64;
   if (upper) {
     mbuf[lane] = m_run;
