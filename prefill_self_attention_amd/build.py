@@ -1,7 +1,8 @@
 """Build libprefill_attn.so (HIP, gfx950) in-tree with hipcc.
 
 Run as ``python -m prefill_self_attention_amd.build`` or call ``build()``.
-Flags: -O3 for gfx950 only; packed-fp32 VALU ops disabled in device code
+Flags: -O3 for gfx950 only; IEEE mode off with relaxed NaN handling (no
+canonicalising moves before max/min); packed-fp32 VALU ops disabled in device code
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass prints a
 harmless "not a recognized feature" warning for it).
 """
@@ -28,6 +29,8 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+           # no NaN canonicalisation around max/min (inputs are finite by contract)
+           "-fno-honor-nans", "-mno-amdgpu-ieee",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument",
            "-I", INCLUDE, "-I", CSRC]

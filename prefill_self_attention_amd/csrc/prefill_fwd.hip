@@ -17,52 +17,51 @@
 // skipping tiles above the diagonal: www.zwxr.cn/news/300951 §3.3):
 //
 //  * Query blocks of 128 rows, key tiles of 64 absolute key positions.  A
-//    query block whose last key is e needs ceil(e / 64) tiles, so block i of
-//    a causal sequence costs about i+1 units.  One work-group takes the pair
-//    of blocks (z, n-1-z) of one (sequence, head): their costs sum to the same
+//    block whose last key is e needs ceil(e / 64) tiles, so block i of a causal
+//    sequence costs about i+1 units.  One work-group takes the pair of blocks
+//    (z, n-1-z) of one (sequence, head): the costs of a pair sum to the same
 //    total for every z, so all work-groups of a sequence carry equal work.
-//  * The work-group has 8 wave64s, two per SIMD, in two groups of four.  The
-//    tile list of the pair (light block's tiles, then the heavy block's) is
-//    split in half: the upper group walks the heavy block's tiles from 0, the
-//    lower group does the light block and then the heavy block's remaining
-//    (highest) tiles.  Each wave owns 32 query rows of the block it is on.
-//    The heavy block's rows thus hold two partial online-softmax states (one
-//    per group), merged through LDS at the end.  Every wave of the launch does
-//    the same number of tiles (17 at T = 2048), and each SIMD runs two waves,
-//    so one wave's softmax VALU work can overlap the other's MFMAs.
-//  * Each group stages its own tile per iteration in LDS: K[64][D] row-major
-//    and V^T[D][64] (keys permuted inside each group of 16, see below), rows
-//    padded by 16 B so 8-lane 16-byte reads fall on distinct banks.  The next
-//    tile's global loads are issued before the current tile's MFMAs.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in VGPRs).  In the
-//    32x32 accumulator layout lane l holds query column l%32 and 16 key rows
-//    8*(r/4) + 4*(l/32) + r%4, so a query's score row lives in two lanes
-//    (l and l^32): the online-softmax max needs one v_permlane32_swap per
-//    tile, the running sum none until the end, and the O rescale is a
-//    per-lane multiply.
+//  * The work-group is 8 wave64s, two per SIMD, in two groups of four; a wave
+//    owns 32 query rows of the block it is on.  The pair's tile list (light
+//    block, then heavy block) is split in half: the upper group walks the heavy
+//    block's tiles from 0, the lower group does the light block and then the
+//    heavy block's remaining (highest) tiles.  The heavy block's rows so hold
+//    two partial online-softmax states, merged through LDS at the end; every
+//    wave does the same number of tiles (17 at T = 2048), and each SIMD runs
+//    two waves, so one wave's softmax VALU work overlaps the other's MFMAs (a
+//    single wave issues VALU at about half the SIMD's rate on this part).
+//  * Tiles reach LDS by direct global-to-LDS loads (global_load_lds_dwordx4:
+//    lane l of an instruction fills bytes [16 l, 16 l + 16) of a 1 KB block),
+//    double-buffered per group, one barrier per iteration; no staging VGPRs.
+//    Rows are stored unpadded with the 16-byte chunk index XORed with
+//    f(row) = 2*(row%4) + (row/4)%2: the 8-row reads of the score operand and
+//    the 4-row, 32-byte transpose reads of the PV operand then hit distinct
+//    banks.
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    (A = K from LDS, B = Q^T held in VGPRs).  In the 32x32 accumulator lane l
+//    holds query column l%32 and key rows 8*(r/4) + 4*(l/32) + r%4, so a
+//    query's scores live in lanes l and l^32: one v_permlane32_swap per tile
+//    for the max, none for the running sum until the end, and the O rescale is
+//    a per-lane multiply.
 //  * Online softmax in the exp2 domain with c = |scale| log2(e) >= 0 (a
-//    negative scale flips q's sign instead): the row max is taken over raw
-//    scores, p = 2^(s c - m) is one FMA and one v_exp_f32.  The running max m
-//    only moves when a tile's max exceeds it by more than 8 (lazy rescale:
-//    p stays below 2^8, O and l are rescaled when m moves), which is exact in
-//    real arithmetic because the final O / l uses one consistent m.
-//  * O^T = V^T P^T, 32x32x16 MFMA: the B operand is P^T converted to bf16
-//    straight from the score accumulator (registers 8s..8s+7 of a 32-key block
-//    are keys 16s + 8*(i/4) + 4*(l/32) + i%4); V^T stores keys of each 16-group
-//    in the order [0..3, 8..11, 4..7, 12..15], so the matching A operand is one
-//    16-byte LDS read.
-//  * Causal masking runs only on tiles that cross a wave's diagonal or the end
-//    of the keys; a wave skips tiles wholly above its rows.
-//  * KV-cache write: the group that stages a tile holding keys of the block's
-//    own new tokens copies exactly those rows to the cache from its staging
-//    registers, with full-row coalesced stores; every new token is written
-//    once.  Prefix keys of chunked prefill are read from the cache, new keys
-//    always from k/v, so no work-group reads a cache position this launch
-//    writes.
-//  * The grid is (head, sequence, pair); with H a multiple of 8 all pairs of
-//    one head land on one XCD (work-groups are dealt round-robin over the 8
-//    XCDs), which keeps that head's K/V in one L2.
+//    negative scale flips q's sign instead): max over raw scores, p =
+//    2^(s c - m) as one FMA and one v_exp_f32.  The running max m only moves
+//    when a tile's max exceeds it by more than 8 (lazy rescale; p stays below
+//    2^8; exact in real arithmetic because O and l share one m).
+//  * O^T = V^T P^T on 32x32x16 MFMA: B = P^T converted to bf16 straight from
+//    the score accumulator; A = V^T read from row-major V with
+//    ds_read_b64_tr_b16, which hands each lane 4 keys of its own d in the
+//    accumulator's key order.
+//  * Causal masking only on tiles that cross a wave's diagonal or the end of
+//    the keys; a wave skips tiles wholly above its rows.
+//  * KV-cache write: when a group's tile holds new tokens of the block it
+//    serves, the group copies exactly those rows from LDS to the cache with
+//    16-byte stores; every new token is written once.  Prefix keys of chunked
+//    prefill are read from the cache, new keys always from k/v, so no
+//    work-group reads a cache position this launch writes.
+//  * Grid (head, sequence, pair): with H a multiple of 8 all pairs of one head
+//    land on one XCD (work-groups are dealt round-robin over the 8 XCDs),
+//    keeping that head's K/V in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,21 +76,22 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kGroupThreads = 256;  // one group = 4 waves
 constexpr int kBM = 128;            // query rows per block (4 waves x 32)
+constexpr int kGroupThreads = 256;  // one group = 4 waves
 constexpr int kBN = 64;             // keys per tile
-constexpr int kPad = 8;             // bf16 elements of padding per LDS row
 constexpr float kRescale = 8.0f;    // lazy-rescale headroom, log2 units
 constexpr float kNegInf = -__builtin_huge_valf();
 // Initial running max: finite, so a first tile in which every key of a row is
-// masked (possible when a group starts mid-sequence) keeps alpha = 2^0 = 1
-// instead of 2^(-inf - -inf); any real score replaces it (alpha = 0 then).
+// masked (a group can start mid-sequence) keeps alpha = 2^0 = 1 instead of
+// 2^(-inf - -inf); any real score replaces it (alpha = 0 then).
 constexpr float kMInit = -1.0e30f;
 
-// max / sum of x over lanes l and l^32 (the two halves of one query's scores)
 __device__ __forceinline__ float row_max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -100,7 +100,6 @@ __device__ __forceinline__ float row_sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t two = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
@@ -108,23 +107,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 template <int D>
 struct Cfg {
-  // LDS row strides (elements): K rows 4 banks apart for the 8-lane 16-byte
-  // reads of the score operand, V rows 8 banks apart for the 4-row, 32-byte
-  // footprint of each 16-lane transpose read.
-  static constexpr int kKStride = D + kPad;
-  static constexpr int kVStride = D + 2 * kPad;
-  static constexpr int kKElems = kBN * kKStride;
-  static constexpr int kSlotElems = kKElems + kBN * kVStride;  // K tile then V tile
-  static constexpr int kChunksPerRow = D / 8;           // 16-B chunks per row
-  static constexpr int kRowsPerPass = kGroupThreads / kChunksPerRow;
-  static constexpr int kPer = kBN / kRowsPerPass;       // 16-B chunks per thread per tile
-  // merge buffer: per upper wave, per lane: m, l and D/32 x 16 accumulators
-  static constexpr int kMergeFloats = 4 * (2 + D / 2) * 64;
-  static constexpr int kLdsElems =
-      (4 * kSlotElems > 2 * kMergeFloats) ? 4 * kSlotElems : 2 * kMergeFloats;
+  static constexpr int kCpr = D / 8;                    // 16-byte chunks per row
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = kBN * kRowBytes;    // one K or V tile
+  static constexpr int kSlotBytes = 2 * kTileBytes;     // K tile then V tile
+  static constexpr int kRowsPerInst = 1024 / kRowBytes; // rows per 1 KB direct load
+  static constexpr int kInstPerTile = kBN / kRowsPerInst;
+  static constexpr int kInstPerWave = kInstPerTile / 4; // per tile, per wave of a group
+  // merge buffer: per upper wave, per lane: m, l and D/2 accumulators
+  static constexpr int kMergeBytes = 4 * (2 + D / 2) * 64 * 4;
+  static constexpr int kLdsBytes = (4 * kSlotBytes > kMergeBytes) ? 4 * kSlotBytes : kMergeBytes;
 };
 
-// One query block of one (sequence, head).
+// 16-byte chunk slot of chunk c in row r (XOR swizzle, stays inside the row)
+template <int D>
+__device__ __forceinline__ int chunk_slot(int r, int c) {
+  return c ^ ((((r & 3) << 1) | ((r >> 2) & 1)) & (Cfg<D>::kCpr - 1));
+}
+
 struct Block {
   int q0;       // first local row
   int qend;     // one past the last local row (<= len)
@@ -143,10 +143,19 @@ __device__ __forceinline__ Block make_block(int qb, int len, int pre) {
   return k;
 }
 
+// State of a wave's 32 query rows.
+template <int D>
+struct Rows {
+  bf16x8_t q[D / 16];
+  f32x16_t o[D / 32];
+  float m, l;
+};
+
 template <int D, bool kChunked>
-__global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads)
+void prefill_fwd_kernel(FwdParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -173,21 +182,17 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;
   const bool upper = wave >= 4;
   const int gw = wave & 3;               // wave within its group
-  const int gtid = tid & (kGroupThreads - 1);
 
-  // two LDS slots per group (double buffer): slot s of group g at (2g + s)
-  uint16_t* const grp_lds = lds + (upper ? 2 * C::kSlotElems : 0);
+  uint8_t* const grp_lds = lds + (upper ? 2 * C::kSlotBytes : 0);
 
   const int64_t row_stride = H * D;      // elements between consecutive tokens
   const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
   const uint16_t* __restrict__ vin = p.v + (int64_t)h * D;
-  // cache element of absolute key position 0 for this (b, h)
   const int64_t cache_base = kChunked ? ((int64_t)b * H + h) * p.cap * D
                                       : (int64_t)seq_start * H * D + (int64_t)h * len * D;
   const float c = p.scale_log2;          // |scale| * log2(e) >= 0
 
   // ---------------------------------------------------------------- schedule
-  // Tile of this group at iteration `it`: (block, tile index), or none.
   auto my_tile = [&](int it, bool& on_hi, int& t) -> bool {
     if (upper) { on_hi = true; t = it; return it < n_iter; }
     if (it < e_lo) { on_hi = false; t = it; return true; }
@@ -197,81 +202,76 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
   };
 
   // ---------------------------------------------------------------- staging
-  // Thread gtid of a group moves 16-B chunk (gtid % (D/8)) of tile rows
-  // gtid / (D/8) + i * kRowsPerPass, i < kPer, for K and for V.  Row pointers
-  // are formed per tile from uniform (scalar) bases; per-lane offsets are
-  // 32-bit.  Full tiles that lie wholly in the new tokens or wholly in the
-  // cached prefix take the unguarded path; the few edge tiles check each row.
-  u32x4_t kreg[C::kPer], vreg[C::kPer];
-  const int srow = gtid / C::kChunksPerRow;
-  const int scol = 8 * (gtid % C::kChunksPerRow);
+  // Wave gw of a group issues instructions j = 4 i + gw (i < kInstPerWave) per
+  // tile and matrix; lane l fills row j * kRowsPerInst + l / kCpr, chunk slot
+  // l % kCpr, from source chunk chunk_slot(row, slot) (the XOR is an
+  // involution).  Rows past the block's last key read the last key instead,
+  // so every LDS row holds finite data (masked keys get weight 0).
+  const int lrow = lane / C::kCpr;
+  const int lslot = lane % C::kCpr;
 
   auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) {
     if (kChunked && kp < pre) return cache + cache_base + (int64_t)kp * D;
     return in + (int64_t)(seq_start + kp - pre) * row_stride;
   };
 
-  auto load_tile = [&](const Block& blk, int t) {
+  auto issue_tile = [&](const Block& blk, int t, int slot) {
     const int t0 = t * kBN;
+    uint8_t* const k_dst = grp_lds + slot * C::kSlotBytes;
+    uint8_t* const v_dst = k_dst + C::kTileBytes;
     const bool full = t0 + kBN <= blk.key_end;
     const bool all_new = !kChunked || t0 >= pre;
     const bool all_cached = kChunked && t0 + kBN <= pre;
     if (full && (all_new || all_cached)) {
-      // uniform tile base and row step (elements)
       const int64_t step = all_new ? row_stride : (int64_t)D;
       const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
                                    : p.kc + cache_base + (int64_t)t0 * D;
       const uint16_t* vt = all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
                                    : p.vc + cache_base + (int64_t)t0 * D;
-      const uint32_t off = (uint32_t)(srow * step + scol);
 #pragma unroll
-      for (int i = 0; i < C::kPer; ++i) {
-        const int64_t pass = (int64_t)(i * C::kRowsPerPass) * step;
-        kreg[i] = *(const u32x4_t*)(kt + pass + off);
-        vreg[i] = *(const u32x4_t*)(vt + pass + off);
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int row = j * C::kRowsPerInst + lrow;
+        const uint32_t off = (uint32_t)(row * step + 8 * chunk_slot<D>(row, lslot));
+        __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < C::kPer; ++i) {
-        const int kp = t0 + srow + i * C::kRowsPerPass;
-        kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (kp < blk.key_end) {
-          kreg[i] = *(const u32x4_t*)(row_ptr(kin, p.kc, kp) + scol);
-          vreg[i] = *(const u32x4_t*)(row_ptr(vin, p.vc, kp) + scol);
-        }
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int row = j * C::kRowsPerInst + lrow;
+        const int kp = min(t0 + row, blk.key_end - 1);
+        const int col = 8 * chunk_slot<D>(row, lslot);
+        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(kin, p.kc, kp) + col),
+                                         (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(vin, p.vc, kp) + col),
+                                         (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
       }
     }
   };
 
-  auto store_tile = [&](const Block& blk, int t, int slot) {
+  // copy the tile's new-token rows of blk from LDS to the cache (group-wide)
+  auto cache_copy = [&](const Block& blk, int t, int slot) {
     const int t0 = t * kBN;
-    uint16_t* const k_lds = grp_lds + slot * C::kSlotElems;
-    uint16_t* const v_lds = k_lds + C::kKElems;
-#pragma unroll
-    for (int i = 0; i < C::kPer; ++i) {
-      const int r = srow + i * C::kRowsPerPass;
-      *(u32x4_t*)(k_lds + r * C::kKStride + scol) = kreg[i];
-      *(u32x4_t*)(v_lds + r * C::kVStride + scol) = vreg[i];
-    }
-    if (t0 + kBN > blk.own_lo) {  // the tile holds new tokens of blk: copy them to the cache
-#pragma unroll
-      for (int i = 0; i < C::kPer; ++i) {
-        const int kp = t0 + srow + i * C::kRowsPerPass;
-        if (kp >= blk.own_lo && kp < blk.key_end) {
-          const int64_t dst = cache_base + (int64_t)kp * D + scol;
-          *(u32x4_t*)(p.kc + dst) = kreg[i];
-          *(u32x4_t*)(p.vc + dst) = vreg[i];
-        }
+    const uint8_t* const k_src = grp_lds + slot * C::kSlotBytes;
+    const uint8_t* const v_src = k_src + C::kTileBytes;
+    const int gl = 64 * gw + lane;       // 0..255 within the group
+    for (int idx = gl; idx < kBN * C::kCpr; idx += kGroupThreads) {
+      const int row = idx / C::kCpr, ch = idx % C::kCpr;
+      const int kp = t0 + row;
+      if (kp >= blk.own_lo && kp < blk.key_end) {
+        const int so = row * C::kRowBytes + 16 * chunk_slot<D>(row, ch);
+        const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
+        *(u32x4_t*)(p.kc + dst) = *(const u32x4_t*)(k_src + so);
+        *(u32x4_t*)(p.vc + dst) = *(const u32x4_t*)(v_src + so);
       }
     }
   };
 
   // ---------------------------------------------------------------- wave state
-  bf16x8_t qop[D / 16];
-  f32x16_t o[D / 32];
-  float m_run, l_run;
-  int qrow0, len_rows;  // this wave's first local row; rows of its block are < len_rows
+  Rows<D> st;
+  int qrow0, len_rows;  // first local row of the wave (32 rows); rows < len_rows exist
 
   auto begin_rows = [&](const Block& blk) {
     qrow0 = blk.q0 + 32 * gw;
@@ -281,17 +281,16 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
     const uint16_t* src = p.q + ((int64_t)(seq_start + (ok ? row : 0)) * H + h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4_t x = ok ? *(const u32x4_t*)(src + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-      if (p.neg_q) x ^= 0x80008000u;  // negative scale: flip the sign of q instead
-      qop[ks] = __builtin_bit_cast(bf16x8_t, x);
+      u32x4_t v = ok ? *(const u32x4_t*)(src + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+      if (p.neg_q) v ^= 0x80008000u;  // negative scale: flip the sign of q instead
+      st.q[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) o[i] = f32x16_t{};
-    m_run = kMInit;
-    l_run = 0.f;
+    for (int i = 0; i < D / 32; ++i) st.o[i] = f32x16_t{};
+    st.m = kMInit;
+    st.l = 0.f;
   };
 
-  // normalise and store this wave's rows
   auto store_rows = [&](float l_part) {
     const int row = qrow0 + ql;
     const float inv = 1.f / row_sum_halves(l_part);
@@ -301,28 +300,30 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        u32x2_t w = {pack_bf16x2(o[mb][4 * cc + 0] * inv, o[mb][4 * cc + 1] * inv),
-                     pack_bf16x2(o[mb][4 * cc + 2] * inv, o[mb][4 * cc + 3] * inv)};
+        u32x2_t w = {pack_bf16x2(st.o[mb][4 * cc + 0] * inv, st.o[mb][4 * cc + 1] * inv),
+                     pack_bf16x2(st.o[mb][4 * cc + 2] * inv, st.o[mb][4 * cc + 3] * inv)};
         *(u32x2_t*)(dst + 32 * mb + 8 * cc) = w;
       }
   };
 
-  // one tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+  // One 64-key tile: S^T = K Q^T (two 32-key blocks), online softmax over the
+  // 64 keys, O^T += V^T P^T.
   auto compute_tile = [&](const Block& blk, int t, int slot, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const uint16_t* const k_lds = grp_lds + slot * C::kSlotElems;
-    const uint16_t* const v_lds = k_lds + C::kKElems;
+    const uint8_t* const k_lds = grp_lds + slot * C::kSlotBytes;
+    const uint8_t* const v_lds = k_lds + C::kTileBytes;
     const int t0 = t * kBN;
     const int qa = pre + qrow0 + ql;  // this lane's absolute query position
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16_t{};
-      const uint16_t* kr = k_lds + (32 * kb + ql) * C::kKStride + 8 * hh;
+      const int kr = 32 * kb + ql;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr + 16 * ks));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s[kb], 0, 0, 0);
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *(const u32x4_t*)(k_lds + kr * C::kRowBytes + 16 * chunk_slot<D>(kr, 2 * ks + hh)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.q[ks], s[kb], 0, 0, 0);
       }
     }
     if constexpr (kMask) {
@@ -342,17 +343,17 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
       for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, s[j >> 1][8 * (j & 1) + i]);
       mx4[j] = m8;
     }
-    float mx = row_max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    const float mx = row_max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
     const float mt = (mx == kNegInf) ? mx : mx * c;
-    if (__any(mt > m_run + kRescale)) {  // wave-uniform; always taken on the first tile
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    if (__any(mt > st.m + kRescale)) {  // wave-uniform; taken on the first real tile
+      const float m_new = fmaxf(st.m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+      st.l *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) o[mb] *= alpha;
-      m_run = m_new;
+      for (int mb = 0; mb < D / 32; ++mb) st.o[mb] *= alpha;
+      st.m = m_new;
     }
-    const float neg_m = -m_run;
+    const float neg_m = -st.m;
     bf16x8_t pb[4];
     float ls[4];
 #pragma unroll
@@ -370,57 +371,55 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
                    pack_bf16x2(e[6], e[7])};
       pb[g] = __builtin_bit_cast(bf16x8_t, w);
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // PV A operand with the LDS transpose read: lane L of 16-lane group G
-    // points at 4 consecutive d of key row 16g + 8r + 4*(G/2) + (L%16)/4,
-    // d = 32 mb + 16*(G%2) + 4*(L%4); the read hands lane L the 4 keys
-    // {16g + 8r + 4*(G/2) + j} at its own d = 32 mb + L%32, i.e. elements
-    // 4r..4r+3 of V^T in the accumulator's key order.
+    st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // V^T operand by transpose read: lane L of 16-lane group G points at 4
+    // consecutive d of key row 16g + 8r + 4*(G/2) + (L%16)/4 at
+    // d = 32 mb + 16*(G%2) + 4*(L%4), and receives the 4 keys
+    // {16g + 8r + 4*(G/2) + j} at its own d = 32 mb + L%32.
     const int tg = lane >> 4, tl = lane & 15;
-    const uint16_t* vr = v_lds + (4 * (tg >> 1) + (tl >> 2)) * C::kVStride + 16 * (tg & 1) + 4 * (tl & 3);
+    const int vrow0 = 4 * (tg >> 1) + (tl >> 2);
+    const int vd0 = 16 * (tg & 1) + 4 * (tl & 3);
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        typedef short s16x4_t __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-        const uint16_t* a0 = vr + (16 * g) * C::kVStride + 32 * mb;
-        const uint16_t* a1 = a0 + 8 * C::kVStride;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
-        typedef short s16x8_t __attribute__((ext_vector_type(8)));
-        s16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        bf16x8_t a = __builtin_bit_cast(bf16x8_t, both);
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], o[mb], 0, 0, 0);
+        s16x4_t part[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = 16 * g + 8 * rr + vrow0;
+          const int d = 32 * mb + vd0;
+          const uint8_t* a = v_lds + row * C::kRowBytes + 16 * chunk_slot<D>(row, d >> 3) + 2 * (d & 7);
+          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
+        }
+        const bf16x8_t vf =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        st.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[g], st.o[mb], 0, 0, 0);
       }
-    }
   };
 
   // ---------------------------------------------------------------- main loop
   bool on_hi_rows = upper || !has_lo;  // which block's rows this wave holds
   begin_rows(on_hi_rows ? bhi : blo);
 
-  // Double-buffered LDS, one barrier per iteration: iteration `it` computes
-  // from slot it%2, then stores the next tile (loaded into registers during
-  // the previous iteration) into the other slot, whose last readers finished
-  // before the previous barrier, then issues the loads for the tile after.
+  // Double-buffered slots, one barrier per iteration: the loads of the next
+  // tile go to the other slot (its last readers finished before the previous
+  // barrier) and land while this tile is computed.
   {
     bool oh;
     int t;
-    if (my_tile(0, oh, t)) {
-      load_tile(oh ? bhi : blo, t);
-      store_tile(oh ? bhi : blo, t, 0);
-    }
-    if (n_iter > 1 && my_tile(1, oh, t)) load_tile(oh ? bhi : blo, t);
+    if (my_tile(0, oh, t)) issue_tile(oh ? bhi : blo, t, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < n_iter; ++it) {
     bool oh;
     int t;
+    if (it + 1 < n_iter && my_tile(it + 1, oh, t)) issue_tile(oh ? bhi : blo, t, (it + 1) & 1);
     if (my_tile(it, oh, t)) {
       const Block& blk = oh ? bhi : blo;
+      if (t * kBN + kBN > blk.own_lo) cache_copy(blk, t, it & 1);
       if (oh && !on_hi_rows) {  // lower group moves from the light block to the heavy one
-        if (qrow0 < len_rows) store_rows(l_run);
+        store_rows(st.l);
         on_hi_rows = true;
         begin_rows(bhi);
       }
@@ -434,39 +433,38 @@ __global__ __launch_bounds__(kThreads) void prefill_fwd_kernel(FwdParams p) {
           compute_tile(blk, t, it & 1, std::false_type{});
       }
     }
-    if (it + 1 < n_iter && my_tile(it + 1, oh, t)) store_tile(oh ? bhi : blo, t, (it + 1) & 1);
-    if (it + 2 < n_iter && my_tile(it + 2, oh, t)) load_tile(oh ? bhi : blo, t);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- merge
   if (!on_hi_rows) {  // lower group never reached the heavy block: finish the light one
-    if (qrow0 < len_rows) store_rows(l_run);
+    store_rows(st.l);
     on_hi_rows = true;
     begin_rows(bhi);   // empty partial state for the heavy block's rows
   }
   // the loop's last barrier has freed the tile buffers
   float* mbuf = reinterpret_cast<float*>(lds) + gw * (2 + D / 2) * 64;
   if (upper) {
-    mbuf[lane] = m_run;
-    mbuf[64 + lane] = l_run;
+    mbuf[lane] = st.m;
+    mbuf[64 + lane] = st.l;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mbuf[(2 + 16 * mb + r) * 64 + lane] = o[mb][r];
+      for (int r = 0; r < 16; ++r) mbuf[(2 + 16 * mb + r) * 64 + lane] = st.o[mb][r];
   }
   __syncthreads();
   if (!upper && qrow0 < len_rows) {
-    const float mb_ = mbuf[lane];
-    const float lb = mbuf[64 + lane];
-    const float m = fmaxf(m_run, mb_);
-    const float fa = __builtin_amdgcn_exp2f(m_run - m);  // 0 if this group saw no tile
-    const float fb = __builtin_amdgcn_exp2f(mb_ - m);
+    const float m2 = mbuf[lane];
+    const float l2 = mbuf[64 + lane];
+    const float m = fmaxf(st.m, m2);
+    const float fa = __builtin_amdgcn_exp2f(st.m - m);  // 0 if this group saw no tile
+    const float fb = __builtin_amdgcn_exp2f(m2 - m);
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mb][r] = o[mb][r] * fa + mbuf[(2 + 16 * mb + r) * 64 + lane] * fb;
-    store_rows(l_run * fa + lb * fb);
+      for (int r = 0; r < 16; ++r) st.o[mb][r] = st.o[mb][r] * fa + mbuf[(2 + 16 * mb + r) * 64 + lane] * fb;
+    store_rows(st.l * fa + l2 * fb);
   }
 }
 
