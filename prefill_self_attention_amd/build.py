@@ -47,6 +47,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out, flush=True)
+    # a kernel whose host-side launch stub was not emitted leaves an undefined
+    # symbol that only shows when the library is loaded: fail here instead
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], stdout=subprocess.PIPE,
+                        stderr=subprocess.STDOUT, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "__device_stub" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("hipcc emitted no launch stub for:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

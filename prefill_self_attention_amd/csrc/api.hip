@@ -119,7 +119,10 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   p.grid_z = nqb;
   // scale * q.k == |scale| * (sign(scale) q).k : keep the exp2-domain factor
   // non-negative so the kernel can take the row max before scaling
-  p.scale_log2 = (float)(std::fabs((double)scale) * 1.4426950408889634);  // log2(e)
+  // |scale| log2(e), kept >= 2^-100 so that a masked score (-inf) always gives
+  // 2^(-inf * c - m) = 0 without a select; below that bound every |s| c is far
+  // under fp32 resolution of 1, so the weights are exactly uniform either way.
+  p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634, 0x1p-100);
   p.neg_q = scale < 0.f ? 1 : 0;
   hipError_t e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
   if (e != hipSuccess) return hip_fail(e);

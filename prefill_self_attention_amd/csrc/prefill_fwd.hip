@@ -43,9 +43,10 @@
 //    query's scores live in lanes l and l^32: one v_permlane32_swap per tile
 //    for the max, none for the running sum until the end, and the O rescale is
 //    a per-lane multiply.
-//  * Online softmax in the exp2 domain with c = |scale| log2(e) >= 0 (a
-//    negative scale flips q's sign instead): max over raw scores, p =
-//    2^(s c - m) as one FMA and one v_exp_f32.  The running max m only moves
+//  * Online softmax in the exp2 domain with c = |scale| log2(e) > 0 (a
+//    negative scale flips q's sign instead; the host keeps c >= 2^-100): max
+//    over raw scores, p = 2^(s c - m) as one FMA and one v_exp_f32, which is 0
+//    for a masked score of -inf.  The running max m only moves
 //    when a tile's max exceeds it by more than 8 (lazy rescale; p stays below
 //    2^8; exact in real arithmetic because O and l share one m).
 //  * O^T = V^T P^T on 32x32x16 MFMA: B = P^T converted to bf16 straight from
@@ -64,6 +65,8 @@
 //    keeping that head's K/V in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "launch.h"
 
@@ -100,6 +103,58 @@ __device__ __forceinline__ float row_sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// LDS reads issued as inline asm.  The main loop's tiles arrive by direct
+// global-to-LDS loads; for a compiler-generated LDS read the compiler cannot
+// always tell that it reads a buffer other than the ones those loads are
+// filling, and then waits for all of them first.  An asm read's result is
+// pending until an lds_wait* call names its registers: LDS operations
+// complete in order, so "at most N outstanding" covers every read issued
+// before the last N.
+template <int kOff>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
+  return r;
+}
+template <int kOff>
+__device__ __forceinline__ s16x4_t lds_read_tr(uint32_t addr) {
+  s16x4_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N, int NV>
+__device__ __forceinline__ void lds_wait_tr(s16x4_t (&r)[NV]) {
+  if constexpr (NV == 2) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+  } else if constexpr (NV == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+  } else {
+    static_assert(NV == 8, "2, 4 or 8 registers");
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+                 : "n"(N));
+  }
+}
+template <int K>
+__device__ __forceinline__ void lds_wait_all(u32x4_t (&a)[K], u32x4_t (&b)[K]) {
+  if constexpr (K == 1) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]));
+  } else if constexpr (K == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
+  } else {
+    static_assert(K == 4, "1, 2 or 4 chunks per lane");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+  }
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2_t two = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
@@ -110,16 +165,24 @@ struct Cfg {
   static constexpr int kCpr = D / 8;                    // 16-byte chunks per row
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kTileBytes = kBN * kRowBytes;    // one K or V tile
-  static constexpr int kSlotBytes = 2 * kTileBytes;     // K tile then V tile
   static constexpr int kRowsPerInst = 1024 / kRowBytes; // rows per 1 KB direct load
   static constexpr int kInstPerTile = kBN / kRowsPerInst;
-  static constexpr int kInstPerWave = kInstPerTile / 4; // per tile, per wave of a group
-  // merge buffer: per upper wave, per lane: m, l and D/2 accumulators
-  static constexpr int kMergeBytes = 4 * (2 + D / 2) * 64 * 4;
-  static constexpr int kLdsBytes = (4 * kSlotBytes > kMergeBytes) ? 4 * kSlotBytes : kMergeBytes;
+  static constexpr int kInstPerWave = kInstPerTile / 4; // per tile and matrix, per wave of a group
+  // LDS map, in tiles: lower group K0 V0 K1 V1 (double buffer); upper group
+  // K ring of 2 and V ring of 3 (its PV step runs one interval behind).
+  static constexpr int kLowerOff = 0;
+  static constexpr int kUpperK = 4 * kTileBytes;
+  static constexpr int kUpperV = 6 * kTileBytes;
+  static constexpr int kLdsBytes = 9 * kTileBytes;
+  static constexpr int kKReadBases = D / 16 < 4 ? D / 16 : 4;  // lane bases of the score operand
+  static constexpr int kVReadsPerStep = 2 * (D / 32);          // transpose reads per 16-key step
+  // merge buffer per upper wave (per lane: m, l and D/2 accumulators)
+  static constexpr int kMergeWaveFloats = (2 + D / 2) * 64;
+  static_assert(4 * kMergeWaveFloats * 4 <= kLdsBytes, "merge buffers must fit the tile area");
 };
 
-// 16-byte chunk slot of chunk c in row r (XOR swizzle, stays inside the row)
+// 16-byte chunk slot of chunk c in row r (XOR swizzle, stays inside the row;
+// depends on r % 8 only)
 template <int D>
 __device__ __forceinline__ int chunk_slot(int r, int c) {
   return c ^ ((((r & 3) << 1) | ((r >> 2) & 1)) & (Cfg<D>::kCpr - 1));
@@ -143,6 +206,27 @@ __device__ __forceinline__ Block make_block(int qb, int len, int pre) {
   return k;
 }
 
+// Tile of a group at position `it` of its list: tile index t of block qb (the
+// heavy block qb_hi or the light block z), and whether there is one.  A free
+// function of plain values, branch-free, with the block index formed by
+// arithmetic: selects between captured variables get folded into selects of
+// their addresses, which pins them (and whole closures) in scratch memory.
+struct Pick {
+  int t, qb;
+  bool on_hi, valid;
+};
+
+__device__ __forceinline__ Pick pick_tile(int it, bool upper, int n_up, int e_lo, int e_hi,
+                                          int z, int qb_hi) {
+  Pick r;
+  const bool hi = upper || it >= e_lo;
+  r.on_hi = hi;
+  r.t = upper ? it : (hi ? n_up + (it - e_lo) : it);
+  r.valid = upper ? (it < n_up) : (!hi || r.t < e_hi);
+  r.qb = z + (hi ? qb_hi - z : 0);
+  return r;
+}
+
 // State of a wave's 32 query rows.
 template <int D>
 struct Rows {
@@ -151,15 +235,28 @@ struct Rows {
   float m, l;
 };
 
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 template <int D, bool kChunked>
 __global__ __launch_bounds__(kThreads)
 void prefill_fwd_kernel(FwdParams p) {
   using C = Cfg<D>;
+  // Every LDS read in the main loop is inline asm (lds_read_* above), so the
+  // compiler places no wait for the direct loads in flight; each read is made
+  // valid by an explicit lgkmcnt wait tied to its registers.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int z = blockIdx.z;
+  // raw id builtins: the device library's id helpers are built with IEEE mode
+  // on and would not inline into this IEEE-off kernel
+  const int h = __builtin_amdgcn_workgroup_id_x();
+  const int b = __builtin_amdgcn_workgroup_id_y();
+  const int z = __builtin_amdgcn_workgroup_id_z();
   const int64_t H = p.num_heads;
 
   const int seq_start = p.cu[b];
@@ -173,9 +270,10 @@ void prefill_fwd_kernel(FwdParams p) {
   const Block bhi = make_block(qb_hi, len, pre);
   const int e_lo = has_lo ? blo.ntiles : 0;
   const int e_hi = bhi.ntiles;
-  const int n_iter = (e_lo + e_hi + 1) / 2;  // tiles of the upper group
+  const int n_up = (e_lo + e_hi + 1) / 2;  // tiles of the upper group
+  const int n_lo = e_lo + e_hi - n_up;     // tiles of the lower group (<= n_up)
 
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int ql = lane & 31;
@@ -183,23 +281,13 @@ void prefill_fwd_kernel(FwdParams p) {
   const bool upper = wave >= 4;
   const int gw = wave & 3;               // wave within its group
 
-  uint8_t* const grp_lds = lds + (upper ? 2 * C::kSlotBytes : 0);
-
   const int64_t row_stride = H * D;      // elements between consecutive tokens
   const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
   const uint16_t* __restrict__ vin = p.v + (int64_t)h * D;
   const int64_t cache_base = kChunked ? ((int64_t)b * H + h) * p.cap * D
                                       : (int64_t)seq_start * H * D + (int64_t)h * len * D;
-  const float c = p.scale_log2;          // |scale| * log2(e) >= 0
-
-  // ---------------------------------------------------------------- schedule
-  auto my_tile = [&](int it, bool& on_hi, int& t) -> bool {
-    if (upper) { on_hi = true; t = it; return it < n_iter; }
-    if (it < e_lo) { on_hi = false; t = it; return true; }
-    on_hi = true;
-    t = n_iter + (it - e_lo);
-    return t < e_hi;
-  };
+  const float c = p.scale_log2;          // |scale| * log2(e), > 0
+  const uint32_t lds0 = lds_addr(lds);
 
   // ---------------------------------------------------------------- staging
   // Wave gw of a group issues instructions j = 4 i + gw (i < kInstPerWave) per
@@ -210,15 +298,15 @@ void prefill_fwd_kernel(FwdParams p) {
   const int lrow = lane / C::kCpr;
   const int lslot = lane % C::kCpr;
 
-  auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) {
+  auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) __attribute__((always_inline)) {
     if (kChunked && kp < pre) return cache + cache_base + (int64_t)kp * D;
     return in + (int64_t)(seq_start + kp - pre) * row_stride;
   };
 
-  auto issue_tile = [&](const Block& blk, int t, int slot) {
+  auto issue_tile = [&](const Block blk, int t, int k_off, int v_off) __attribute__((always_inline)) {
     const int t0 = t * kBN;
-    uint8_t* const k_dst = grp_lds + slot * C::kSlotBytes;
-    uint8_t* const v_dst = k_dst + C::kTileBytes;
+    uint8_t* const k_dst = lds + k_off;
+    uint8_t* const v_dst = lds + v_off;
     const bool full = t0 + kBN <= blk.key_end;
     const bool all_new = !kChunked || t0 >= pre;
     const bool all_cached = kChunked && t0 + kBN <= pre;
@@ -252,19 +340,29 @@ void prefill_fwd_kernel(FwdParams p) {
   };
 
   // copy the tile's new-token rows of blk from LDS to the cache (group-wide)
-  auto cache_copy = [&](const Block& blk, int t, int slot) {
+  auto cache_copy = [&](const Block blk, int t, int k_off, int v_off) __attribute__((always_inline)) {
+    constexpr int kPer = C::kCpr / 4;    // chunks per lane and matrix
     const int t0 = t * kBN;
-    const uint8_t* const k_src = grp_lds + slot * C::kSlotBytes;
-    const uint8_t* const v_src = k_src + C::kTileBytes;
     const int gl = 64 * gw + lane;       // 0..255 within the group
-    for (int idx = gl; idx < kBN * C::kCpr; idx += kGroupThreads) {
+    u32x4_t kr[kPer], vr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = gl + kGroupThreads * i;
+      const int row = idx / C::kCpr, ch = idx % C::kCpr;
+      const uint32_t so = row * C::kRowBytes + 16 * chunk_slot<D>(row, ch);
+      kr[i] = lds_read_b128<0>(lds0 + k_off + so);
+      vr[i] = lds_read_b128<0>(lds0 + v_off + so);
+    }
+    lds_wait_all(kr, vr);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = gl + kGroupThreads * i;
       const int row = idx / C::kCpr, ch = idx % C::kCpr;
       const int kp = t0 + row;
       if (kp >= blk.own_lo && kp < blk.key_end) {
-        const int so = row * C::kRowBytes + 16 * chunk_slot<D>(row, ch);
         const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
-        *(u32x4_t*)(p.kc + dst) = *(const u32x4_t*)(k_src + so);
-        *(u32x4_t*)(p.vc + dst) = *(const u32x4_t*)(v_src + so);
+        *(u32x4_t*)(p.kc + dst) = kr[i];
+        *(u32x4_t*)(p.vc + dst) = vr[i];
       }
     }
   };
@@ -273,7 +371,7 @@ void prefill_fwd_kernel(FwdParams p) {
   Rows<D> st;
   int qrow0, len_rows;  // first local row of the wave (32 rows); rows < len_rows exist
 
-  auto begin_rows = [&](const Block& blk) {
+  auto begin_rows = [&](const Block& blk) __attribute__((always_inline)) {
     qrow0 = blk.q0 + 32 * gw;
     len_rows = blk.qend;
     const int row = qrow0 + ql;
@@ -291,7 +389,7 @@ void prefill_fwd_kernel(FwdParams p) {
     st.l = 0.f;
   };
 
-  auto store_rows = [&](float l_part) {
+  auto store_rows = [&](float l_part) __attribute__((always_inline)) {
     const int row = qrow0 + ql;
     const float inv = 1.f / row_sum_halves(l_part);
     if (row >= len_rows) return;
@@ -306,26 +404,63 @@ void prefill_fwd_kernel(FwdParams p) {
       }
   };
 
-  // One 64-key tile: S^T = K Q^T (two 32-key blocks), online softmax over the
-  // 64 keys, O^T += V^T P^T.
-  auto compute_tile = [&](const Block& blk, int t, int slot, auto mask_tag) {
+  // Lane parts of the LDS read addresses (byte offsets within a tile).
+  //  Score operand: lane l reads key row kr = 32 kb + l%32, chunk 2 ks + l/32;
+  //  the swizzle depends on kr % 8 = l % 8 only, and for ks = j + 4 m the
+  //  slot is 8 m + slot(2 j + l/32), so bases j < 4 plus immediates cover all.
+  //  PV operand: lane L of 16-lane group G points at 4 consecutive d of key
+  //  row 16 g + 8 r + 4 (G/2) + (L%16)/4 at d = 32 mb + 16 (G%2) + 4 (L%4) and
+  //  receives the 4 keys {16 g + 8 r + 4 (G/2) + j} at its own d = 32 mb + L%32;
+  //  chunk 4 mb + c lands in slot 8 (mb/2) + slot(4 (mb%2) + c), so two bases
+  //  (mb even / odd) plus immediates cover all.
+  uint32_t kbase[C::kKReadBases];
+#pragma unroll
+  for (int j = 0; j < C::kKReadBases; ++j) kbase[j] = ql * C::kRowBytes + 16 * chunk_slot<D>(ql, 2 * j + hh);
+  uint32_t vbase[2];
+  {
+    const int tg = lane >> 4, tl = lane & 15;
+    const int vrow0 = 4 * (tg >> 1) + (tl >> 2);
+    const int vd0 = 16 * (tg & 1) + 4 * (tl & 3);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = 32 * e + vd0;
+      vbase[e] = vrow0 * C::kRowBytes + 16 * chunk_slot<D>(vrow0, (d >> 3) & (C::kCpr - 1)) + 2 * (d & 7);
+    }
+  }
+
+  // S^T = K Q^T for one 64-key tile (two 32-key blocks), K from LDS at k_off.
+  auto score = [&](int k_off, f32x16_t (&s)[2]) __attribute__((always_inline)) {
+    constexpr int NK = D / 16;
+    uint32_t kb_addr[C::kKReadBases];
+#pragma unroll
+    for (int j = 0; j < C::kKReadBases; ++j) kb_addr[j] = lds0 + k_off + kbase[j];
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
+    u32x4_t a[NK][2];
+    auto rd = [&](auto ks_tag) __attribute__((always_inline)) {
+      constexpr int ks = decltype(ks_tag)::value;
+      constexpr int o = 128 * (ks >> 2);
+      a[ks][0] = lds_read_b128<o>(kb_addr[ks & 3]);
+      a[ks][1] = lds_read_b128<o + 32 * C::kRowBytes>(kb_addr[ks & 3]);
+    };
+    constexpr int kAhead = NK < 4 ? NK : 4;  // 16-d steps in flight
+    static_for<0, kAhead>(rd);
+    static_for<0, NK>([&](auto ks_tag) __attribute__((always_inline)) {
+      constexpr int ks = decltype(ks_tag)::value;
+      constexpr int later = (NK - 1 - ks) < (kAhead - 1) ? (NK - 1 - ks) : (kAhead - 1);
+      lds_wait<2 * later>(a[ks][0], a[ks][1]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks][0]), st.q[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks][1]), st.q[ks], s[1], 0, 0, 0);
+      if constexpr (ks + kAhead < NK) rd(std::integral_constant<int, ks + kAhead>{});
+    });
+  };
+
+  // Online softmax over one tile's scores: updates m, l (and rescales O when m
+  // moves), returns P^T as the PV B operand.
+  auto softmax = [&](f32x16_t (&s)[2], const Block blk, int t, auto mask_tag, bf16x8_t (&pb)[4]) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const uint8_t* const k_lds = grp_lds + slot * C::kSlotBytes;
-    const uint8_t* const v_lds = k_lds + C::kTileBytes;
     const int t0 = t * kBN;
     const int qa = pre + qrow0 + ql;  // this lane's absolute query position
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const int kr = 32 * kb + ql;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, *(const u32x4_t*)(k_lds + kr * C::kRowBytes + 16 * chunk_slot<D>(kr, 2 * ks + hh)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.q[ks], s[kb], 0, 0, 0);
-      }
-    }
     if constexpr (kMask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -354,7 +489,6 @@ void prefill_fwd_kernel(FwdParams p) {
       st.m = m_new;
     }
     const float neg_m = -st.m;
-    bf16x8_t pb[4];
     float ls[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -362,9 +496,7 @@ void prefill_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float sv = s[g >> 1][8 * (g & 1) + i];
-        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, neg_m));
-        if constexpr (kMask) x = (sv == kNegInf) ? 0.f : x;  // also right for c == 0
-        e[i] = x;
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, neg_m));  // c > 0: masked -> 0
       }
       ls[g] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       u32x4_t w = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
@@ -372,65 +504,126 @@ void prefill_fwd_kernel(FwdParams p) {
       pb[g] = __builtin_bit_cast(bf16x8_t, w);
     }
     st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // V^T operand by transpose read: lane L of 16-lane group G points at 4
-    // consecutive d of key row 16g + 8r + 4*(G/2) + (L%16)/4 at
-    // d = 32 mb + 16*(G%2) + 4*(L%4), and receives the 4 keys
-    // {16g + 8r + 4*(G/2) + j} at its own d = 32 mb + L%32.
-    const int tg = lane >> 4, tl = lane & 15;
-    const int vrow0 = 4 * (tg >> 1) + (tl >> 2);
-    const int vd0 = 16 * (tg & 1) + 4 * (tl & 3);
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        s16x4_t part[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int row = 16 * g + 8 * rr + vrow0;
-          const int d = 32 * mb + vd0;
-          const uint8_t* a = v_lds + row * C::kRowBytes + 16 * chunk_slot<D>(row, d >> 3) + 2 * (d & 7);
-          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a);
-        }
-        const bf16x8_t vf =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // O^T += V^T P^T for one tile, V from LDS at v_off; 16-key steps g outer,
+  // the D/32 accumulators inner (no back-to-back dependent MFMAs).
+  auto pv = [&](int v_off, const bf16x8_t (&pb)[4]) __attribute__((always_inline)) {
+    constexpr int NV = C::kVReadsPerStep;
+    const uint32_t va0 = lds0 + v_off + vbase[0];
+    const uint32_t va1 = lds0 + v_off + vbase[1];
+    s16x4_t vt[4][NV];
+    auto rd = [&](auto g_tag) __attribute__((always_inline)) {
+      constexpr int g = decltype(g_tag)::value;
+      static_for<0, D / 32>([&](auto mb_tag) __attribute__((always_inline)) {
+        constexpr int mb = decltype(mb_tag)::value;
+        constexpr int o = 128 * (mb >> 1) + 16 * g * C::kRowBytes;
+        const uint32_t a = (mb & 1) ? va1 : va0;
+        vt[g][2 * mb] = lds_read_tr<o>(a);
+        vt[g][2 * mb + 1] = lds_read_tr<o + 8 * C::kRowBytes>(a);
+      });
+    };
+    rd(std::integral_constant<int, 0>{});
+    rd(std::integral_constant<int, 1>{});
+    static_for<0, 4>([&](auto g_tag) __attribute__((always_inline)) {
+      constexpr int g = decltype(g_tag)::value;
+      lds_wait_tr<(g < 3 ? NV : 0)>(vt[g]);
+      static_for<0, D / 32>([&](auto mb_tag) __attribute__((always_inline)) {
+        constexpr int mb = decltype(mb_tag)::value;
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(vt[g][2 * mb], vt[g][2 * mb + 1], 0, 1, 2, 3, 4, 5, 6, 7));
         st.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[g], st.o[mb], 0, 0, 0);
-      }
+      });
+      if constexpr (g + 2 < 4) rd(std::integral_constant<int, g + 2>{});
+    });
+  };
+
+  // does this wave have rows that see some key of tile t, and must it mask?
+  auto tile_use = [&](const Block blk, int t, bool& use, bool& mask) __attribute__((always_inline)) {
+    const int t0 = t * kBN;
+    const int qa0 = pre + qrow0;
+    use = qrow0 < len_rows && t0 <= qa0 + 31;
+    mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > blk.key_end);
   };
 
   // ---------------------------------------------------------------- main loop
+  // Interval j ends with one barrier.  Lower group: tile j as S, softmax, PV.
+  // Upper group: PV of its tile j-1 (P kept in registers, V in a ring of
+  // three), then S and softmax of tile j.  On each SIMD one wave's softmax so
+  // runs beside the other's MFMAs.  Loads of both groups' tile j+1 are issued
+  // at the start of interval j into buffers whose last readers finished
+  // before the previous barrier.
   bool on_hi_rows = upper || !has_lo;  // which block's rows this wave holds
-  begin_rows(on_hi_rows ? bhi : blo);
+  begin_rows(make_block(on_hi_rows ? +qb_hi : +z, len, pre));
 
-  // Double-buffered slots, one barrier per iteration: the loads of the next
-  // tile go to the other slot (its last readers finished before the previous
-  // barrier) and land while this tile is computed.
+  auto lower_k = [&](int j) { return C::kLowerOff + (j & 1) * 2 * C::kTileBytes; };
   {
-    bool oh;
-    int t;
-    if (my_tile(0, oh, t)) issue_tile(oh ? bhi : blo, t, 0);
+    const Pick p0 = pick_tile(0, upper, n_up, e_lo, e_hi, z, qb_hi);
+    if (p0.valid) {
+      if (upper) issue_tile(make_block(p0.qb, len, pre), p0.t, C::kUpperK, C::kUpperV);
+      else issue_tile(make_block(p0.qb, len, pre), p0.t, lower_k(0), lower_k(0) + C::kTileBytes);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    bool oh;
-    int t;
-    if (it + 1 < n_iter && my_tile(it + 1, oh, t)) issue_tile(oh ? bhi : blo, t, (it + 1) & 1);
-    if (my_tile(it, oh, t)) {
-      const Block& blk = oh ? bhi : blo;
-      if (t * kBN + kBN > blk.own_lo) cache_copy(blk, t, it & 1);
-      if (oh && !on_hi_rows) {  // lower group moves from the light block to the heavy one
+
+  bf16x8_t p_prev[4];
+  bool have_prev = false;
+  int v_prev = 2, v_cur = 0, v_next = 1;  // upper V ring: tiles j-1, j, j+1
+  for (int j = 0; j <= n_up; ++j) {
+    if (upper) {
+      if (j + 1 < n_up) {
+        const Pick nx = pick_tile(j + 1, true, n_up, e_lo, e_hi, z, qb_hi);
+        issue_tile(make_block(nx.qb, len, pre), nx.t, C::kUpperK + ((j + 1) & 1) * C::kTileBytes,
+                   C::kUpperV + v_next * C::kTileBytes);
+      }
+      if (have_prev) pv(C::kUpperV + v_prev * C::kTileBytes, p_prev);
+      have_prev = false;
+      if (j < n_up) {
+        const Block blk = bhi;
+        if (j * kBN + kBN > blk.own_lo)  // a self-paired block's first tiles hold new tokens
+          cache_copy(blk, j, C::kUpperK + (j & 1) * C::kTileBytes, C::kUpperV + v_cur * C::kTileBytes);
+        bool use, mask;
+        tile_use(blk, j, use, mask);
+        if (use) {
+          f32x16_t s[2];
+          score(C::kUpperK + (j & 1) * C::kTileBytes, s);
+          if (mask)
+            softmax(s, blk, j, std::true_type{}, p_prev);
+          else
+            softmax(s, blk, j, std::false_type{}, p_prev);
+          have_prev = true;
+        }
+      }
+      const int r = v_prev;
+      v_prev = v_cur;
+      v_cur = v_next;
+      v_next = r;
+    } else if (j < n_lo) {
+      if (j + 1 < n_lo) {
+        const Pick nx = pick_tile(j + 1, false, n_up, e_lo, e_hi, z, qb_hi);
+        issue_tile(make_block(nx.qb, len, pre), nx.t, lower_k(j + 1), lower_k(j + 1) + C::kTileBytes);
+      }
+      const Pick pk = pick_tile(j, false, n_up, e_lo, e_hi, z, qb_hi);
+      const Block blk = make_block(pk.qb, len, pre);
+      const int t = pk.t;
+      if (t * kBN + kBN > blk.own_lo) cache_copy(blk, t, lower_k(j), lower_k(j) + C::kTileBytes);
+      if (pk.on_hi && !on_hi_rows) {  // lower group moves from the light block to the heavy one
         store_rows(st.l);
         on_hi_rows = true;
         begin_rows(bhi);
       }
-      const int t0 = t * kBN;
-      const int qa0 = pre + qrow0;
-      if (qrow0 < len_rows && t0 <= qa0 + 31) {  // rows present and not all above the tile
-        const bool need_mask = (t0 + kBN - 1 > qa0) || (t0 + kBN > blk.key_end);
-        if (need_mask)
-          compute_tile(blk, t, it & 1, std::true_type{});
+      bool use, mask;
+      tile_use(blk, t, use, mask);
+      if (use) {
+        f32x16_t s[2];
+        bf16x8_t pb[4];
+        score(lower_k(j), s);
+        if (mask)
+          softmax(s, blk, t, std::true_type{}, pb);
         else
-          compute_tile(blk, t, it & 1, std::false_type{});
+          softmax(s, blk, t, std::false_type{}, pb);
+        pv(lower_k(j) + C::kTileBytes, pb);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
@@ -444,7 +637,7 @@ void prefill_fwd_kernel(FwdParams p) {
     begin_rows(bhi);   // empty partial state for the heavy block's rows
   }
   // the loop's last barrier has freed the tile buffers
-  float* mbuf = reinterpret_cast<float*>(lds) + gw * (2 + D / 2) * 64;
+  float* mbuf = reinterpret_cast<float*>(lds) + gw * C::kMergeWaveFloats;
   if (upper) {
     mbuf[lane] = st.m;
     mbuf[64 + lane] = st.l;
