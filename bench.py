@@ -104,6 +104,101 @@ def cpu_baseline(w, q, k, v, flops):
                       % (w.num_tokens, w.num_heads, w.head_dim)}
 
 
+def timed(fn, steps, warmup):
+    """Mean and sorted per-launch times (ms) of fn on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def bench_chunked(args, wl, P):
+    """The heaviest step of the chunked workload (last 512-token chunk of the
+    8192-token prompt beside the 64 decode rows) and, separately, the 64
+    decode rows alone: TFLOP/s over the step's causal pairs and the decode
+    share as GB/s of cached K/V read."""
+    import torch
+    dev = torch.device("cuda:0")
+    H, D, R = wl.num_heads, wl.head_dim, len(wl.contexts)
+    t = wl.tensors()
+    kc = torch.zeros((1 + R, H, wl.cap, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    for r, ctx in enumerate(wl.contexts):
+        kc[1 + r, :, :ctx] = t["pre_k"][r].to(dev)
+        vc[1 + r, :, :ctx] = t["pre_v"][r].to(dev)
+    c = wl.num_chunks - 1
+    st = wl.step(c)
+    sl = slice(c * wl.chunk_len, (c + 1) * wl.chunk_len)
+    # the prompt's earlier chunks are already in the cache
+    kc[0, :, :c * wl.chunk_len] = t["pk"][:c * wl.chunk_len].transpose(0, 1).to(dev)
+    vc[0, :, :c * wl.chunk_len] = t["pv"][:c * wl.chunk_len].transpose(0, 1).to(dev)
+    q = torch.cat([t["pq"][sl], t["dq"]]).to(dev)
+    k = torch.cat([t["pk"][sl], t["dk"]]).to(dev)
+    v = torch.cat([t["pv"][sl], t["dv"]]).to(dev)
+    out = torch.empty_like(q)
+    cu = torch.tensor(st.cu_seqlens, dtype=torch.int32, device=dev)
+    pre = torch.tensor(st.prefix_lens, dtype=torch.int32, device=dev)
+
+    def step():
+        P.prefill_attn_chunked(q, k, v, cu, kc, vc, out, pre, scale=st.scale, max_seqlen=wl.chunk_len)
+
+    ms, launches = timed(step, args.steps, args.warmup)
+    pairs = causal_pairs(st.lengths, st.prefix_lens)
+    flops = 4.0 * D * H * pairs
+    # decode rows alone: rows 1..R of the cache, one new token each
+    qd, kd, vd = t["dq"].to(dev), t["dk"].to(dev), t["dv"].to(dev)
+    outd = torch.empty_like(qd)
+    cud = torch.arange(R + 1, dtype=torch.int32, device=dev)
+    pred = torch.tensor(wl.contexts, dtype=torch.int32, device=dev)
+    kcd, vcd = kc[1:], vc[1:]
+
+    def decode():
+        P.prefill_attn_chunked(qd, kd, vd, cud, kcd, vcd, outd, pred, scale=st.scale, max_seqlen=1)
+
+    msd, launchesd = timed(decode, args.steps, args.warmup)
+    dec_bytes = 2.0 * sum(c_ + 1 for c_ in wl.contexts) * H * D * 2  # K and V of every context row read
+    value = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "step": "chunk %d of %d (prefix %d) + %d decode rows" % (c, wl.num_chunks, c * wl.chunk_len, R),
+                   "tokens": int(q.shape[0]), "num_heads": H, "head_dim": D, "causal": True,
+                   "kv_cache_write": True, "scale": st.scale},
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "launch_us": {"mean": round(sum(launches) / len(launches) * 1e3, 2),
+                      "median": round(launches[len(launches) // 2] * 1e3, 2)},
+        "decode_only": {"rows": R, "context_tokens": sum(wl.contexts),
+                        "launch_us_mean": round(sum(launchesd) / len(launchesd) * 1e3, 2),
+                        "kv_read_gbps": round(dec_bytes / (msd * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_8tbs": round(dec_bytes / (msd * 1e-3) / 8e12, 4)},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -120,8 +215,9 @@ def main():
     P.load()
 
     w = I.workload(args.workload)
-    if not isinstance(w, I.Varlen):
-        raise SystemExit("bench.py times varlen workloads; chunked steps are covered by tests")
+    if isinstance(w, I.ChunkedWorkload):
+        print(json.dumps(bench_chunked(args, w, P)))
+        return
     q, k, v = w.tensors()
     N, H, D = q.shape
     dev = torch.device("cuda:0")
