@@ -44,13 +44,13 @@ def _load():
     lib = ctypes.CDLL(_LIB)
     p = ctypes.c_void_p
     i32 = ctypes.c_int32
-    lib.oracle_prefill_varlen.argtypes = [p, p, p, p, i32, i32, i32, ctypes.c_float,
+    lib.oracle_prefill_varlen.argtypes = [p, p, p, p, i32, i32, i32, i32, ctypes.c_float,
                                           p, p, p, p]
     lib.oracle_prefill_varlen.restype = ctypes.c_int
-    lib.oracle_prefill_chunked.argtypes = [p, p, p, p, i32, i32, i32, i32, p,
+    lib.oracle_prefill_chunked.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p,
                                            ctypes.c_float, p, p, p, p]
     lib.oracle_prefill_chunked.restype = ctypes.c_int
-    lib.oracle_prefill_rows.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, p,
+    lib.oracle_prefill_rows.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, p,
                                         ctypes.c_float, p, ctypes.c_int64, p]
     lib.oracle_prefill_rows.restype = ctypes.c_int
     lib.oracle_cache_image.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
@@ -84,6 +84,16 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _heads(q, k, v):
+    """(H, HK): query heads and K/V heads; H must be a multiple of HK [P5 §2.4]."""
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape:
+        raise ValueError("q [N, H, D], k and v [N, HK, D] expected")
+    N, H, D = q.shape
+    if k.shape[0] != N or k.shape[2] != D or H % k.shape[1] != 0:
+        raise ValueError("k / v must be [N, HK, D] with HK dividing H")
+    return H, k.shape[1]
+
+
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError("%s: oracle rejected the metadata (code %d)" % (what, rc))
@@ -97,7 +107,9 @@ def prefill_varlen(q, k, v, cu_seqlens, scale, k_cache=None, v_cache=None,
                    want_probs=False):
     """Varlen causal prefill.
 
-    q, k, v: bf16 [N, H, D] (uint16 bits or torch.bfloat16).
+    q: bf16 [N, H, D]; k, v: bf16 [N, HK, D] with HK dividing H (HK < H:
+    grouped K/V heads, query head h reads K/V head h // (H // HK)); uint16
+    bits or torch.bfloat16.
     cu_seqlens: int [B + 1].  scale: the float32 value the GPU receives.
     k_cache, v_cache: optional flat bf16 buffers (>= N*H*D elements) holding
     the caller's contents; copies receive the cache image and are returned.
@@ -106,6 +118,7 @@ def prefill_varlen(q, k, v, cu_seqlens, scale, k_cache=None, v_cache=None,
     q, k, v = _u16(q), _u16(k), _u16(v)
     cu = _i32(cu_seqlens)
     N, H, D = q.shape
+    _, HK = _heads(q, k, v)
     B = cu.shape[0] - 1
     if cu[-1] != N:
         raise ValueError("cu_seqlens[-1] must equal the number of tokens")
@@ -119,7 +132,7 @@ def prefill_varlen(q, k, v, cu_seqlens, scale, k_cache=None, v_cache=None,
         n = int(cu[1] - cu[0]) if B == 1 else 0
         probs = np.zeros((H, n, n), dtype=np.float64)
     rc = _load().oracle_prefill_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, D, ctypes.c_float(scale),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, HK, D, ctypes.c_float(scale),
         _ptr(out), _ptr(kc) if kc is not None else None,
         _ptr(vc) if vc is not None else None,
         _ptr(probs) if probs is not None else None)
@@ -131,7 +144,7 @@ def prefill_chunked(q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache, scale,
                     want_probs=False):
     """Chunked prefill with a cached prefix per sequence.
 
-    k_cache, v_cache: bf16 [B, H, cap, D] holding the prefix; copies receive
+    k_cache, v_cache: bf16 [B, HK, cap, D] holding the prefix; copies receive
     the image with the new tokens appended and are returned.
     Returns (out float64 [N,H,D], k_cache_image, v_cache_image, probs).
     """
@@ -141,17 +154,18 @@ def prefill_chunked(q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache, scale,
     kc = _u16(k_cache).copy()
     vc = _u16(v_cache).copy()
     N, H, D = q.shape
+    _, HK = _heads(q, k, v)
     B = cu.shape[0] - 1
     cap = kc.shape[2]
-    if kc.shape != (B, H, cap, D) or vc.shape != kc.shape:
-        raise ValueError("cache must be [B, H, cap, D]")
+    if kc.shape != (B, HK, cap, D) or vc.shape != kc.shape:
+        raise ValueError("cache must be [B, HK, cap, D]")
     out = np.zeros((N, H, D), dtype=np.float64)
     probs = None
     if want_probs:
         n = int(cu[1] - cu[0]) if B == 1 else 0
         probs = np.zeros((H, n, int(pre[0]) + n if B == 1 else 0), dtype=np.float64)
     rc = _load().oracle_prefill_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, D, cap, _ptr(pre),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, HK, D, cap, _ptr(pre),
         ctypes.c_float(scale), _ptr(out), _ptr(kc), _ptr(vc),
         _ptr(probs) if probs is not None else None)
     _check(rc, "prefill_chunked")
@@ -167,6 +181,7 @@ def prefill_rows(q, k, v, cu_seqlens, scale, rows, prefix_lens=None,
     q, k, v = _u16(q), _u16(k), _u16(v)
     cu = _i32(cu_seqlens)
     N, H, D = q.shape
+    _, HK = _heads(q, k, v)
     B = cu.shape[0] - 1
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     out = np.zeros((rows.shape[0], H, D), dtype=np.float64)
@@ -178,7 +193,7 @@ def prefill_rows(q, k, v, cu_seqlens, scale, rows, prefix_lens=None,
         vc = _u16(v_cache)
         cap = kc.shape[2]
     rc = _load().oracle_prefill_rows(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, D, cap,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, HK, D, cap,
         _ptr(pre) if pre is not None else None,
         _ptr(kc) if kc is not None else None,
         _ptr(vc) if vc is not None else None,
@@ -190,7 +205,8 @@ def prefill_rows(q, k, v, cu_seqlens, scale, rows, prefix_lens=None,
 def cache_image(k, v, cu_seqlens, k_cache, v_cache, prefix_lens=None):
     """The cache image only (no attention): copies of k_cache / v_cache with
     the new tokens' K/V placed.  Varlen layout if prefix_lens is None (flat
-    buffers of >= N*H*D elements), else chunked [B, H, cap, D]."""
+    buffers of >= N*HK*D elements), else chunked [B, HK, cap, D]; HK is k's
+    head count."""
     k, v = _u16(k), _u16(v)
     cu = _i32(cu_seqlens)
     N, H, D = k.shape

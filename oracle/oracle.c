@@ -31,6 +31,13 @@
  * pairs only; each pair is computed by the same sequential loops, so the
  * result does not depend on the thread count.
  *
+ * Grouped key/value heads [P5 §2.4: grouped-query attention keeps fewer K/V
+ * heads than query heads, 32 -> 8 in its example, to shrink the cache]: K, V
+ * and the cache carry num_kv_heads heads, and query head h reads K/V head
+ * h / (num_heads / num_kv_heads) -- consecutive query heads share one K/V head
+ * (the page does not spell out the grouping; this is the plain reading).
+ * num_kv_heads == num_heads is ordinary multi-head attention.
+ *
  * Parity status: every function here is pinned by tests/test_oracle.py
  * (brute force, a library routine, closed forms, invariants); none is
  * "parity unpinned".
@@ -98,28 +105,32 @@ static void attend_row(const uint16_t *q, const uint16_t *const *kbase,
  * inputs; prefix tokens from the cache laid out [B, H, cap, D].
  */
 typedef struct {
-    const uint16_t *q, *k, *v;        /* [N, H, D] new tokens */
+    const uint16_t *q, *k, *v;        /* q [N, H, D]; k, v [N, HK, D] new tokens */
     const int32_t *cu;                /* [B + 1] */
     const int32_t *prefix;            /* [B] or NULL (no cached prefix) */
     const uint16_t *kc_in, *vc_in;    /* chunked cache contents before the call */
     int32_t B, H, D, cap;
     double scale;
+    int32_t HK;                       /* K/V heads; H is a multiple of HK */
 } problem_t;
+
+/* K/V head read by query head h */
+static int64_t kv_head(const problem_t *P, int64_t h) { return h / (P->H / P->HK); }
 
 static void gather_keys(const problem_t *P, int b, int h, int64_t n_keys,
                         const uint16_t **kp, const uint16_t **vp)
 {
-    const int64_t H = P->H, D = P->D;
+    const int64_t HK = P->HK, D = P->D, g = kv_head(P, h);
     const int64_t pre = P->prefix ? P->prefix[b] : 0;
     for (int64_t j = 0; j < n_keys; ++j) {
         if (j < pre) {
-            int64_t off = (((int64_t)b * H + h) * P->cap + j) * D;
+            int64_t off = (((int64_t)b * HK + g) * P->cap + j) * D;
             kp[j] = P->kc_in + off;
             vp[j] = P->vc_in + off;
         } else {
             int64_t tok = (int64_t)P->cu[b] + (j - pre);
-            kp[j] = P->k + (tok * H + h) * D;
-            vp[j] = P->v + (tok * H + h) * D;
+            kp[j] = P->k + (tok * HK + g) * D;
+            vp[j] = P->v + (tok * HK + g) * D;
         }
     }
 }
@@ -182,25 +193,26 @@ static int run_all(const problem_t *P, double *out, double *probs)
  * Q [P2 §1.3], head-major [batch, heads, seq, head_dim] [P2 §1.3; P4 §3.2;
  * P1 §3 recommends the head-major layout].  Prefill writes them for every
  * prompt position [P5 §1.1; P1 §4].
- *   varlen : sequence b's block is [H, len_b, D] starting at element cu_b*H*D
- *   chunked: [B, H, cap, D]; own token t of sequence b lands at position
+ *   varlen : sequence b's block is [HK, len_b, D] starting at element cu_b*HK*D
+ *   chunked: [B, HK, cap, D]; own token t of sequence b lands at position
  *            prefix_b + t.
+ * (HK = num_kv_heads; one cache row per K/V head.)
  * Bits are copied unchanged; every other element is left as the caller
  * filled it.
  */
 static void write_cache(const problem_t *P, uint16_t *kc, uint16_t *vc)
 {
-    const int64_t H = P->H, D = P->D;
+    const int64_t HK = P->HK, D = P->D;
     for (int b = 0; b < P->B; ++b) {
         const int64_t n = (int64_t)P->cu[b + 1] - P->cu[b];
-        for (int64_t h = 0; h < H; ++h)
+        for (int64_t h = 0; h < HK; ++h)
             for (int64_t t = 0; t < n; ++t) {
-                const int64_t src = (((int64_t)P->cu[b] + t) * H + h) * D;
+                const int64_t src = (((int64_t)P->cu[b] + t) * HK + h) * D;
                 int64_t dst;
                 if (P->prefix)
-                    dst = (((int64_t)b * H + h) * P->cap + P->prefix[b] + t) * D;
+                    dst = (((int64_t)b * HK + h) * P->cap + P->prefix[b] + t) * D;
                 else
-                    dst = (int64_t)P->cu[b] * H * D + (h * n + t) * D;
+                    dst = (int64_t)P->cu[b] * HK * D + (h * n + t) * D;
                 memcpy(kc + dst, P->k + src, sizeof(uint16_t) * (size_t)D);
                 memcpy(vc + dst, P->v + src, sizeof(uint16_t) * (size_t)D);
             }
@@ -210,6 +222,7 @@ static void write_cache(const problem_t *P, uint16_t *kc, uint16_t *vc)
 static int check_meta(const problem_t *P)
 {
     if (P->B < 0 || P->H < 1 || P->D < 1) return -2;
+    if (P->HK < 1 || P->H % P->HK != 0) return -2;
     if (P->cu[0] != 0) return -3;
     for (int b = 0; b < P->B; ++b) {
         if (P->cu[b + 1] < P->cu[b]) return -3;
@@ -229,12 +242,12 @@ static int check_meta(const problem_t *P)
  */
 int oracle_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int32_t *cu_seqlens, int32_t num_seqs,
-                          int32_t num_heads, int32_t head_dim, float scale,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
                           double *out, uint16_t *k_cache, uint16_t *v_cache,
                           double *probs)
 {
     problem_t P = {q, k, v, cu_seqlens, NULL, NULL, NULL,
-                   num_seqs, num_heads, head_dim, 0, (double)scale};
+                   num_seqs, num_heads, head_dim, 0, (double)scale, num_kv_heads};
     int rc = check_meta(&P);
     if (rc) return rc;
     if (probs && num_seqs != 1) return -5;
@@ -253,13 +266,13 @@ int oracle_prefill_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *
  */
 int oracle_prefill_chunked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            const int32_t *cu_seqlens, int32_t num_seqs,
-                           int32_t num_heads, int32_t head_dim,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t cache_capacity, const int32_t *prefix_lens,
                            float scale, double *out,
                            uint16_t *k_cache, uint16_t *v_cache, double *probs)
 {
     problem_t P = {q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache,
-                   num_seqs, num_heads, head_dim, cache_capacity, (double)scale};
+                   num_seqs, num_heads, head_dim, cache_capacity, (double)scale, num_kv_heads};
     int rc = check_meta(&P);
     if (rc) return rc;
     if (probs && num_seqs != 1) return -5;
@@ -279,14 +292,14 @@ int oracle_prefill_chunked(const uint16_t *q, const uint16_t *k, const uint16_t 
  */
 int oracle_prefill_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const int32_t *cu_seqlens, int32_t num_seqs,
-                        int32_t num_heads, int32_t head_dim,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t cache_capacity, const int32_t *prefix_lens,
                         const uint16_t *k_cache, const uint16_t *v_cache,
                         float scale, const int64_t *rows, int64_t n_rows,
                         double *out)
 {
     problem_t P = {q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache,
-                   num_seqs, num_heads, head_dim, cache_capacity, (double)scale};
+                   num_seqs, num_heads, head_dim, cache_capacity, (double)scale, num_kv_heads};
     int rc = check_meta(&P);
     if (rc) return rc;
     const int64_t H = num_heads, D = head_dim;
@@ -331,12 +344,13 @@ int oracle_prefill_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * same placement rule as write_cache above.
  */
 int oracle_cache_image(const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
-                       int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                        int32_t cache_capacity, const int32_t *prefix_lens,
                        uint16_t *k_cache, uint16_t *v_cache)
 {
+    /* only the K/V heads matter for the image */
     problem_t P = {NULL, k, v, cu_seqlens, prefix_lens, NULL, NULL,
-                   num_seqs, num_heads, head_dim, cache_capacity, 0.0};
+                   num_seqs, num_kv_heads, head_dim, cache_capacity, 0.0, num_kv_heads};
     int rc = check_meta(&P);
     if (rc) return rc;
     write_cache(&P, k_cache, v_cache);

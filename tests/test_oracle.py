@@ -364,3 +364,81 @@ def test_cache_image_only_matches_full_oracle():
     kc, vc = oracle.cache_image(kk, kv, cu, kc0, vc0, prefix_lens=pre)
     np.testing.assert_array_equal(kc, kimg)
     np.testing.assert_array_equal(vc, vimg)
+
+
+# ---------------------------------------------------------------- grouped K/V heads [P5 §2.4]
+
+def _gqa_inputs(n, H, HK, D, seed):
+    g = I.generator(seed)
+    q = I.randn_bf16(g, (n, H, D))
+    k = I.randn_bf16(g, (n, HK, D))
+    v = I.randn_bf16(g, (n, HK, D))
+    return q, k, v
+
+
+@pytest.mark.parametrize("H,HK", [(8, 2), (6, 3), (4, 1)])
+def test_gqa_matches_torch_sdpa_enable_gqa(H, HK):
+    """A library routine: torch's float64 attention with enable_gqa (each K/V
+    head serves H/HK consecutive query heads); HK = 1 is multi-query."""
+    n, D = 70, 64
+    q, k, v = _gqa_inputs(n, H, HK, D, 300 + H * 10 + HK)
+    scale = I.default_scale(D)
+    out, _, _, _ = oracle.prefill_varlen(bits(q), bits(k), bits(v), [0, n], scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.double().permute(1, 0, 2), k.double().permute(1, 0, 2), v.double().permute(1, 0, 2),
+        is_causal=True, scale=scale, enable_gqa=True).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_equals_mha_on_repeated_heads():
+    """Grouping is the plain repetition of each K/V head over its query heads."""
+    n, H, HK, D = 41, 8, 2, 32
+    q, k, v = _gqa_inputs(n, H, HK, D, 331)
+    scale = I.default_scale(D)
+    out, _, _, _ = oracle.prefill_varlen(bits(q), bits(k), bits(v), [0, 17, n], scale)
+    kr = k.repeat_interleave(H // HK, dim=1)
+    vr = v.repeat_interleave(H // HK, dim=1)
+    ref, _, _, _ = oracle.prefill_varlen(bits(q), bits(kr), bits(vr), [0, 17, n], scale)
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_gqa_chunked_matches_torch_sdpa_with_prefix_mask():
+    H, HK, D, pre, n, cap = 6, 2, 64, 29, 13, 48
+    q, k, v = _gqa_inputs(n, H, HK, D, 341)
+    g = I.generator(342)
+    kc = I.randn_bf16(g, (1, HK, cap, D))
+    vc = I.randn_bf16(g, (1, HK, cap, D))
+    scale = I.default_scale(D)
+    out, kimg, vimg, _ = oracle.prefill_chunked(bits(q), bits(k), bits(v), [0, n], [pre],
+                                                bits(kc), bits(vc), scale)
+    Kall = torch.cat([kc[0, :, :pre].double(), k.double().permute(1, 0, 2)], dim=1)
+    Vall = torch.cat([vc[0, :, :pre].double(), v.double().permute(1, 0, 2)], dim=1)
+    mask = torch.arange(pre + n)[None, :] <= (pre + torch.arange(n))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.double().permute(1, 0, 2), Kall, Vall, attn_mask=mask, scale=scale, enable_gqa=True)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(kimg[0, :, pre:pre + n], bits(k).transpose(1, 0, 2))
+    np.testing.assert_array_equal(vimg[0, :, pre:pre + n], bits(v).transpose(1, 0, 2))
+    np.testing.assert_array_equal(kimg[0, :, :pre], bits(kc)[0, :, :pre])
+
+
+def test_gqa_varlen_cache_holds_kv_heads_only():
+    """The cache keeps one row per K/V head: sequence b's block is [HK, len_b, D]."""
+    H, HK, D = 8, 2, 32
+    lengths = [5, 11]
+    q, k, v = _gqa_inputs(sum(lengths), H, HK, D, 351)
+    cu = I.cu_from_lengths(lengths)
+    fill = np.full(sum(lengths) * HK * D, 0x7FC1, np.uint16)
+    _, kimg, vimg, _ = oracle.prefill_varlen(bits(q), bits(k), bits(v), cu, 0.125,
+                                             k_cache=fill, v_cache=fill)
+    for b, L in enumerate(lengths):
+        blk = kimg[cu[b] * HK * D:(cu[b] + L) * HK * D].reshape(HK, L, D)
+        np.testing.assert_array_equal(blk, bits(k)[cu[b]:cu[b] + L].transpose(1, 0, 2))
+        blk = vimg[cu[b] * HK * D:(cu[b] + L) * HK * D].reshape(HK, L, D)
+        np.testing.assert_array_equal(blk, bits(v)[cu[b]:cu[b] + L].transpose(1, 0, 2))
+
+
+def test_gqa_rejects_heads_that_do_not_divide():
+    q, k, v = _gqa_inputs(4, 6, 4, 32, 361)
+    with pytest.raises(ValueError):
+        oracle.prefill_varlen(bits(q), bits(k), bits(v), [0, 4], 0.1)
