@@ -220,19 +220,21 @@ def main():
         return
     q, k, v = w.tensors()
     N, H, D = q.shape
+    HK = k.shape[1]
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
     out = torch.empty_like(qd)
-    kc = torch.empty_like(qd)
-    vc = torch.empty_like(qd)
+    kc = torch.empty_like(kd)
+    vc = torch.empty_like(kd)
     max_seqlen = w.max_seqlen
     torch.cuda.synchronize()
 
     pairs = causal_pairs(w.lengths)
     flops = 4.0 * D * H * pairs
-    kv_bytes = 2.0 * N * H * D * 2
-    alg_bytes = 6.0 * N * H * D * 2  # read q, k, v; write out, k_cache, v_cache
+    kv_bytes = 2.0 * N * HK * D * 2
+    # read q, k, v; write out, k_cache, v_cache
+    alg_bytes = 2.0 * N * H * D * 2 + 4.0 * N * HK * D * 2
 
     def step():
         P.prefill_attn_varlen(qd, kd, vd, cu, kc, vc, out, scale=w.scale, max_seqlen=max_seqlen)
@@ -277,7 +279,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "seq_lens": w.lengths if len(w.lengths) <= 8 else
-                   "%d sequences" % len(w.lengths), "tokens": N, "num_heads": H, "head_dim": D,
+                   "%d sequences" % len(w.lengths), "tokens": N, "num_heads": H,
+                   "num_kv_heads": HK, "head_dim": D,
                    "causal": True, "kv_cache_write": True, "scale": w.scale},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kv_write_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),

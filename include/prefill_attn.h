@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
     PA_OK = 0,
     PA_ERR_NULL = 1,      /* a required pointer is NULL */
-    PA_ERR_SHAPE = 2,     /* num_seqs < 0, num_heads < 1, max_seqlen < 0, cache_capacity < 1, or a grid limit exceeded */
+    PA_ERR_SHAPE = 2,     /* num_seqs < 0, num_heads < 1, max_seqlen < 0, cache_capacity < 1, num_kv_heads < 1 or not dividing num_heads, or a grid limit exceeded */
     PA_ERR_HEAD_DIM = 3,  /* head_dim not in {32, 64, 128} */
     PA_ERR_SCALE = 4,     /* scale is NaN or infinite */
     PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
@@ -122,6 +122,36 @@ pa_status prefill_attn_chunked(const uint16_t *q, const uint16_t *k, const uint1
                                uint16_t *k_cache, uint16_t *v_cache,
                                int32_t cache_capacity, uint16_t *out, float scale,
                                hipStream_t stream, const int32_t *prefix_lens);
+
+/*
+ * Grouped K/V heads (grouped-query / multi-query attention) [P5 §2.4: fewer
+ * K/V heads than query heads, 32 -> 8 in its example, shrink the KV cache in
+ * proportion].  As prefill_attn_varlen / prefill_attn_chunked, except:
+ *
+ *   num_kv_heads   HK >= 1 dividing num_heads H.  Query head h reads K/V head
+ *                  h / (H / HK): consecutive query heads share one K/V head
+ *                  (HK = 1: one K/V head for all, multi-query).
+ *   k, v           bf16 [N, HK, D] device.
+ *   k_cache,       varlen: sequence b's block is [HK, len_b, D] starting at
+ *   v_cache        element cu[b] * HK * D (N * HK * D elements in total);
+ *                  chunked: [num_seqs, HK, cache_capacity, D].  Each K/V head
+ *                  row is written once.
+ *   q, out         bf16 [N, H, D] as before.
+ *
+ * With num_kv_heads == num_heads these are the calls above; errors as above,
+ * plus PA_ERR_SHAPE when num_kv_heads < 1 or does not divide num_heads.
+ */
+pa_status prefill_attn_varlen_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const int32_t *cu_seqlens, int32_t num_seqs,
+                                  int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, uint16_t *k_cache, uint16_t *v_cache,
+                                  uint16_t *out, float scale, hipStream_t stream);
+pa_status prefill_attn_chunked_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, uint16_t *k_cache, uint16_t *v_cache,
+                                   int32_t cache_capacity, uint16_t *out, float scale,
+                                   hipStream_t stream, const int32_t *prefix_lens);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *pa_status_string(int status);

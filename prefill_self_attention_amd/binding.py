@@ -36,6 +36,12 @@ def load() -> ctypes.CDLL:
     lib.prefill_attn_chunked.argtypes = [p, p, p, p, i32, i32, i32, i32, p, p, i32, p,
                                          ctypes.c_float, p, p]
     lib.prefill_attn_chunked.restype = ctypes.c_int
+    lib.prefill_attn_varlen_gqa.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, p,
+                                            ctypes.c_float, p]
+    lib.prefill_attn_varlen_gqa.restype = ctypes.c_int
+    lib.prefill_attn_chunked_gqa.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, i32, p,
+                                             ctypes.c_float, p, p]
+    lib.prefill_attn_chunked_gqa.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_set_check_mode.argtypes = [ctypes.c_int]
@@ -95,29 +101,40 @@ def _max_seqlen(cu_seqlens) -> int:
     return max([c[i + 1] - c[i] for i in range(len(c) - 1)] or [0])
 
 
+def _heads(q, k, v):
+    """(H, HK, D): k and v may carry fewer heads than q (grouped K/V heads)."""
+    if q.dim() != 3 or k.dim() != 3 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q must be [N, H, D] and k, v [N, HK, D]")
+    N, H, D = q.shape
+    if k.shape[0] != N or k.shape[2] != D:
+        raise ValueError("k/v must be [N, HK, D] with q's N and D")
+    return H, k.shape[1], D
+
+
 def prefill_attn_varlen(q, k, v, cu_seqlens, k_cache, v_cache, out, scale=None,
                         max_seqlen=None, stream=None):
     """Varlen causal prefill + KV-cache write (see prefill_attn.h).
 
-    q, k, v, out: bf16 [N, H, D] device tensors; cu_seqlens: int32 [B + 1]
-    device; k_cache, v_cache: bf16 device tensors of N*H*D elements (sequence
-    b's [H, len_b, D] block starts at element cu[b]*H*D).  scale defaults to
-    1/sqrt(D).  max_seqlen: host int; computed from cu_seqlens (a sync) if
-    omitted.  Returns out.
+    q, out: bf16 [N, H, D] device tensors; k, v: bf16 [N, HK, D] with HK
+    dividing H (HK < H: grouped K/V heads, prefill_attn_varlen_gqa);
+    cu_seqlens: int32 [B + 1] device; k_cache, v_cache: bf16 device tensors of
+    N*HK*D elements (sequence b's [HK, len_b, D] block starts at element
+    cu[b]*HK*D).  scale defaults to 1/sqrt(D).  max_seqlen: host int; computed
+    from cu_seqlens (a sync) if omitted.  Returns out.
     """
     import torch
     for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("out", out)):
         _check_tensor(n, t, torch.bfloat16)
     _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
-    N, H, D = q.shape
+    H, HK, D = _heads(q, k, v)
     B = cu_seqlens.shape[0] - 1
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seqlen is None:
         max_seqlen = _max_seqlen(cu_seqlens)
-    st = load().prefill_attn_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, D,
+    st = load().prefill_attn_varlen_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
         _ptr(k_cache), _ptr(v_cache), _ptr(out), ctypes.c_float(scale), _stream(stream))
     if st != PA_OK:
         raise PrefillAttnError(st)
@@ -128,7 +145,7 @@ def prefill_attn_chunked(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens
                          scale=None, max_seqlen=None, stream=None):
     """Chunked prefill: new tokens attend to a cached prefix and to each other.
 
-    k_cache, v_cache: bf16 [B, H, cap, D] device; prefix_lens: int32 [B]
+    k_cache, v_cache: bf16 [B, HK, cap, D] device; prefix_lens: int32 [B]
     device.  New tokens' K/V are written at positions prefix_b .. prefix_b +
     len_b - 1.  Other arguments as for prefill_attn_varlen.  Returns out.
     """
@@ -138,18 +155,18 @@ def prefill_attn_chunked(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens
         _check_tensor(n, t, torch.bfloat16)
     _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
     _check_tensor("prefix_lens", prefix_lens, torch.int32)
-    N, H, D = q.shape
+    H, HK, D = _heads(q, k, v)
     B = cu_seqlens.shape[0] - 1
-    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != H or \
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != HK or \
             k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache/v_cache must be [B, H, cap, D]")
+        raise ValueError("k_cache/v_cache must be [B, HK, cap, D]")
     cap = k_cache.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seqlen is None:
         max_seqlen = _max_seqlen(cu_seqlens)
-    st = load().prefill_attn_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, D,
+    st = load().prefill_attn_chunked_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
         _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
         _stream(stream), _ptr(prefix_lens))
     if st != PA_OK:

@@ -94,9 +94,10 @@ pa_status check_metadata(const int32_t* cu, int32_t num_seqs, int32_t max_seqlen
 }
 
 pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
-              int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
-              uint16_t* kc, uint16_t* vc, int32_t cap, uint16_t* out, float scale,
-              hipStream_t stream, const int32_t* prefix) {
+              int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+              int32_t head_dim, uint16_t* kc, uint16_t* vc, int32_t cap, uint16_t* out,
+              float scale, hipStream_t stream, const int32_t* prefix) {
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   int nqb = 0;
   pa_status st = check_grid(num_seqs, max_seqlen, num_heads, &nqb);
   if (st != PA_OK) return st;
@@ -115,6 +116,7 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   p.vc = vc;
   p.out = out;
   p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
   p.cap = cap;
   p.grid_z = nqb;
   // scale * q.k == |scale| * (sign(scale) q).k : keep the exp2-domain factor
@@ -133,23 +135,24 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
 
 extern "C" {
 
-pa_status prefill_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
-                              int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
-                              uint16_t* v_cache, uint16_t* out, float scale,
-                              hipStream_t stream) {
+pa_status prefill_attn_varlen_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  uint16_t* k_cache, uint16_t* v_cache, uint16_t* out,
+                                  float scale, hipStream_t stream) {
   pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
                               k_cache, v_cache, out, scale);
   if (st != PA_OK) return st;
-  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, k_cache, v_cache,
-             0, out, scale, stream, nullptr);
+  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_kv_heads, head_dim,
+             k_cache, v_cache, 0, out, scale, stream, nullptr);
 }
 
-pa_status prefill_attn_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
-                               int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
-                               uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
-                               float scale, hipStream_t stream, const int32_t* prefix_lens) {
+pa_status prefill_attn_chunked_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, uint16_t* k_cache, uint16_t* v_cache,
+                                   int32_t cache_capacity, uint16_t* out, float scale,
+                                   hipStream_t stream, const int32_t* prefix_lens) {
   pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
                               k_cache, v_cache, out, scale);
   if (st != PA_OK) return st;
@@ -158,15 +161,34 @@ pa_status prefill_attn_chunked(const uint16_t* q, const uint16_t* k, const uint1
       (const void*)prefix_lens == (const void*)v_cache || (const void*)prefix_lens == (const void*)out)
     return PA_ERR_ALIAS;
   if (cache_capacity < 1) return PA_ERR_SHAPE;
-  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim, k_cache, v_cache,
-             cache_capacity, out, scale, stream, prefix_lens);
+  return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_kv_heads, head_dim,
+             k_cache, v_cache, cache_capacity, out, scale, stream, prefix_lens);
+}
+
+pa_status prefill_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                              int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
+                              uint16_t* v_cache, uint16_t* out, float scale,
+                              hipStream_t stream) {
+  return prefill_attn_varlen_gqa(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_heads,
+                                 head_dim, k_cache, v_cache, out, scale, stream);
+}
+
+pa_status prefill_attn_chunked(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                               int32_t num_heads, int32_t head_dim, uint16_t* k_cache,
+                               uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
+                               float scale, hipStream_t stream, const int32_t* prefix_lens) {
+  return prefill_attn_chunked_gqa(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_heads,
+                                  head_dim, k_cache, v_cache, cache_capacity, out, scale, stream,
+                                  prefix_lens);
 }
 
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "PA_OK: success";
     case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
-    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid count or size (num_seqs, max_seqlen, num_heads, cache_capacity or grid limit)";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid count or size (num_seqs, max_seqlen, num_heads, num_kv_heads not dividing num_heads, cache_capacity or grid limit)";
     case PA_ERR_HEAD_DIM: return "PA_ERR_HEAD_DIM: head_dim must be 32, 64 or 128";
     case PA_ERR_SCALE: return "PA_ERR_SCALE: scale must be finite";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: tensor pointers must be 16-byte aligned";

@@ -8,14 +8,15 @@ namespace pa {
 
 struct FwdParams {
   const uint16_t* q;        // [N, H, D] bf16
-  const uint16_t* k;
+  const uint16_t* k;        // [N, num_kv_heads, D]
   const uint16_t* v;
   const int32_t* cu;        // [B + 1]
   const int32_t* prefix;    // [B] (chunked) or nullptr (varlen)
-  uint16_t* kc;             // varlen: packed [H, len_b, D] blocks; chunked: [B, H, cap, D]
+  uint16_t* kc;             // varlen: packed [HK, len_b, D] blocks; chunked: [B, HK, cap, D]
   uint16_t* vc;
   uint16_t* out;            // [N, H, D] bf16
-  int32_t num_heads;
+  int32_t num_heads;        // query heads
+  int32_t num_kv_heads;     // K/V heads (divides num_heads)
   int32_t cap;              // chunked cache capacity (0 for varlen)
   int32_t grid_z;           // work-groups per (head, sequence): pairs of query blocks
   float scale_log2;         // |scale| * log2(e)

@@ -11,7 +11,10 @@
 // keys of its own request ["大模型 Prompt Prefill 阶段的高效 Batching 与算子排布"
 // §2: the varlen kernel reads cu_seqlens and never mixes requests], and the
 // K/V of every new token are copied into the head-major cache
-// ["大模型推理优化：Prefill、Decode与KV Cache的工程实践" §1.3].
+// ["大模型推理优化：Prefill、Decode与KV Cache的工程实践" §1.3].  With grouped
+// K/V heads (untitled page www.zwxr.cn/news/300951 §2.4: fewer K/V heads
+// than query heads shrink the cache) query head h reads K/V head
+// h / (num_heads / num_kv_heads).
 //
 // How it is computed (blockwise, never materialising the T x T scores, and
 // skipping tiles above the diagonal: www.zwxr.cn/news/300951 §3.3):
@@ -281,11 +284,17 @@ void prefill_fwd_kernel(FwdParams p) {
   const bool upper = wave >= 4;
   const int gw = wave & 3;               // wave within its group
 
-  const int64_t row_stride = H * D;      // elements between consecutive tokens
-  const uint16_t* __restrict__ kin = p.k + (int64_t)h * D;
-  const uint16_t* __restrict__ vin = p.v + (int64_t)h * D;
-  const int64_t cache_base = kChunked ? ((int64_t)b * H + h) * p.cap * D
-                                      : (int64_t)seq_start * H * D + (int64_t)h * len * D;
+  // grouped K/V heads: query head h reads K/V head hk; the first query head
+  // of each group writes that K/V head's cache rows
+  const int64_t HK = p.num_kv_heads;
+  const int group = p.num_heads / p.num_kv_heads;
+  const int hk = h / group;
+  const bool writes_cache = h == hk * group;
+  const int64_t row_stride = HK * D;     // K/V elements between consecutive tokens
+  const uint16_t* __restrict__ kin = p.k + (int64_t)hk * D;
+  const uint16_t* __restrict__ vin = p.v + (int64_t)hk * D;
+  const int64_t cache_base = kChunked ? ((int64_t)b * HK + hk) * p.cap * D
+                                      : (int64_t)seq_start * HK * D + (int64_t)hk * len * D;
   const float c = p.scale_log2;          // |scale| * log2(e), > 0
   const uint32_t lds0 = lds_addr(lds);
 
@@ -582,7 +591,7 @@ void prefill_fwd_kernel(FwdParams p) {
       if (j < n_up) {
         const Block blk = bhi;
         if (j * kBN + kBN > blk.own_lo)  // a self-paired block's first tiles hold new tokens
-          cache_copy(blk, j, C::kUpperK + (j & 1) * C::kTileBytes, C::kUpperV + v_cur * C::kTileBytes);
+          if (writes_cache) cache_copy(blk, j, C::kUpperK + (j & 1) * C::kTileBytes, C::kUpperV + v_cur * C::kTileBytes);
         bool use, mask;
         tile_use(blk, j, use, mask);
         if (use) {
@@ -607,7 +616,7 @@ void prefill_fwd_kernel(FwdParams p) {
       const Pick pk = pick_tile(j, false, n_up, e_lo, e_hi, z, qb_hi);
       const Block blk = make_block(pk.qb, len, pre);
       const int t = pk.t;
-      if (t * kBN + kBN > blk.own_lo) cache_copy(blk, t, lower_k(j), lower_k(j) + C::kTileBytes);
+      if (writes_cache && t * kBN + kBN > blk.own_lo) cache_copy(blk, t, lower_k(j), lower_k(j) + C::kTileBytes);
       if (pk.on_hi && !on_hi_rows) {  // lower group moves from the light block to the heavy one
         store_rows(st.l);
         on_hi_rows = true;

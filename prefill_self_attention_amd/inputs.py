@@ -108,7 +108,8 @@ def loguniform_lengths(seed: int = 5, total: int = 65536, lo: int = 64,
 
 @dataclass
 class Varlen:
-    """A varlen prefill problem: flattened q/k/v [N, H, D] plus cu_seqlens."""
+    """A varlen prefill problem: flattened q [N, H, D], k/v [N, HK, D] plus
+    cu_seqlens (HK = num_kv_heads, default H)."""
     name: str
     lengths: List[int]
     num_heads: int
@@ -116,10 +117,13 @@ class Varlen:
     seed: int
     scale: float = 0.0
     cu_seqlens: List[int] = field(default_factory=list)
+    num_kv_heads: int = 0
 
     def __post_init__(self):
         if not self.scale:
             self.scale = default_scale(self.head_dim)
+        if not self.num_kv_heads:
+            self.num_kv_heads = self.num_heads
         self.cu_seqlens = cu_from_lengths(self.lengths)
 
     @property
@@ -131,12 +135,13 @@ class Varlen:
         return max(self.lengths) if self.lengths else 0
 
     def tensors(self):
-        """(q, k, v) as CPU bf16 [N, H, D], drawn in that order from the seed."""
+        """(q, k, v) as CPU bf16, q [N, H, D] and k, v [N, HK, D], drawn in
+        that order from the seed."""
         g = generator(self.seed)
-        shape = (self.num_tokens, self.num_heads, self.head_dim)
-        q = randn_bf16(g, shape)
-        k = randn_bf16(g, shape)
-        v = randn_bf16(g, shape)
+        q = randn_bf16(g, (self.num_tokens, self.num_heads, self.head_dim))
+        kv = (self.num_tokens, self.num_kv_heads, self.head_dim)
+        k = randn_bf16(g, kv)
+        v = randn_bf16(g, kv)
         return q, k, v
 
 
@@ -237,6 +242,8 @@ def workload(name: str):
         return ChunkedWorkload(seed=4)
     if name == "longmix_65536_plus_32768_H32_D128":
         return Varlen(name, loguniform_lengths(5), 32, 128, seed=5)
+    if name == "single_T2048_H32_KV8_D128":
+        return Varlen(name, [2048], 32, 128, seed=6, num_kv_heads=8)
     raise KeyError(name)
 
 
@@ -246,4 +253,5 @@ WORKLOADS = [
     "single_T2048_H32_D128",
     "chunked_8192x512_plus_64_decode_H32_D128",
     "longmix_65536_plus_32768_H32_D128",
+    "single_T2048_H32_KV8_D128",
 ]

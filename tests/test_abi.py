@@ -31,8 +31,9 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "prefill_attn_varlen", "prefill_attn_chunked", "pa_status_string",
-        "pa_set_check_mode", "pa_last_hip_error"])
+        "prefill_attn_varlen", "prefill_attn_chunked", "prefill_attn_varlen_gqa",
+        "prefill_attn_chunked_gqa", "pa_status_string", "pa_set_check_mode",
+        "pa_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol(lib):
