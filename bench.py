@@ -169,6 +169,22 @@ def bench_chunked(args, wl, P):
 
     msd, launchesd = timed(decode, args.steps, args.warmup)
     dec_bytes = 2.0 * sum(c_ + 1 for c_ in wl.contexts) * H * D * 2  # K and V of every context row read
+
+    # the same step and decode rows through the split-KV path (plan, attention
+    # over key segments, merge), workspaces allocated before timing
+    ws = torch.empty(P.splitkv_workspace_size(1 + R, q.shape[0], H, D, wl.cap), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(P.splitkv_workspace_size(R, R, H, D, wl.cap), dtype=torch.uint8, device=dev)
+
+    def step_split():
+        P.prefill_attn_chunked_splitkv(q, k, v, cu, kc, vc, out, pre, scale=st.scale,
+                                       max_seqlen=wl.chunk_len, workspace=ws)
+
+    def decode_split():
+        P.prefill_attn_chunked_splitkv(qd, kd, vd, cud, kcd, vcd, outd, pred, scale=st.scale,
+                                       max_seqlen=1, workspace=wsd)
+
+    mss, launchess = timed(step_split, args.steps, args.warmup)
+    msds, launchesds = timed(decode_split, args.steps, args.warmup)
     value = flops / (ms * 1e-3) / 1e12
     return {
         "metric": METRIC,
@@ -194,6 +210,12 @@ def bench_chunked(args, wl, P):
                         "launch_us_mean": round(sum(launchesd) / len(launchesd) * 1e3, 2),
                         "kv_read_gbps": round(dec_bytes / (msd * 1e-3) / 1e9, 1),
                         "frac_of_hbm_8tbs": round(dec_bytes / (msd * 1e-3) / 8e12, 4)},
+        "splitkv": {"ms_per_step": round(mss, 5),
+                    "tflops": round(flops / (mss * 1e-3) / 1e12, 2),
+                    "launch_us_mean": round(sum(launchess) / len(launchess) * 1e3, 2),
+                    "decode_only_us_mean": round(sum(launchesds) / len(launchesds) * 1e3, 2),
+                    "decode_kv_read_gbps": round(dec_bytes / (msds * 1e-3) / 1e9, 1),
+                    "decode_frac_of_hbm_8tbs": round(dec_bytes / (msds * 1e-3) / 8e12, 4)},
         "roofline": None,
         "cpu_baseline": None,
     }

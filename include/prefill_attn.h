@@ -46,6 +46,7 @@
 #ifndef PREFILL_ATTN_H
 #define PREFILL_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -63,7 +64,8 @@ typedef enum {
     PA_ERR_ALIAS = 6,     /* an output pointer equals an input or another output pointer */
     PA_ERR_SEQLENS = 7,   /* check mode: cu_seqlens[0] != 0, decreasing, or a length > max_seqlen */
     PA_ERR_CAPACITY = 8,  /* check mode: a prefix length < 0 or prefix + length > cache_capacity */
-    PA_ERR_HIP = 9        /* a HIP runtime call failed; see pa_last_hip_error() */
+    PA_ERR_HIP = 9,       /* a HIP runtime call failed; see pa_last_hip_error() */
+    PA_ERR_WORKSPACE = 10 /* split-KV: workspace_bytes below prefill_attn_splitkv_workspace_size() */
 } pa_status;
 
 /*
@@ -152,6 +154,52 @@ pa_status prefill_attn_chunked_gqa(const uint16_t *q, const uint16_t *k, const u
                                    int32_t head_dim, uint16_t *k_cache, uint16_t *v_cache,
                                    int32_t cache_capacity, uint16_t *out, float scale,
                                    hipStream_t stream, const int32_t *prefix_lens);
+
+/*
+ * Split-KV chunked prefill.  Same result and cache writes as
+ * prefill_attn_chunked_gqa, computed so that long key ranges do not serialise
+ * on one work-group: in a chunked step a prompt chunk is batched with decode
+ * rows [P3 §3; P2 §2.2], and a decode row reads every cached position of its
+ * sequence [P5 §3.3], so a few long rows would otherwise leave most compute
+ * units idle.  Each query block's keys are cut into segments of at least 1024
+ * keys; every segment is an independent work item, and a block with more
+ * than one segment is finished by an fp32 log-sum-exp merge of the segments'
+ * partial results.  Three kernels are enqueued on `stream`: plan, attention,
+ * merge.  Rows differ from prefill_attn_chunked_gqa only by floating-point
+ * rounding order.
+ *
+ *   num_tokens        N, the rows of q, k, v and out (host); cu_seqlens[B]
+ *                     must not exceed it (check mode: PA_ERR_SEQLENS).
+ *   workspace         device scratch memory, 16-byte aligned, of at least
+ *                     prefill_attn_splitkv_workspace_size(...) bytes, owned by
+ *                     the caller; its contents on entry do not matter and on
+ *                     return are unspecified.  Calls that overlap in time
+ *                     (other streams) need separate workspaces.
+ *   other arguments   as prefill_attn_chunked_gqa.
+ *
+ * Errors as prefill_attn_chunked_gqa, plus PA_ERR_NULL for a NULL workspace,
+ * PA_ERR_ALIGN, PA_ERR_ALIAS if the workspace equals another pointer,
+ * PA_ERR_SHAPE for num_tokens < 0, and PA_ERR_WORKSPACE when workspace_bytes
+ * is too small.  B == 0, max_seqlen == 0 or num_tokens == 0 enqueue nothing.
+ */
+pa_status prefill_attn_chunked_splitkv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                       const int32_t *cu_seqlens, int32_t num_seqs,
+                                       int32_t max_seqlen, int32_t num_tokens,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       uint16_t *k_cache, uint16_t *v_cache,
+                                       int32_t cache_capacity, uint16_t *out, float scale,
+                                       hipStream_t stream, const int32_t *prefix_lens,
+                                       void *workspace, size_t workspace_bytes);
+
+/*
+ * Workspace bytes prefill_attn_chunked_splitkv needs for these sizes (host
+ * values only; 0 for invalid arguments).  It grows with num_tokens * num_heads
+ * * head_dim * segments, segments being at most 64 and at most
+ * ceil(cache_capacity / 1024).
+ */
+size_t prefill_attn_splitkv_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                           int32_t num_heads, int32_t head_dim,
+                                           int32_t cache_capacity);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *pa_status_string(int status);

@@ -42,6 +42,11 @@ def load() -> ctypes.CDLL:
     lib.prefill_attn_chunked_gqa.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, i32, p,
                                              ctypes.c_float, p, p]
     lib.prefill_attn_chunked_gqa.restype = ctypes.c_int
+    lib.prefill_attn_chunked_splitkv.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p, p,
+                                                 i32, p, ctypes.c_float, p, p, p, ctypes.c_size_t]
+    lib.prefill_attn_chunked_splitkv.restype = ctypes.c_int
+    lib.prefill_attn_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.prefill_attn_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_set_check_mode.argtypes = [ctypes.c_int]
@@ -169,6 +174,51 @@ def prefill_attn_chunked(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
         _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
         _stream(stream), _ptr(prefix_lens))
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out
+
+
+def splitkv_workspace_size(num_seqs: int, num_tokens: int, num_heads: int, head_dim: int,
+                           cache_capacity: int) -> int:
+    """Bytes of device workspace prefill_attn_chunked_splitkv needs (0: invalid sizes)."""
+    return int(load().prefill_attn_splitkv_workspace_size(
+        int(num_seqs), int(num_tokens), int(num_heads), int(head_dim), int(cache_capacity)))
+
+
+def prefill_attn_chunked_splitkv(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens,
+                                 scale=None, max_seqlen=None, stream=None, workspace=None):
+    """Chunked prefill with split key ranges and a log-sum-exp merge.
+
+    Same arguments and result as prefill_attn_chunked (up to rounding order).
+    workspace: a uint8 device tensor of at least splitkv_workspace_size(...)
+    bytes; allocated here through torch when omitted.  Returns out.
+    """
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    _check_tensor("prefix_lens", prefix_lens, torch.int32)
+    H, HK, D = _heads(q, k, v)
+    N = q.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != HK or \
+            k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [B, HK, cap, D]")
+    cap = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    need = splitkv_workspace_size(B, N, H, D, cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8)
+    st = load().prefill_attn_chunked_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), N, H, HK, D,
+        _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
+        _stream(stream), _ptr(prefix_lens), _ptr(workspace), workspace.numel())
     if st != PA_OK:
         raise PrefillAttnError(st)
     return out

@@ -131,9 +131,120 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   return PA_OK;
 }
 
+// Compute units of the current device and resident split-attention
+// work-groups per unit, queried once per device and head size.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_split_occ[kMaxDevices][3];
+
+pa_status split_grid(int head_dim, int* fwd_grid, int* merge_grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  const int di = head_dim == 32 ? 0 : head_dim == 64 ? 1 : 2;
+  int occ = g_split_occ[dev][di].load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    occ = pa::fwd_split_blocks_per_cu(head_dim);
+    if (occ <= 0) return hip_fail(hipErrorInvalidConfiguration);
+    g_split_occ[dev][di].store(occ, std::memory_order_relaxed);
+  }
+  *fwd_grid = cus * occ;
+  *merge_grid = cus * 8;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t prefill_attn_splitkv_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                           int32_t num_heads, int32_t head_dim,
+                                           int32_t cache_capacity) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || cache_capacity < 1) return 0;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return 0;
+  return pa::split_layout(num_seqs, num_tokens, num_heads, head_dim, cache_capacity).bytes;
+}
+
+pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const int32_t* cu_seqlens, int32_t num_seqs,
+                                       int32_t max_seqlen, int32_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
+                                       uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
+                                       float scale, hipStream_t stream,
+                                       const int32_t* prefix_lens, void* workspace,
+                                       size_t workspace_bytes) {
+  pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
+                              k_cache, v_cache, out, scale);
+  if (st != PA_OK) return st;
+  if (!prefix_lens || !workspace) return PA_ERR_NULL;
+  const void* outs[4] = {k_cache, v_cache, out, workspace};
+  const void* ins[5] = {q, k, v, cu_seqlens, prefix_lens};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (outs[i] == ins[j]) return PA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[i] == outs[j]) return PA_ERR_ALIAS;
+  }
+  if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  if (cache_capacity < 1 || num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_kv_heads < 1 || num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  int nqb = 0;
+  st = check_grid(num_seqs, max_seqlen, num_heads, &nqb);
+  if (st != PA_OK) return st;
+  const pa::SplitLayout L =
+      pa::split_layout(num_seqs, num_tokens, num_heads, head_dim, cache_capacity);
+  if (workspace_bytes < L.bytes) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0 || max_seqlen == 0 || num_tokens == 0) return PA_OK;
+  if (check_mode()) {
+    st = check_metadata(cu_seqlens, num_seqs, max_seqlen, prefix_lens, cache_capacity, stream);
+    if (st != PA_OK) return st;
+    int32_t last = 0;
+    hipError_t e = hipMemcpyAsync(&last, cu_seqlens + num_seqs, sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (last > num_tokens) return PA_ERR_SEQLENS;
+  }
+  int fwd_grid = 0, merge_grid = 0;
+  st = split_grid(head_dim, &fwd_grid, &merge_grid);
+  if (st != PA_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  pa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.cu = cu_seqlens;
+  p.prefix = prefix_lens;
+  p.kc = k_cache;
+  p.vc = v_cache;
+  p.out = out;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.cap = cache_capacity;
+  p.grid_z = nqb;
+  p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634, 0x1p-100);
+  p.neg_q = scale < 0.f ? 1 : 0;
+  p.hdr = reinterpret_cast<const int32_t*>(ws + L.off_hdr);
+  p.items = reinterpret_cast<const int4*>(ws + L.off_items);
+  p.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
+  p.part_o = reinterpret_cast<float*>(ws + L.off_o);
+  p.seg_tiles = L.seg_tiles;
+  p.max_segs = L.max_segs;
+  p.split_grid = fwd_grid;
+  hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, ws, stream);
+  if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, stream);
+  if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return PA_OK;
+}
 
 pa_status prefill_attn_varlen_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
@@ -196,6 +307,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_SEQLENS: return "PA_ERR_SEQLENS: cu_seqlens must start at 0, be non-decreasing and have lengths <= max_seqlen";
     case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: prefix_lens must be >= 0 with prefix + length <= cache_capacity";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP runtime call failed (see pa_last_hip_error)";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace smaller than prefill_attn_splitkv_workspace_size()";
     default: return "unknown pa_status";
   }
 }

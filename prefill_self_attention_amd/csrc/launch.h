@@ -1,10 +1,13 @@
 // launch.h -- internal interface between the C-ABI layer (api.hip) and the
-// gfx950 kernels (prefill_fwd.hip).  Not part of the public ABI.
+// gfx950 kernels (prefill_fwd.hip, splitkv.hip).  Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pa {
+
+constexpr int kQueryBlock = 128;  // query rows per block
+constexpr int kKeyTile = 64;      // keys per tile
 
 struct FwdParams {
   const uint16_t* q;        // [N, H, D] bf16
@@ -21,6 +24,14 @@ struct FwdParams {
   int32_t grid_z;           // work-groups per (head, sequence): pairs of query blocks
   float scale_log2;         // |scale| * log2(e)
   int32_t neg_q;            // 1 if scale < 0: q's sign is flipped in the kernel
+  // split-KV chunked mode only (see SplitLayout)
+  const int32_t* hdr;       // [0] = number of work items, [1] = number of merged blocks
+  const int4* items;        // work items: {sequence, query block, segment, segments of the block}
+  float* part_o;            // [N, H, max_segs, D] fp32 partial outputs (normalised)
+  float* part_lse;          // [N, H, max_segs] fp32 log2-sum-exp2 of each partial
+  int32_t seg_tiles;        // key tiles per segment
+  int32_t max_segs;         // segments per block, at most
+  int32_t split_grid;       // work-groups of the persistent split-KV launch
 };
 
 // Query rows per block, and work-groups per (head, sequence) for a maximum length.
@@ -30,5 +41,30 @@ int fwd_grid_blocks(int max_seqlen);
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream);
+
+// ------------------------------------------------------------ split-KV layout
+// Workspace of the split-KV chunked call, carved from one caller buffer.
+// Every region starts on a 256-byte boundary.
+struct SplitLayout {
+  int32_t seg_tiles;     // key tiles per segment
+  int32_t max_segs;      // ceil(ceil(cap / 64) / seg_tiles)
+  int64_t max_blocks;    // bound on the query blocks of the batch: N / 128 + B + 1
+  int64_t max_items;     // max_blocks * max_segs
+  size_t off_hdr, off_items, off_merges, off_lse, off_o, bytes;
+};
+SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t cap);
+
+// Plan (one work-group): item list, merge list and their counts in the
+// workspace.  Then the persistent attention pass over the items, then the
+// merge of blocks with more than one segment.
+hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
+                               int32_t num_tokens, const SplitLayout& L, void* ws,
+                               hipStream_t stream);
+hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
+                                int head_dim, int grid, hipStream_t stream);
+// Resident work-groups per compute unit of the split attention kernel (0 on error).
+int fwd_split_blocks_per_cu(int head_dim);
 
 }  // namespace pa

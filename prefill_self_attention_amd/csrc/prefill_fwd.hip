@@ -80,6 +80,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -88,9 +89,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 128;            // query rows per block (4 waves x 32)
+constexpr int kBM = kQueryBlock;    // query rows per block (4 waves x 32)
 constexpr int kGroupThreads = 256;  // one group = 4 waves
-constexpr int kBN = 64;             // keys per tile
+constexpr int kBN = kKeyTile;       // keys per tile
 constexpr float kRescale = 8.0f;    // lazy-rescale headroom, log2 units
 constexpr float kNegInf = -__builtin_huge_valf();
 // Initial running max: finite, so a first tile in which every key of a row is
@@ -246,33 +247,33 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int D, bool kChunked>
-__global__ __launch_bounds__(kThreads)
-void prefill_fwd_kernel(FwdParams p) {
+// One work item of a work-group: head h of sequence b, and either the pair of
+// query blocks (z, n-1-z) over all their keys or, in split mode (kSplit), the
+// single block z over key tiles [seg * seg_tiles, (seg + 1) * seg_tiles) --
+// one of the nseg segments of its keys.  A block with one segment is stored
+// as usual; otherwise its rows get a partial result (normalised O in fp32 and
+// log2 of its sum of weights), merged by a later pass.
+template <int D, bool kChunked, bool kSplit>
+__device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z, int seg, int nseg) {
   using C = Cfg<D>;
   // Every LDS read in the main loop is inline asm (lds_read_* above), so the
   // compiler places no wait for the direct loads in flight; each read is made
   // valid by an explicit lgkmcnt wait tied to its registers.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
-
-  // raw id builtins: the device library's id helpers are built with IEEE mode
-  // on and would not inline into this IEEE-off kernel
-  const int h = __builtin_amdgcn_workgroup_id_x();
-  const int b = __builtin_amdgcn_workgroup_id_y();
-  const int z = __builtin_amdgcn_workgroup_id_z();
   const int64_t H = p.num_heads;
 
   const int seq_start = p.cu[b];
   const int len = p.cu[b + 1] - seq_start;
   const int nqb = (len + kBM - 1) / kBM;
-  const int qb_hi = nqb - 1 - z;
+  const int qb_hi = kSplit ? z : nqb - 1 - z;
   if (z > qb_hi) return;                 // no block pair left for this work-group
   const int pre = kChunked ? p.prefix[b] : 0;
-  const bool has_lo = z < qb_hi;
+  const bool has_lo = !kSplit && z < qb_hi;
   const Block blo = make_block(z, len, pre);
   const Block bhi = make_block(qb_hi, len, pre);
+  const int tb = kSplit ? seg * p.seg_tiles : 0;  // first key tile of the item
   const int e_lo = has_lo ? blo.ntiles : 0;
-  const int e_hi = bhi.ntiles;
+  const int e_hi = kSplit ? min(p.seg_tiles, bhi.ntiles - tb) : bhi.ntiles;
   const int n_up = (e_lo + e_hi + 1) / 2;  // tiles of the upper group
   const int n_lo = e_lo + e_hi - n_up;     // tiles of the lower group (<= n_up)
 
@@ -411,6 +412,28 @@ void prefill_fwd_kernel(FwdParams p) {
                      pack_bf16x2(st.o[mb][4 * cc + 2] * inv, st.o[mb][4 * cc + 3] * inv)};
         *(u32x2_t*)(dst + 32 * mb + 8 * cc) = w;
       }
+  };
+
+  // Split mode: the rows' partial result over this item's keys, O / l in fp32
+  // and log2(l) + m (the log2 of the sum of 2^(s c) over those keys; -inf
+  // when a row sees none of them), at slot (token, head, segment).
+  auto store_partial = [&](float l_part) __attribute__((always_inline)) {
+    const int row = qrow0 + ql;
+    const float l = row_sum_halves(l_part);
+    if (row >= len_rows) return;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const int64_t slot = ((int64_t)(seq_start + row) * H + h) * p.max_segs + seg;
+    float* dst = p.part_o + slot * D + 4 * hh;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const f32x4_t w = {st.o[mb][4 * cc + 0] * inv, st.o[mb][4 * cc + 1] * inv,
+                           st.o[mb][4 * cc + 2] * inv, st.o[mb][4 * cc + 3] * inv};
+        *(f32x4_t*)(dst + 32 * mb + 8 * cc) = w;
+      }
+    if (hh == 0) p.part_lse[slot] = any ? st.m + __builtin_amdgcn_logf(l) : kNegInf;
   };
 
   // Lane parts of the LDS read addresses (byte offsets within a tile).
@@ -569,8 +592,8 @@ void prefill_fwd_kernel(FwdParams p) {
   {
     const Pick p0 = pick_tile(0, upper, n_up, e_lo, e_hi, z, qb_hi);
     if (p0.valid) {
-      if (upper) issue_tile(make_block(p0.qb, len, pre), p0.t, C::kUpperK, C::kUpperV);
-      else issue_tile(make_block(p0.qb, len, pre), p0.t, lower_k(0), lower_k(0) + C::kTileBytes);
+      if (upper) issue_tile(make_block(p0.qb, len, pre), tb + p0.t, C::kUpperK, C::kUpperV);
+      else issue_tile(make_block(p0.qb, len, pre), tb + p0.t, lower_k(0), lower_k(0) + C::kTileBytes);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -583,24 +606,25 @@ void prefill_fwd_kernel(FwdParams p) {
     if (upper) {
       if (j + 1 < n_up) {
         const Pick nx = pick_tile(j + 1, true, n_up, e_lo, e_hi, z, qb_hi);
-        issue_tile(make_block(nx.qb, len, pre), nx.t, C::kUpperK + ((j + 1) & 1) * C::kTileBytes,
+        issue_tile(make_block(nx.qb, len, pre), tb + nx.t, C::kUpperK + ((j + 1) & 1) * C::kTileBytes,
                    C::kUpperV + v_next * C::kTileBytes);
       }
       if (have_prev) pv(C::kUpperV + v_prev * C::kTileBytes, p_prev);
       have_prev = false;
       if (j < n_up) {
         const Block blk = bhi;
-        if (j * kBN + kBN > blk.own_lo)  // a self-paired block's first tiles hold new tokens
-          if (writes_cache) cache_copy(blk, j, C::kUpperK + (j & 1) * C::kTileBytes, C::kUpperV + v_cur * C::kTileBytes);
+        const int t = tb + j;
+        if (t * kBN + kBN > blk.own_lo)  // a self-paired block's first tiles hold new tokens
+          if (writes_cache) cache_copy(blk, t, C::kUpperK + (j & 1) * C::kTileBytes, C::kUpperV + v_cur * C::kTileBytes);
         bool use, mask;
-        tile_use(blk, j, use, mask);
+        tile_use(blk, t, use, mask);
         if (use) {
           f32x16_t s[2];
           score(C::kUpperK + (j & 1) * C::kTileBytes, s);
           if (mask)
-            softmax(s, blk, j, std::true_type{}, p_prev);
+            softmax(s, blk, t, std::true_type{}, p_prev);
           else
-            softmax(s, blk, j, std::false_type{}, p_prev);
+            softmax(s, blk, t, std::false_type{}, p_prev);
           have_prev = true;
         }
       }
@@ -611,11 +635,11 @@ void prefill_fwd_kernel(FwdParams p) {
     } else if (j < n_lo) {
       if (j + 1 < n_lo) {
         const Pick nx = pick_tile(j + 1, false, n_up, e_lo, e_hi, z, qb_hi);
-        issue_tile(make_block(nx.qb, len, pre), nx.t, lower_k(j + 1), lower_k(j + 1) + C::kTileBytes);
+        issue_tile(make_block(nx.qb, len, pre), tb + nx.t, lower_k(j + 1), lower_k(j + 1) + C::kTileBytes);
       }
       const Pick pk = pick_tile(j, false, n_up, e_lo, e_hi, z, qb_hi);
       const Block blk = make_block(pk.qb, len, pre);
-      const int t = pk.t;
+      const int t = tb + pk.t;
       if (writes_cache && t * kBN + kBN > blk.own_lo) cache_copy(blk, t, lower_k(j), lower_k(j) + C::kTileBytes);
       if (pk.on_hi && !on_hi_rows) {  // lower group moves from the light block to the heavy one
         store_rows(st.l);
@@ -666,7 +690,36 @@ void prefill_fwd_kernel(FwdParams p) {
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[mb][r] = st.o[mb][r] * fa + mbuf[(2 + 16 * mb + r) * 64 + lane] * fb;
-    store_rows(st.l * fa + l2 * fb);
+    st.m = m;  // the partial's log2-sum-exp2 is taken against the merged max
+    if (kSplit && nseg > 1)
+      store_partial(st.l * fa + l2 * fb);
+    else
+      store_rows(st.l * fa + l2 * fb);
+  }
+}
+
+template <int D, bool kChunked>
+__global__ __launch_bounds__(kThreads)
+void prefill_fwd_kernel(FwdParams p) {
+  // raw id builtins: the device library's id helpers are built with IEEE mode
+  // on and would not inline into this IEEE-off kernel
+  fwd_item<D, kChunked, false>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
+                               __builtin_amdgcn_workgroup_id_z(), 0, 1);
+}
+
+// Split-KV chunked prefill: a persistent grid walks the planned items, item i
+// of head h being step i * H + h; with the grid a multiple of H (and of the 8
+// XCDs) a work-group keeps one head, and all of a head's items run on one XCD.
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void prefill_fwd_split_kernel(FwdParams p) {
+  const int H = p.num_heads;
+  const int64_t steps = (int64_t)p.hdr[0] * H;
+  const int grid = p.split_grid;
+  for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += grid) {
+    const int4 it = p.items[g / H];
+    fwd_item<D, true, true>(p, (int)(g % H), it.x, it.y, it.z, it.w);
+    __syncthreads();  // the next item's first loads reuse the merge buffers
   }
 }
 
@@ -678,6 +731,29 @@ hipError_t launch_d(const FwdParams& p, int num_seqs, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream) {
+  const dim3 grid(p.split_grid);
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL(prefill_fwd_split_kernel<32>, grid, dim3(kThreads), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(prefill_fwd_split_kernel<64>, grid, dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(prefill_fwd_split_kernel<128>, grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int fwd_split_blocks_per_cu(int head_dim) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<32>, kThreads, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<64>, kThreads, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<128>, kThreads, 0); break;
+    default: break;
+  }
+  return e == hipSuccess ? n : 0;
+}
 
 int fwd_block_rows() { return kBM; }
 

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "prefill_attn_varlen", "prefill_attn_chunked", "prefill_attn_varlen_gqa",
-        "prefill_attn_chunked_gqa", "pa_status_string", "pa_set_check_mode",
+        "prefill_attn_chunked_gqa", "prefill_attn_chunked_splitkv",
+        "prefill_attn_splitkv_workspace_size", "pa_status_string", "pa_set_check_mode",
         "pa_last_hip_error"])
 
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         s = P.pa_status_string(code)
         assert s.startswith("PA_")
     assert P.pa_status_string(42) == "unknown pa_status"
@@ -72,7 +73,18 @@ def chunked(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64, kc=
                                     ctypes.c_float(scale), None, pre)
 
 
-@pytest.mark.parametrize("f", [varlen, chunked])
+WS = 1 << 40  # a workspace size no test call can exceed
+
+
+def splitkv(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64, kc=A[4],
+            vc=A[5], cap=32, out=A[6], scale=0.125, pre=A[7], N=16, HK=None, ws=A[8],
+            ws_bytes=WS):
+    return lib.prefill_attn_chunked_splitkv(q, k, v, cu, B, maxlen, N, H, H if HK is None else HK,
+                                            D, kc, vc, cap, out, ctypes.c_float(scale), None,
+                                            pre, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("f", [varlen, chunked, splitkv])
 def test_host_rejections(lib, f):
     assert f(lib, q=None) == 1
     assert f(lib, out=None) == 1
@@ -92,17 +104,46 @@ def test_host_rejections(lib, f):
     assert f(lib, vc=A[4]) == 6
 
 
-def test_chunked_only_rejections(lib):
-    assert chunked(lib, pre=None) == 1
-    assert chunked(lib, cap=0) == 2
-    assert chunked(lib, pre=A[6]) == 6
+@pytest.mark.parametrize("f", [chunked, splitkv])
+def test_chunked_only_rejections(lib, f):
+    assert f(lib, pre=None) == 1
+    assert f(lib, cap=0) == 2
+    assert f(lib, pre=A[6]) == 6
 
 
-@pytest.mark.parametrize("f", [varlen, chunked])
+def test_splitkv_rejections(lib):
+    assert splitkv(lib, ws=None) == 1
+    assert splitkv(lib, ws=A[8] + 4) == 5
+    assert splitkv(lib, ws=A[6]) == 6      # workspace is out
+    assert splitkv(lib, ws=A[0]) == 6      # workspace is q
+    assert splitkv(lib, N=-1) == 2
+    assert splitkv(lib, HK=3) == 2
+    need = lib.prefill_attn_splitkv_workspace_size(1, 16, 2, 64, 32)
+    assert need > 0
+    assert splitkv(lib, ws_bytes=need - 1) == 10
+    assert P.pa_status_string(10).startswith("PA_ERR_WORKSPACE")
+
+
+def test_splitkv_workspace_size():
+    f = P.splitkv_workspace_size
+    assert f(1, 16, 2, 64, 0) == 0 and f(-1, 16, 2, 64, 8) == 0 and f(1, 16, 2, 48, 8) == 0
+    # grows with tokens, heads, head size and (up to 64 segments) capacity
+    base = f(65, 576, 32, 128, 8192)
+    assert f(65, 1152, 32, 128, 8192) > base and f(65, 576, 32, 128, 16384) > base
+    assert f(65, 576, 32, 64, 8192) < base
+    # segments of 1024 keys: 8192 keys -> 8 segments of fp32 partials per (token, head)
+    assert base >= 576 * 32 * 8 * 129 * 4
+    # beyond 64 * 1024 keys the segment count stays at 64
+    assert f(1, 128, 8, 128, 1 << 20) < 2 * f(1, 128, 8, 128, 1 << 16) + 4096
+
+
+@pytest.mark.parametrize("f", [varlen, chunked, splitkv])
 def test_empty_problem_is_a_no_op(lib, f):
     # nothing is enqueued: these would fault if anything touched the fake pointers
     assert f(lib, B=0) == 0
     assert f(lib, maxlen=0) == 0
+    if f is splitkv:
+        assert f(lib, N=0) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
