@@ -136,8 +136,10 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_split_occ[kMaxDevices][3];
+std::atomic<int> g_dec_occ[kMaxDevices][3][4];
 
-pa_status split_grid(int head_dim, int* fwd_grid, int* merge_grid) {
+pa_status split_grid(int head_dim, int heads_per_unit, int* fwd_grid, int* dec_grid,
+                     int* merge_grid) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -155,7 +157,15 @@ pa_status split_grid(int head_dim, int* fwd_grid, int* merge_grid) {
     if (occ <= 0) return hip_fail(hipErrorInvalidConfiguration);
     g_split_occ[dev][di].store(occ, std::memory_order_relaxed);
   }
+  const int gi = heads_per_unit == 1 ? 0 : heads_per_unit == 2 ? 1 : heads_per_unit == 4 ? 2 : 3;
+  int docc = g_dec_occ[dev][di][gi].load(std::memory_order_relaxed);
+  if (docc <= 0) {
+    docc = pa::splitkv_decode_blocks_per_cu(head_dim, heads_per_unit);
+    if (docc <= 0) return hip_fail(hipErrorInvalidConfiguration);
+    g_dec_occ[dev][di][gi].store(docc, std::memory_order_relaxed);
+  }
   *fwd_grid = cus * occ;
+  *dec_grid = cus * docc;
   *merge_grid = cus * 8;
   return PA_OK;
 }
@@ -212,8 +222,9 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
     if (e != hipSuccess) return hip_fail(e);
     if (last > num_tokens) return PA_ERR_SEQLENS;
   }
-  int fwd_grid = 0, merge_grid = 0;
-  st = split_grid(head_dim, &fwd_grid, &merge_grid);
+  const int gc = pa::splitkv_heads_per_unit(num_heads, num_kv_heads);
+  int fwd_grid = 0, dec_grid = 0, merge_grid = 0;
+  st = split_grid(head_dim, gc, &fwd_grid, &dec_grid, &merge_grid);
   if (st != PA_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
@@ -239,8 +250,11 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
   p.seg_tiles = L.seg_tiles;
   p.max_segs = L.max_segs;
   p.split_grid = fwd_grid;
+  p.dec_items = reinterpret_cast<const int4*>(ws + L.off_dec);
+  p.dec_grid = dec_grid;
   hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, ws, stream);
   if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, stream);
+  if (e == hipSuccess) e = pa::launch_splitkv_decode(p, head_dim, gc, stream);
   if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;

@@ -32,6 +32,8 @@ struct FwdParams {
   int32_t seg_tiles;        // key tiles per segment
   int32_t max_segs;         // segments per block, at most
   int32_t split_grid;       // work-groups of the persistent split-KV launch
+  const int4* dec_items;    // decode-row items: {sequence, segment, segments, 0}; hdr[2] of them
+  int32_t dec_grid;         // work-groups of the persistent decode launch
 };
 
 // Query rows per block, and work-groups per (head, sequence) for a maximum length.
@@ -50,7 +52,8 @@ struct SplitLayout {
   int32_t max_segs;      // ceil(ceil(cap / 64) / seg_tiles)
   int64_t max_blocks;    // bound on the query blocks of the batch: N / 128 + B + 1
   int64_t max_items;     // max_blocks * max_segs
-  size_t off_hdr, off_items, off_merges, off_lse, off_o, bytes;
+  int64_t max_dec_items; // num_seqs * max_segs
+  size_t off_hdr, off_items, off_dec, off_merges, off_lse, off_o, bytes;
 };
 SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                          int32_t head_dim, int32_t cap);
@@ -64,6 +67,13 @@ hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
                                 int head_dim, int grid, hipStream_t stream);
+// Length-1 rows of the split-KV call: a memory-bound pass over their
+// segments; `heads_per_unit` query heads (1, 2, 4 or 8, dividing
+// num_heads / num_kv_heads) share each load of a K/V row.
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit,
+                                 hipStream_t stream);
+int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit);
+int splitkv_heads_per_unit(int num_heads, int num_kv_heads);
 // Resident work-groups per compute unit of the split attention kernel (0 on error).
 int fwd_split_blocks_per_cu(int head_dim);
 

@@ -61,21 +61,24 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 }
 
 struct SeqPlan {
-  int items, merges;
+  int items, dec, merges;
 };
 
-// Segments of every query block of one sequence (work items), and the merge
-// entries of the blocks with more than one segment.  Segment counts are
-// capped at max_segs, so malformed metadata cannot address outside the
-// workspace.
+// Segments of every query block of one sequence (work items; a length-1
+// sequence's go to the decode list), and the merge entries of the blocks with
+// more than one segment.  Segment counts are capped at max_segs, so malformed
+// metadata cannot address outside the workspace.
 __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs) {
-  SeqPlan r{0, 0};
+  SeqPlan r{0, 0, 0};
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
     const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
     if (ns < 1) continue;
-    r.items += ns;
+    if (len == 1)
+      r.dec += ns;
+    else
+      r.items += ns;
     if (ns > 1) r.merges += (qend - q0 + kMergeRows - 1) / kMergeRows;
   }
   return r;
@@ -87,16 +90,17 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs) {
 __global__ __launch_bounds__(kPlanThreads)
 void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
                          int num_seqs, int num_tokens, int seg_tiles, int max_segs,
-                         int64_t max_items, int64_t max_merges, int32_t* __restrict__ hdr,
-                         int4* __restrict__ items, int4* __restrict__ merges) {
-  __shared__ int wsum[2][kPlanThreads / 64];
+                         int64_t max_items, int64_t max_dec, int64_t max_merges,
+                         int32_t* __restrict__ hdr, int4* __restrict__ items,
+                         int4* __restrict__ dec, int4* __restrict__ merges) {
+  __shared__ int wsum[3][kPlanThreads / 64];
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63, wave = tid >> 6;
-  int64_t base_i = 0, base_m = 0;
+  int64_t base_i = 0, base_d = 0, base_m = 0;
   for (int b0 = 0; b0 < num_seqs; b0 += kPlanThreads) {
     const int b = b0 + tid;
     int start = 0, len = 0, pre = 0;
-    SeqPlan c{0, 0};
+    SeqPlan c{0, 0, 0};
     if (b < num_seqs) {
       start = cu[b];
       const int end = cu[b + 1];
@@ -106,42 +110,55 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       c = count_seq(len, pre, seg_tiles, max_segs);
     }
     const int si = wave_incl_scan(c.items, lane);
+    const int sd = wave_incl_scan(c.dec, lane);
     const int sm = wave_incl_scan(c.merges, lane);
     if (lane == 63) {
       wsum[0][wave] = si;
-      wsum[1][wave] = sm;
+      wsum[1][wave] = sd;
+      wsum[2][wave] = sm;
     }
     __syncthreads();
-    int64_t off_i = base_i + si - c.items, off_m = base_m + sm - c.merges;
-    int64_t tot_i = 0, tot_m = 0;
+    int64_t off_i = base_i + si - c.items, off_d = base_d + sd - c.dec, off_m = base_m + sm - c.merges;
+    int64_t tot_i = 0, tot_d = 0, tot_m = 0;
     for (int w = 0; w < kPlanThreads / 64; ++w) {
       if (w < wave) {
         off_i += wsum[0][w];
-        off_m += wsum[1][w];
+        off_d += wsum[1][w];
+        off_m += wsum[2][w];
       }
       tot_i += wsum[0][w];
-      tot_m += wsum[1][w];
+      tot_d += wsum[1][w];
+      tot_m += wsum[2][w];
     }
     __syncthreads();  // wsum is rewritten by the next round
-    if (c.items > 0) {
+    if (c.items + c.dec > 0) {
       for (int qb = 0; qb * kQueryBlock < len; ++qb) {
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
         const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
-        for (int s = 0; s < ns; ++s, ++off_i)
-          if (off_i < max_items) items[off_i] = make_int4(b, qb, s, ns);
+        for (int s = 0; s < ns; ++s) {
+          if (len == 1) {
+            if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
+            ++off_d;
+          } else {
+            if (off_i < max_items) items[off_i] = make_int4(b, qb, s, ns);
+            ++off_i;
+          }
+        }
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
       }
     }
     base_i += tot_i;
+    base_d += tot_d;
     base_m += tot_m;
   }
   if (tid == 0) {
     hdr[0] = (int32_t)(base_i < max_items ? base_i : max_items);
     hdr[1] = (int32_t)(base_m < max_merges ? base_m : max_merges);
+    hdr[2] = (int32_t)(base_d < max_dec ? base_d : max_dec);
   }
 }
 
@@ -191,6 +208,233 @@ void splitkv_merge_kernel(const int32_t* __restrict__ hdr, const int4* __restric
   }
 }
 
+// ---------------------------------------------------------------- decode rows
+// A length-1 row is one query against its cached prefix plus itself: per key
+// 4 D flops against 4 D bytes of K and V, so the pass is bound by HBM, not by
+// the matrix cores.  It runs on the vector ALUs straight from 16-byte loads:
+// lane l of a wave owns the 8 elements d = 8 (l % LPK) + [0, 8) of key slot
+// l / LPK (LPK = D / 8 lanes per key, KPI = 64 / LPK keys per step); the
+// scores come from a DPP butterfly over each key's LPK lanes, and every key
+// slot keeps its own online-softmax state, combined across slots and waves at
+// the end of the unit.  A unit is (item, GC query heads of one K/V head):
+// each K/V row loaded serves all GC heads.
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPK (4, 8 or 16) lanes, result in every lane.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f<0xB1>(x);                            // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);                            // quad_perm [2,3,0,1]
+  if constexpr (LPK >= 8) x += dpp_f<0x141>(x);   // row_half_mirror
+  if constexpr (LPK >= 16) x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 w, float (&f)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float lane_read(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x)));
+}
+
+constexpr int kDecThreads = 256;
+constexpr int kDecUnroll = 4;        // key steps whose loads are issued together
+constexpr float kDecRescale = 8.0f;  // lazy rescale headroom, log2 units
+constexpr float kDecMInit = -1.0e30f;
+
+template <int D, int GC>
+__global__ __launch_bounds__(kDecThreads)
+void splitkv_decode_kernel(FwdParams p) {
+  constexpr int LPK = D / 8, KPI = 64 / LPK;
+  __shared__ float red[4][GC][2 + D];
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  // wave-uniform in a scalar register: the key loop below is then a scalar loop
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kslot = lane / LPK, dch = lane % LPK;
+  const int H = p.num_heads, HK = p.num_kv_heads, G = H / HK;
+  const int units = H / GC;
+  const int64_t steps = (int64_t)p.hdr[2] * units;
+  const float c = p.scale_log2;
+  const int seg_keys = p.seg_tiles * kKeyTile;
+  const float neg_inf = -__builtin_huge_valf();
+
+  for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += p.dec_grid) {
+    const int4 it = p.dec_items[g / units];
+    const int h0 = (int)(g % units) * GC;
+    const int hk = h0 / G;
+    const int b = it.x, s = it.y, ns = it.z;
+    const int tok = p.cu[b];
+    const int pre = p.prefix[b];
+    const int k0 = s * seg_keys;
+    const int k1 = min(k0 + seg_keys, pre + 1);  // keys [k0, k1) of this segment
+    const int per = ((k1 - k0 + 3) / 4 + KPI - 1) / KPI * KPI;
+    const int w0 = k0 + wave * per;
+    const int w1 = min(w0 + per, k1);            // this wave's keys
+    const int64_t crow = ((int64_t)b * HK + hk) * p.cap;
+    const uint16_t* __restrict__ kc = p.kc + crow * D;  // this (sequence, K/V head)'s cache
+    const uint16_t* __restrict__ vc = p.vc + crow * D;
+    const uint16_t* kn = p.k + ((int64_t)tok * HK + hk) * D + 8 * dch;  // the row's own key
+    const uint16_t* vn = p.v + ((int64_t)tok * HK + hk) * D + 8 * dch;
+    const int wc = min(w1, pre);  // the wave's cached keys are [w0, wc); key pre comes from k, v
+    float qf[GC][8], o[GC][8], m[GC], l[GC];
+#pragma unroll
+    for (int gi = 0; gi < GC; ++gi) {
+      uint4 w = *(const uint4*)(p.q + ((int64_t)tok * H + h0 + gi) * D + 8 * dch);
+      if (p.neg_q) {
+        w.x ^= 0x80008000u;
+        w.y ^= 0x80008000u;
+        w.z ^= 0x80008000u;
+        w.w ^= 0x80008000u;
+      }
+      bf16x8_to_f32(w, qf[gi]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[gi][i] = 0.f;
+      m[gi] = kDecMInit;
+      l[gi] = 0.f;
+    }
+
+    // cached keys kb + u KPI + kslot of a group of kDecUnroll steps; positions
+    // past the wave's last cached key load that key again (and are masked)
+    auto load = [&](int kb, uint4 (&kr)[kDecUnroll], uint4 (&vr)[kDecUnroll]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) {
+        const uint32_t off = (uint32_t)min(kb + u * KPI + kslot, wc - 1) * D + 8 * dch;
+        kr[u] = *(const uint4*)(kc + off);
+        vr[u] = *(const uint4*)(vc + off);
+      }
+    };
+    auto consume_one = [&](bool ok, const uint4 kr, const uint4 vr) __attribute__((always_inline)) {
+      float kf[8], vf[8];
+      bf16x8_to_f32(kr, kf);
+      bf16x8_to_f32(vr, vf);
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        float d0 = qf[gi][0] * kf[0], d1 = qf[gi][1] * kf[1];
+#pragma unroll
+        for (int i = 2; i < 8; i += 2) {
+          d0 = __builtin_fmaf(qf[gi][i], kf[i], d0);
+          d1 = __builtin_fmaf(qf[gi][i + 1], kf[i + 1], d1);
+        }
+        const float dot = group_sum<LPK>(d0 + d1);  // every lane, then the mask
+        const float sc = ok ? dot * c : neg_inf;
+        if (__any(sc > m[gi] + kDecRescale)) {
+          const float mn = fmaxf(m[gi], sc);
+          const float a = __builtin_amdgcn_exp2f(m[gi] - mn);
+          l[gi] *= a;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[gi][i] *= a;
+          m[gi] = mn;
+        }
+        const float pe = __builtin_amdgcn_exp2f(sc - m[gi]);
+        l[gi] += pe;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[gi][i] = __builtin_fmaf(pe, vf[i], o[gi][i]);
+      }
+    };
+    auto consume = [&](int kb, const uint4 (&kr)[kDecUnroll], const uint4 (&vr)[kDecUnroll]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) consume_one(kb + u * KPI + kslot < wc, kr[u], vr[u]);
+    };
+    // two register sets: the next group's loads are in flight while a group
+    // is consumed
+    if (w0 < wc) {
+      constexpr int kStep = kDecUnroll * KPI;
+      uint4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
+      load(w0, ka, va);
+      for (int kb = w0;; kb += 2 * kStep) {
+        load(kb + kStep, kb2, vb2);
+        consume(kb, ka, va);
+        if (kb + kStep >= wc) break;
+        load(kb + 2 * kStep, ka, va);
+        consume(kb + kStep, kb2, vb2);
+        if (kb + 2 * kStep >= wc) break;
+      }
+    }
+    if (w0 <= pre && pre < w1)  // the row's own key, in key slot 0
+      consume_one(kslot == 0, *(const uint4*)kn, *(const uint4*)vn);
+
+    // combine the KPI key slots of the wave (lanes l and l ^ x, x >= LPK)
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) {
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        const float m2 = lane_read(m[gi], lane ^ x);
+        const float l2 = lane_read(l[gi], lane ^ x);
+        const float mn = fmaxf(m[gi], m2);
+        const float a = __builtin_amdgcn_exp2f(m[gi] - mn), a2 = __builtin_amdgcn_exp2f(m2 - mn);
+        l[gi] = l[gi] * a + l2 * a2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[gi][i] = o[gi][i] * a + lane_read(o[gi][i], lane ^ x) * a2;
+        m[gi] = mn;
+      }
+    }
+    // then the four waves, through LDS
+    if (lane < LPK) {
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        if (lane == 0) {
+          red[wave][gi][0] = m[gi];
+          red[wave][gi][1] = l[gi];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[wave][gi][2 + 8 * dch + i] = o[gi][i];
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < LPK) {
+#pragma unroll
+      for (int gi = 0; gi < GC; ++gi) {
+        float mm = red[0][gi][0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) mm = fmaxf(mm, red[w][gi][0]);
+        float ll = 0.f, oo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) oo[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float a = __builtin_amdgcn_exp2f(red[w][gi][0] - mm);
+          ll = __builtin_fmaf(red[w][gi][1], a, ll);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) oo[i] = __builtin_fmaf(red[w][gi][2 + 8 * dch + i], a, oo[i]);
+        }
+        const float inv = ll > 0.f ? 1.f / ll : 0.f;
+        const int64_t row = (int64_t)tok * H + h0 + gi;
+        if (ns == 1) {
+          uint4 w;
+          w.x = pack_bf16x2(oo[0] * inv, oo[1] * inv);
+          w.y = pack_bf16x2(oo[2] * inv, oo[3] * inv);
+          w.z = pack_bf16x2(oo[4] * inv, oo[5] * inv);
+          w.w = pack_bf16x2(oo[6] * inv, oo[7] * inv);
+          *(uint4*)(p.out + row * D + 8 * dch) = w;
+        } else {
+          const int64_t slot = row * p.max_segs + s;
+          float* dst = p.part_o + slot * D + 8 * dch;
+          *(float4*)dst = make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
+          *(float4*)(dst + 4) = make_float4(oo[4] * inv, oo[5] * inv, oo[6] * inv, oo[7] * inv);
+          if (lane == 0) p.part_lse[slot] = ll > 0.f ? mm + __builtin_amdgcn_logf(ll) : neg_inf;
+        }
+      }
+    }
+    // the segment holding the row's own position writes its K/V to the cache,
+    // once per K/V head (the unit of the group's first query heads)
+    if (wave == 1 && lane < LPK && s == ns - 1 && h0 == hk * G) {
+      *(uint4*)(p.kc + (crow + pre) * D + 8 * dch) = *(const uint4*)kn;
+      *(uint4*)(p.vc + (crow + pre) * D + 8 * dch) = *(const uint4*)vn;
+    }
+    __syncthreads();  // red is rewritten by the next unit
+  }
+}
+
 }  // namespace
 
 SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
@@ -204,11 +448,13 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
   if (L.max_segs < 1) L.max_segs = 1;
   L.max_blocks = (int64_t)num_tokens / kQueryBlock + num_seqs + 1;
   L.max_items = L.max_blocks * L.max_segs;
+  L.max_dec_items = ((int64_t)num_seqs + 1) * L.max_segs;
   const int64_t max_merges = (int64_t)num_tokens / kMergeRows + num_seqs + 1;
   const size_t slots = (size_t)num_tokens * num_heads * L.max_segs;
   L.off_hdr = 0;
   L.off_items = 256;
-  L.off_merges = L.off_items + round256(16 * (size_t)L.max_items);
+  L.off_dec = L.off_items + round256(16 * (size_t)L.max_items);
+  L.off_merges = L.off_dec + round256(16 * (size_t)L.max_dec_items);
   L.off_lse = L.off_merges + round256(16 * (size_t)max_merges);
   L.off_o = L.off_lse + round256(4 * slots);
   L.bytes = L.off_o + round256(4 * slots * head_dim);
@@ -221,9 +467,10 @@ hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t
   char* base = static_cast<char*>(ws);
   const int64_t max_merges = (int64_t)(L.off_lse - L.off_merges) / 16;
   hipLaunchKernelGGL(splitkv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, prefix,
-                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, L.max_items, max_merges,
-                     reinterpret_cast<int32_t*>(base + L.off_hdr),
+                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, L.max_items, L.max_dec_items,
+                     max_merges, reinterpret_cast<int32_t*>(base + L.off_hdr),
                      reinterpret_cast<int4*>(base + L.off_items),
+                     reinterpret_cast<int4*>(base + L.off_dec),
                      reinterpret_cast<int4*>(base + L.off_merges));
   return hipGetLastError();
 }
@@ -239,6 +486,62 @@ hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const 
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace pa
+
+namespace pa {
+
+int splitkv_heads_per_unit(int num_heads, int num_kv_heads) {
+  const int g = num_heads / num_kv_heads;
+  return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
+}
+
+namespace {
+template <int D>
+hipError_t decode_d(const FwdParams& p, int gc, hipStream_t stream) {
+  const dim3 grid(p.dec_grid), block(kDecThreads);
+  switch (gc) {
+    case 1: hipLaunchKernelGGL((splitkv_decode_kernel<D, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((splitkv_decode_kernel<D, 2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((splitkv_decode_kernel<D, 4>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((splitkv_decode_kernel<D, 8>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template <int D>
+int decode_occ(int gc) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (gc) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 1>, kDecThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 2>, kDecThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 4>, kDecThreads, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 8>, kDecThreads, 0); break;
+    default: break;
+  }
+  return e == hipSuccess ? n : 0;
+}
+}  // namespace
+
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit,
+                                 hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return decode_d<32>(p, heads_per_unit, stream);
+    case 64: return decode_d<64>(p, heads_per_unit, stream);
+    case 128: return decode_d<128>(p, heads_per_unit, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit) {
+  switch (head_dim) {
+    case 32: return decode_occ<32>(heads_per_unit);
+    case 64: return decode_occ<64>(heads_per_unit);
+    case 128: return decode_occ<128>(heads_per_unit);
+    default: return 0;
+  }
 }
 
 }  // namespace pa

@@ -61,7 +61,7 @@ def run_split(q, k, v, cu, pre, kc, vc, scale, ws=None, max_seqlen=None):
     return out
 
 
-def check_case(lengths, prefix, cap, H, HK, D, seed, what):
+def check_case(lengths, prefix, cap, H, HK, D, seed, what, scale=None):
     g = I.generator(seed)
     cu = I.cu_from_lengths(lengths)
     N, B = cu[-1], len(lengths)
@@ -70,8 +70,9 @@ def check_case(lengths, prefix, cap, H, HK, D, seed, what):
     v = I.randn_bf16(g, (N, HK, D))
     kc0 = sentinel_cache(g, B, HK, cap, D, prefix)
     vc0 = sentinel_cache(g, B, HK, cap, D, prefix)
-    scale = I.default_scale(D)
-    say("case %s: lengths=%s prefix=%s cap=%d H=%d HK=%d D=%d" % (what, lengths, prefix, cap, H, HK, D))
+    scale = I.default_scale(D) if scale is None else scale
+    say("case %s: lengths=%s prefix=%s cap=%d H=%d HK=%d D=%d scale=%g"
+        % (what, lengths, prefix, cap, H, HK, D, scale))
     whole, need = workspace_for(B, N, H, D, cap)
     kc, vc = kc0.cuda(), vc0.cuda()
     out = run_split(q, k, v, cu, prefix, kc, vc, scale, ws=whole[:need])
@@ -95,10 +96,22 @@ def test_splitkv_segment_edges_full(D):
     check_case(LENGTHS, PREFIX, 3000, 3, 3, D, 900 + D, "splitkv edges D=%d" % D)
 
 
-@pytest.mark.parametrize("H,HK,D", [(8, 2, 128), (4, 1, 64)])
+@pytest.mark.parametrize("H,HK,D", [(8, 2, 128), (4, 1, 64), (16, 2, 64), (6, 3, 32), (32, 1, 128)])
 def test_splitkv_grouped_heads(H, HK, D):
+    # decode rows share each K/V load among 4, 4, 8, 2 and 8 query heads
     check_case([96, 1, 1, 33, 1], [1500, 3000, 1, 64, 2048], 3100, H, HK, D, 910 + H + D,
                "splitkv gqa H=%d HK=%d" % (H, HK))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.0])
+def test_splitkv_other_scales(scale):
+    check_case([1, 70, 1], [1500, 1100, 3], 1600, 4, 4, 64, 950, "splitkv scale", scale=scale)
+
+
+def test_splitkv_decode_rows_only():
+    """A batch of decode rows only (no prompt chunk), contexts across segment edges."""
+    ctx = [0, 1, 63, 64, 1023, 1024, 1025, 2047, 2048, 4095, 5000]
+    check_case([1] * len(ctx), ctx, 5001, 4, 4, 128, 960, "splitkv decode only")
 
 
 def test_splitkv_long_context_many_segments():
