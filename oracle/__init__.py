@@ -55,6 +55,8 @@ def _load():
     lib.oracle_prefill_rows.restype = ctypes.c_int
     lib.oracle_cache_image.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
     lib.oracle_cache_image.restype = ctypes.c_int
+    lib.oracle_quantize_rows_int8.argtypes = [p, ctypes.c_int64, i32, p, p]
+    lib.oracle_quantize_rows_int8.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -227,3 +229,32 @@ def cache_image(k, v, cu_seqlens, k_cache, v_cache, prefix_lens=None):
                                     _ptr(kc), _ptr(vc))
     _check(rc, "cache_image")
     return kc, vc
+
+
+def quantize_rows_int8(x):
+    """INT8 codes and float32 scales of bf16 rows (the last axis is one row):
+    symmetric, one scale per row, scale = amax/127, code = rint(x * 127/amax)
+    in float32 (see oracle.c).  Returns (codes int8 x.shape, scales float32
+    x.shape[:-1])."""
+    a = _u16(x)
+    d = a.shape[-1]
+    rows = a.size // d if d else 0
+    codes = np.zeros(a.shape, np.int8)
+    scales = np.zeros(a.shape[:-1], np.float32)
+    rc = _load().oracle_quantize_rows_int8(_ptr(a), rows, d, _ptr(codes), _ptr(scales))
+    _check(rc, "quantize_rows_int8")
+    return codes, scales
+
+
+def cache_image_int8(k, v, cu_seqlens):
+    """INT8 varlen cache image: the bf16 varlen image of cache_image (sequence
+    b's [HK, len_b, D] block at row cu[b]*HK) with every (token, K/V head) row
+    quantised by quantize_rows_int8.  Returns (k_codes, k_scales, v_codes,
+    v_scales) as flat arrays of N*HK*D int8 and N*HK float32."""
+    kk = _u16(k)
+    N, HK, D = kk.shape
+    z = np.zeros(N * HK * D, np.uint16)
+    kimg, vimg = cache_image(k, v, cu_seqlens, z, z)
+    kq, ks = quantize_rows_int8(kimg.reshape(N * HK, D))
+    vq, vs = quantize_rows_int8(vimg.reshape(N * HK, D))
+    return kq.reshape(-1), ks.reshape(-1), vq.reshape(-1), vs.reshape(-1)

@@ -357,6 +357,53 @@ int oracle_cache_image(const uint16_t *k, const uint16_t *v, const int32_t *cu_s
     return 0;
 }
 
+/*
+ * INT8 rows for a quantised KV cache [P2 §4.3: only K and V are quantised,
+ * Q keeps its precision; INT8 halves the cache; the scale may be per tensor,
+ * per channel or per token, finer being more accurate].  The pages fix no
+ * formula; the reading taken here is symmetric, one float32 scale per
+ * (token, K/V head) row of D values:
+ *     amax  = max_d |x_d|              (bf16 widened to float: exact)
+ *     scale = amax / 127               (float32 division, round to nearest)
+ *     code  = rint(x_d * (127 / amax)) (float32 division and product, ties
+ *                                       to even), in [-127, 127]
+ * and a row with amax < 2^-100 (127 / amax would leave float32's range for
+ * the smallest bf16 values) is stored as scale 0 with all codes 0.  The
+ * dequantised value is code * scale.  The integer decision is made in
+ * float32 -- the precision of the kernel's epilogue -- with the same
+ * operations, so codes and scales compare bit for bit.  x is rows * d bf16
+ * values, row-major; codes rows * d, scales rows.
+ */
+int oracle_quantize_rows_int8(const uint16_t *x, int64_t rows, int32_t d,
+                              int8_t *codes, float *scales)
+{
+    if (rows < 0 || d < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * d;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < d; ++i) {
+            const float a = fabsf((float)bf16_bits_to_double(xr[i]));
+            if (a > amax) amax = a;
+        }
+        int8_t *cr = codes + r * d;
+        if (!(amax >= 0x1p-100f)) {
+            scales[r] = 0.0f;
+            for (int32_t i = 0; i < d; ++i) cr[i] = 0;
+            continue;
+        }
+        scales[r] = amax / 127.0f;
+        const float inv = 127.0f / amax;
+        for (int32_t i = 0; i < d; ++i) {
+            float t = rintf((float)bf16_bits_to_double(xr[i]) * inv);
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            cr[i] = (int8_t)t;
+        }
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -442,3 +442,97 @@ def test_gqa_rejects_heads_that_do_not_divide():
     q, k, v = _gqa_inputs(4, 6, 4, 32, 361)
     with pytest.raises(ValueError):
         oracle.prefill_varlen(bits(q), bits(k), bits(v), [0, 4], 0.1)
+
+
+# ---------------------------------------------------------------- INT8 KV rows
+# Quantised cache rows ("大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.3:
+# K and V only, INT8 halves the cache, per-token scales are one of the listed
+# granularities).  The oracle's reading: symmetric, one float32 scale per
+# (token, K/V head) row, scale = amax/127, code = rint(x * 127/amax).
+
+def _bf16(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+
+
+def test_int8_exact_grid_ties_to_even():
+    """amax = 127/64 makes 127/amax = 64 exactly, so every code is
+    round-half-even(64 x) of an exact product: checked with Fractions.  The
+    other entries are k/128, so odd k land exactly on a tie."""
+    from fractions import Fraction
+    ks = [-127, 5, -5, 7, 3, -3, 1, 0, 64, 65, -66, 100, 2, 9, -11]
+    x = _bf16([127 / 64.0] + [k / 128.0 for k in ks])
+    codes, scales = oracle.quantize_rows_int8(x.view(1, -1))
+    want = [127] + [round(Fraction(64) * Fraction(k, 128)) for k in ks]  # Python round: ties to even
+    assert codes[0].tolist() == want
+    assert want[2:5] == [2, -2, 4] and want[5:7] == [2, -2]  # 2.5->2, -2.5->-2, 3.5->4, 1.5->2
+    assert scales[0] == np.float32(1 / 64)
+
+
+def test_int8_hand_example():
+    """Row [1, -2, 0.5, 0.25, 0.75, -1.5, 0, 0]: amax 2, 127/amax = 63.5 exactly,
+    products exact, codes 64 (63.5 to even), -127, 32 (31.75), 16 (15.875),
+    48 (47.625), -95 (-95.25), 0, 0; scale = 2/127 rounded to float32."""
+    from fractions import Fraction
+    codes, scales = oracle.quantize_rows_int8(_bf16([[1, -2, 0.5, 0.25, 0.75, -1.5, 0, 0]]))
+    assert codes[0].tolist() == [64, -127, 32, 16, 48, -95, 0, 0]
+    s = Fraction(float(scales[0]))
+    ulp = Fraction(2) ** (-7 - 23)  # 2/127 lies in [2^-7, 2^-6)
+    assert abs(s - Fraction(2, 127)) <= ulp / 2
+
+
+@pytest.mark.parametrize("sigma", [1.0, 1e-3, 40.0])
+def test_int8_properties_random_rows(sigma):
+    g = torch.Generator().manual_seed(77)
+    x = (torch.randn(500, 128, generator=g) * sigma).to(torch.bfloat16)
+    codes, scales = oracle.quantize_rows_int8(x)
+    xf = x.float().double().numpy()
+    c = codes.astype(np.float64)
+    s = scales.astype(np.float64)
+    assert np.all(np.abs(codes.astype(np.int32)) <= 127)
+    # the largest |x| of each row maps to +-127 with the sign of x
+    arg = np.abs(xf).argmax(axis=1)
+    top = c[np.arange(len(arg)), arg]
+    assert np.all(np.abs(top) == 127) and np.all(np.sign(top) == np.sign(xf[np.arange(len(arg)), arg]))
+    # dequantisation error at most half a step (plus float32 rounding slop)
+    err = np.abs(xf - c * s[:, None])
+    assert np.all(err <= 0.5 * s[:, None] * (1 + 2.0 ** -20) + 2.0 ** -22 * np.abs(xf))
+    # scale is amax / 127 to float32 accuracy
+    amax = np.abs(xf).max(axis=1)
+    assert np.allclose(s, amax / 127, rtol=2.0 ** -23, atol=0)
+    # odd symmetry and invariance under power-of-two scaling
+    cn, sn = oracle.quantize_rows_int8(-x)
+    assert np.array_equal(cn, -codes) and np.array_equal(sn, scales)
+    c4, s4 = oracle.quantize_rows_int8((x.float() * 4).to(torch.bfloat16))
+    assert np.array_equal(c4, codes) and np.array_equal(s4, scales * 4)
+
+
+def test_int8_zero_and_tiny_rows():
+    x = torch.zeros(3, 64, dtype=torch.bfloat16)
+    x[1, 5] = 1e-35   # amax below 2^-100: stored as zeros
+    x[2, 7] = -3.0
+    codes, scales = oracle.quantize_rows_int8(x)
+    assert scales[0] == 0 and scales[1] == 0 and not codes[:2].any()
+    assert codes[2, 7] == -127 and np.count_nonzero(codes[2]) == 1
+    from fractions import Fraction
+    assert abs(Fraction(float(scales[2])) - Fraction(3, 127)) <= Fraction(2) ** (-6 - 23) / 2
+
+
+def test_int8_cache_image_layout_bruteforce():
+    """Sequence b's [HK, len_b, D] block at row cu[b]*HK: placement checked
+    row by row against single-row quantisation."""
+    lengths, HK, D = [3, 1, 5], 2, 32
+    g = torch.Generator().manual_seed(78)
+    N = sum(lengths)
+    k = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    cu = [0, 3, 4, 9]
+    kq, ks, vq, vs = oracle.cache_image_int8(k, v, cu)
+    assert kq.shape == (N * HK * D,) and ks.shape == (N * HK,)
+    for b, L in enumerate(lengths):
+        for hk in range(HK):
+            for t in range(L):
+                row = cu[b] * HK + hk * L + t
+                ck, sk = oracle.quantize_rows_int8(k[cu[b] + t, hk].view(1, D))
+                cv, sv = oracle.quantize_rows_int8(v[cu[b] + t, hk].view(1, D))
+                assert np.array_equal(kq[row * D:(row + 1) * D], ck[0]) and ks[row] == sk[0]
+                assert np.array_equal(vq[row * D:(row + 1) * D], cv[0]) and vs[row] == sv[0]
