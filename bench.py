@@ -285,6 +285,20 @@ def main():
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+
+    # the same step writing an INT8 cache (codes + one float scale per token
+    # and K/V head) instead of the bf16 cache
+    kq8 = torch.empty((N * HK * D,), dtype=torch.int8, device=dev)
+    vq8 = torch.empty_like(kq8)
+    ks8 = torch.empty((N * HK,), dtype=torch.float32, device=dev)
+    vs8 = torch.empty_like(ks8)
+
+    def step_int8():
+        P.prefill_attn_varlen_int8(qd, kd, vd, cu, kq8, vq8, ks8, vs8, out, scale=w.scale,
+                                   max_seqlen=max_seqlen)
+
+    ms8, launches8 = timed(step_int8, args.steps, args.warmup)
+    cache8_bytes = 2.0 * N * HK * (D + 4)
     traffic, traffic_note = read_traffic() if args.workload == "single_T2048_H32_D128" else (None, "n/a")
 
     res = {
@@ -315,6 +329,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
+        "int8_cache": {"launch_us_mean": round(sum(launches8) / len(launches8) * 1e3, 2),
+                       "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2),
+                       "cache_bytes_written": cache8_bytes,
+                       "bf16_cache_bytes": kv_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -23,7 +23,9 @@
  *     over keys of sequence b only [P1 §3 and P4 §2.2 formula; P5 §1.1 causal
  *     visibility; P3 §2 no attention across requests].
  *   - head_dim D in {32, 64, 128}.  scale: any finite float (0 allowed); the
- *     usual value is 1/sqrt(D).
+ *     usual value is 1/sqrt(D).  Scores |scale * q.k| up to 2^26 are supported
+ *     (attention logits are many orders of magnitude smaller); beyond that the
+ *     softmax weights may overflow.
  *   - All pointers are caller-owned device memory aligned to 16 bytes.  The
  *     library keeps no pointer after returning, allocates no memory, creates
  *     no stream and never synchronises the device (except in check mode,
@@ -154,6 +156,33 @@ pa_status prefill_attn_chunked_gqa(const uint16_t *q, const uint16_t *k, const u
                                    int32_t head_dim, uint16_t *k_cache, uint16_t *v_cache,
                                    int32_t cache_capacity, uint16_t *out, float scale,
                                    hipStream_t stream, const int32_t *prefix_lens);
+
+/*
+ * Varlen prefill writing an INT8 KV cache.  Attention is computed exactly as
+ * prefill_attn_varlen_gqa (on the bf16 inputs); only the cache write differs:
+ * K and V are quantised, Q is not [P2 §4.3: quantising the KV cache to INT8
+ * halves its size and read traffic; scales may be per tensor, per channel or
+ * per token].  Each (token, K/V head) row of D values gets one float scale:
+ *     scale = amax / 127,  code = rint(x * (127 / amax)),  |code| <= 127,
+ * in float32 with ties to even (a row whose amax is below 2^-100 is stored
+ * as scale 0 and codes 0); the value it stands for is code * scale.
+ *
+ *   k_cache, v_cache   int8 device, written only, laid out as the bf16 varlen
+ *                      cache: sequence b's [HK, len_b, D] block starts at
+ *                      byte cu[b] * HK * D (N * HK * D bytes in total).
+ *   k_scale, v_scale   float device, written only: sequence b's [HK, len_b]
+ *                      block starts at element cu[b] * HK (N * HK floats).
+ *   other arguments    as prefill_attn_varlen_gqa.
+ *
+ * Errors as prefill_attn_varlen_gqa; the scale pointers are outputs too
+ * (PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_ALIAS apply to them).
+ */
+pa_status prefill_attn_varlen_int8(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int8_t *k_cache, int8_t *v_cache,
+                                   float *k_scale, float *v_scale, uint16_t *out, float scale,
+                                   hipStream_t stream);
 
 /*
  * Split-KV chunked prefill.  Same result and cache writes as

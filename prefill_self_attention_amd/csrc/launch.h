@@ -34,6 +34,12 @@ struct FwdParams {
   int32_t split_grid;       // work-groups of the persistent split-KV launch
   const int4* dec_items;    // decode-row items: {sequence, segment, segments, 0}; hdr[2] of them
   int32_t dec_grid;         // work-groups of the persistent decode launch
+  // INT8 cache (varlen only): codes in kq/vq laid out as kc/vc, one float
+  // scale per (token, K/V head) row in ks/vs (the cache layout without D)
+  int8_t* kq;
+  int8_t* vq;
+  float* ks;
+  float* vs;
 };
 
 // Query rows per block, and work-groups per (head, sequence) for a maximum length.
@@ -43,6 +49,9 @@ int fwd_grid_blocks(int max_seqlen);
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream);
+// Varlen with an INT8 cache (kq, vq, ks, vs instead of kc, vc).
+hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,
+                                   hipStream_t stream);
 
 // ------------------------------------------------------------ split-KV layout
 // Workspace of the split-KV chunked call, carved from one caller buffer.

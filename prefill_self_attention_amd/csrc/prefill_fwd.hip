@@ -164,6 +164,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
 }
 
+// ---------------------------------------------------------------- INT8 rows
+// Symmetric INT8 cache rows, one float scale per (token, K/V head) row of D
+// values ["大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.3: K and V
+// quantised, Q kept; INT8 halves the cache; per-token scales are one of the
+// granularities it lists]: scale = amax / 127, code = rint(x * (127 / amax))
+// with ties to even, both in float32; rows with amax < 2^-100 are stored as
+// scale 0 and codes 0.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+// maximum over aligned groups of N (4, 8 or 16) lanes, in every lane
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));                            // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));                            // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x = fmaxf(x, dpp_f<0x141>(x));     // row_half_mirror
+  if constexpr (N >= 16) x = fmaxf(x, dpp_f<0x140>(x));    // row_mirror
+  return x;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float absmax8(const u32x4_t w) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  return m;
+}
+constexpr float kInt8MinAmax = 0x1p-100f;
+__device__ __forceinline__ float int8_scale(float amax) { return amax >= kInt8MinAmax ? amax / 127.0f : 0.0f; }
+__device__ __forceinline__ uint32_t int8_code(float x, float inv) {
+  const float t = fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)t & 0xffu;
+}
+__device__ __forceinline__ u32x2_t quantize8(const u32x4_t w, float amax) {
+  const float inv = amax >= kInt8MinAmax ? 127.0f / amax : 0.0f;
+  u32x2_t r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    r[i] = int8_code(bf16_lo(w[2 * i]), inv) | int8_code(bf16_hi(w[2 * i]), inv) << 8 |
+           int8_code(bf16_lo(w[2 * i + 1]), inv) << 16 | int8_code(bf16_hi(w[2 * i + 1]), inv) << 24;
+  return r;
+}
+
 template <int D>
 struct Cfg {
   static constexpr int kCpr = D / 8;                    // 16-byte chunks per row
@@ -253,7 +297,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // one of the nseg segments of its keys.  A block with one segment is stored
 // as usual; otherwise its rows get a partial result (normalised O in fp32 and
 // log2 of its sum of weights), merged by a later pass.
-template <int D, bool kChunked, bool kSplit>
+template <int D, bool kChunked, bool kSplit, bool kInt8 = false>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z, int seg, int nseg) {
   using C = Cfg<D>;
   // Every LDS read in the main loop is inline asm (lds_read_* above), so the
@@ -369,7 +413,21 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       const int idx = gl + kGroupThreads * i;
       const int row = idx / C::kCpr, ch = idx % C::kCpr;
       const int kp = t0 + row;
-      if (kp >= blk.own_lo && kp < blk.key_end) {
+      const bool mine = kp >= blk.own_lo && kp < blk.key_end;
+      if constexpr (kInt8) {
+        // the row's absolute maximum over its kCpr lanes (all lanes take part)
+        const float ka = group_max<C::kCpr>(absmax8(kr[i]));
+        const float va = group_max<C::kCpr>(absmax8(vr[i]));
+        if (mine) {
+          const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
+          *(u32x2_t*)(p.kq + dst) = quantize8(kr[i], ka);
+          *(u32x2_t*)(p.vq + dst) = quantize8(vr[i], va);
+          if (ch == 0) {
+            p.ks[cache_base / D + kp] = int8_scale(ka);
+            p.vs[cache_base / D + kp] = int8_scale(va);
+          }
+        }
+      } else if (mine) {
         const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
         *(u32x4_t*)(p.kc + dst) = kr[i];
         *(u32x4_t*)(p.vc + dst) = vr[i];
@@ -698,13 +756,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   }
 }
 
-template <int D, bool kChunked>
+template <int D, bool kChunked, bool kInt8 = false>
 __global__ __launch_bounds__(kThreads)
 void prefill_fwd_kernel(FwdParams p) {
   // raw id builtins: the device library's id helpers are built with IEEE mode
   // on and would not inline into this IEEE-off kernel
-  fwd_item<D, kChunked, false>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
-                               __builtin_amdgcn_workgroup_id_z(), 0, 1);
+  fwd_item<D, kChunked, false, kInt8>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
+                                      __builtin_amdgcn_workgroup_id_z(), 0, 1);
 }
 
 // Split-KV chunked prefill: a persistent grid walks the planned items, item i
@@ -731,6 +789,18 @@ hipError_t launch_d(const FwdParams& p, int num_seqs, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,
+                                   hipStream_t stream) {
+  const dim3 grid(p.num_heads, num_seqs, p.grid_z);
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL((prefill_fwd_kernel<32, false, true>), grid, dim3(kThreads), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((prefill_fwd_kernel<64, false, true>), grid, dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((prefill_fwd_kernel<128, false, true>), grid, dim3(kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(p.split_grid);
