@@ -55,6 +55,9 @@ def _load():
     lib.oracle_prefill_rows.restype = ctypes.c_int
     lib.oracle_cache_image.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
     lib.oracle_cache_image.restype = ctypes.c_int
+    lib.oracle_prefill_chunked_paged.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, i32, p,
+                                                 ctypes.c_float, p, p, p]
+    lib.oracle_prefill_chunked_paged.restype = ctypes.c_int
     lib.oracle_quantize_rows_int8.argtypes = [p, ctypes.c_int64, i32, p, p]
     lib.oracle_quantize_rows_int8.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -258,3 +261,29 @@ def cache_image_int8(k, v, cu_seqlens):
     kq, ks = quantize_rows_int8(kimg.reshape(N * HK, D))
     vq, vs = quantize_rows_int8(vimg.reshape(N * HK, D))
     return kq.reshape(-1), ks.reshape(-1), vq.reshape(-1), vs.reshape(-1)
+
+
+def prefill_chunked_paged(q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache, block_table, scale):
+    """Chunked prefill over a paged cache (see oracle.c): k_cache / v_cache are
+    [num_blocks, HK, 16, D] bf16, block_table [B, max_blocks_per_seq] int32.
+    Returns (out float64 [N, H, D], k_cache image, v_cache image)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    cu = _i32(cu_seqlens)
+    pre = _i32(prefix_lens)
+    bt = _i32(block_table)
+    kc = _u16(k_cache).copy()
+    vc = _u16(v_cache).copy()
+    N, H, D = q.shape
+    HK = k.shape[1]
+    B = cu.shape[0] - 1
+    nb = kc.shape[0]
+    if kc.shape != (nb, HK, 16, D) or vc.shape != kc.shape:
+        raise ValueError("paged cache must be [num_blocks, HK, 16, D]")
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block table must be [B, max_blocks_per_seq]")
+    out = np.zeros((N, H, D), np.float64)
+    rc = _load().oracle_prefill_chunked_paged(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, H, HK, D, nb, _ptr(bt), bt.shape[1], _ptr(pre),
+        ctypes.c_float(scale), _ptr(out), _ptr(kc), _ptr(vc))
+    _check(rc, "prefill_chunked_paged")
+    return out, kc, vc

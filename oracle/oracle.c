@@ -112,7 +112,30 @@ typedef struct {
     int32_t B, H, D, cap;
     double scale;
     int32_t HK;                       /* K/V heads; H is a multiple of HK */
+    /* paged cache (NULL: the [B, HK, cap, D] slab): block table [B, bt_stride]
+     * of physical block indices, blocks [num_blocks, HK, PAGE, D] */
+    const int32_t *bt;
+    int32_t bt_stride, num_blocks;
 } problem_t;
+
+/*
+ * Paged KV cache [P2 §4.2 and P5 §3.4: the cache is cut into fixed blocks of
+ * 16 tokens that need not be contiguous, and a block table maps each logical
+ * block of a request to a physical one; P4 §4.1 gives a block as a small
+ * tokens x heads x head_dim array].  Reading taken here: physical block n
+ * holds [HK, 16, D] (head-major inside the block, like the slab), and cache
+ * position j of sequence b lives in block bt[b][j / 16], row j % 16.
+ */
+enum { PAGE = 16 };
+
+/* element offset of cache position j of sequence b, K/V head g */
+static int64_t cache_off(const problem_t *P, int64_t b, int64_t g, int64_t j)
+{
+    const int64_t HK = P->HK, D = P->D;
+    if (!P->bt) return ((b * HK + g) * P->cap + j) * D;
+    const int64_t blk = P->bt[b * P->bt_stride + j / PAGE];
+    return ((blk * HK + g) * PAGE + j % PAGE) * D;
+}
 
 /* K/V head read by query head h */
 static int64_t kv_head(const problem_t *P, int64_t h) { return h / (P->H / P->HK); }
@@ -124,7 +147,7 @@ static void gather_keys(const problem_t *P, int b, int h, int64_t n_keys,
     const int64_t pre = P->prefix ? P->prefix[b] : 0;
     for (int64_t j = 0; j < n_keys; ++j) {
         if (j < pre) {
-            int64_t off = (((int64_t)b * HK + g) * P->cap + j) * D;
+            int64_t off = cache_off(P, b, g, j);
             kp[j] = P->kc_in + off;
             vp[j] = P->vc_in + off;
         } else {
@@ -210,7 +233,7 @@ static void write_cache(const problem_t *P, uint16_t *kc, uint16_t *vc)
                 const int64_t src = (((int64_t)P->cu[b] + t) * HK + h) * D;
                 int64_t dst;
                 if (P->prefix)
-                    dst = (((int64_t)b * HK + h) * P->cap + P->prefix[b] + t) * D;
+                    dst = cache_off(P, b, h, P->prefix[b] + t);
                 else
                     dst = (int64_t)P->cu[b] * HK * D + (h * n + t) * D;
                 memcpy(kc + dst, P->k + src, sizeof(uint16_t) * (size_t)D);
@@ -229,6 +252,13 @@ static int check_meta(const problem_t *P)
         if (P->prefix) {
             if (P->prefix[b] < 0) return -4;
             if ((int64_t)P->prefix[b] + (P->cu[b + 1] - P->cu[b]) > P->cap) return -4;
+        }
+        if (P->bt) {  /* every block the sequence touches must exist */
+            const int64_t used = ((int64_t)P->prefix[b] + (P->cu[b + 1] - P->cu[b]) + PAGE - 1) / PAGE;
+            for (int64_t i = 0; i < used; ++i) {
+                const int32_t blk = P->bt[(int64_t)b * P->bt_stride + i];
+                if (blk < 0 || blk >= P->num_blocks) return -7;
+            }
         }
     }
     return 0;
@@ -401,6 +431,34 @@ int oracle_quantize_rows_int8(const uint16_t *x, int64_t rows, int32_t d,
             cr[i] = (int8_t)t;
         }
     }
+    return 0;
+}
+
+/*
+ * Chunked prefill over a paged cache: as oracle_prefill_chunked, with the
+ * prefix read from and the new tokens' K/V written to the blocks the block
+ * table names (layout above).  k_cache / v_cache are [num_blocks, HK, 16, D];
+ * block_table is [num_seqs, max_blocks_per_seq].  Blocks may be shared
+ * between sequences (prefix sharing); new tokens must not land in a shared
+ * block, as in any paged cache.
+ */
+int oracle_prefill_chunked_paged(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const int32_t *cu_seqlens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_blocks, const int32_t *block_table,
+                                 int32_t max_blocks_per_seq, const int32_t *prefix_lens,
+                                 float scale, double *out,
+                                 uint16_t *k_cache, uint16_t *v_cache)
+{
+    if (!block_table || !prefix_lens || max_blocks_per_seq < 1 || num_blocks < 1) return -2;
+    problem_t P = {q, k, v, cu_seqlens, prefix_lens, k_cache, v_cache,
+                   num_seqs, num_heads, head_dim, max_blocks_per_seq * PAGE, (double)scale,
+                   num_kv_heads, block_table, max_blocks_per_seq, num_blocks};
+    int rc = check_meta(&P);
+    if (rc) return rc;
+    /* the prefix is read before any new token is written (positions differ) */
+    if (run_all(&P, out, NULL)) return -1;
+    write_cache(&P, k_cache, v_cache);
     return 0;
 }
 

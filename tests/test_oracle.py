@@ -536,3 +536,105 @@ def test_int8_cache_image_layout_bruteforce():
                 cv, sv = oracle.quantize_rows_int8(v[cu[b] + t, hk].view(1, D))
                 assert np.array_equal(kq[row * D:(row + 1) * D], ck[0]) and ks[row] == sk[0]
                 assert np.array_equal(vq[row * D:(row + 1) * D], cv[0]) and vs[row] == sv[0]
+
+
+# ---------------------------------------------------------------- paged cache
+# Paged KV cache ("大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.2,
+# untitled page www.zwxr.cn/news/300951 §3.4: 16-token blocks, not contiguous,
+# located through a block table; requests with a common prefix may share
+# blocks).  Reading: blocks [num_blocks, HK, 16, D], position j of sequence b in
+# block table[b][j // 16], row j % 16.
+
+def _paged_from_slab(slab, bt, num_blocks):
+    """Scatter a [B, HK, cap, D] slab into [num_blocks, HK, 16, D] pages."""
+    B, HK, cap, D = slab.shape
+    pages = torch.zeros((num_blocks, HK, 16, D), dtype=slab.dtype)
+    for b in range(B):
+        for i in range(cap // 16):
+            pages[bt[b][i]] = slab[b, :, 16 * i:16 * (i + 1)]
+    return pages
+
+
+def _slab_from_paged(pages, bt, cap):
+    B = len(bt)
+    HK, D = pages.shape[1], pages.shape[3]
+    slab = np.zeros((B, HK, cap, D), np.uint16)
+    for b in range(B):
+        for i in range(cap // 16):
+            slab[b, :, 16 * i:16 * (i + 1)] = pages[bt[b][i]]
+    return slab
+
+
+def _chunked_case(seed, lengths, prefix, cap, H, HK, D):
+    g = torch.Generator().manual_seed(seed)
+    N = sum(lengths)
+    q = torch.randn(N, H, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(len(lengths), HK, cap, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(len(lengths), HK, cap, D, generator=g).to(torch.bfloat16)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    return q, k, v, cu, kc, vc
+
+
+@pytest.mark.parametrize("H,HK", [(4, 4), (4, 2)])
+def test_paged_equals_slab_under_block_permutation(H, HK):
+    """Any placement of the blocks gives the slab layout's outputs exactly, and
+    the written pages, read back through the table, are the slab image."""
+    lengths, prefix, cap, D = [5, 1, 40, 17], [33, 80, 0, 16], 96, 32
+    q, k, v, cu, kc, vc = _chunked_case(90 + H + HK, lengths, prefix, cap, H, HK, D)
+    B, nbps = len(lengths), cap // 16
+    perm = np.random.default_rng(91).permutation(B * nbps + 7)[:B * nbps]
+    bt = perm.reshape(B, nbps).astype(np.int32)
+    nblocks = B * nbps + 7
+    kp = _paged_from_slab(kc, bt, nblocks)
+    vp = _paged_from_slab(vc, bt, nblocks)
+    ref, kimg, vimg, _ = oracle.prefill_chunked(q, k, v, cu, prefix, kc, vc, 0.2)
+    out, kpi, vpi = oracle.prefill_chunked_paged(q, k, v, cu, prefix, kp, vp, bt, 0.2)
+    assert np.array_equal(out, ref)
+    assert np.array_equal(_slab_from_paged(kpi, bt, cap), kimg.reshape(B, HK, cap, D))
+    assert np.array_equal(_slab_from_paged(vpi, bt, cap), vimg.reshape(B, HK, cap, D))
+    # blocks no sequence maps are untouched
+    unused = sorted(set(range(nblocks)) - set(bt.reshape(-1).tolist()))
+    assert np.array_equal(kpi[unused], kp[unused].view(torch.int16).numpy().view(np.uint16))
+
+
+def test_paged_shared_prefix_blocks():
+    """Two requests with the same 32-token prefix share its two physical
+    blocks; each gets what it would get with a private copy."""
+    H, D = 2, 32
+    g = torch.Generator().manual_seed(92)
+    pk = torch.randn(32, H, D, generator=g).to(torch.bfloat16)
+    pv = torch.randn(32, H, D, generator=g).to(torch.bfloat16)
+    lengths, prefix = [3, 1], [32, 32]
+    q = torch.randn(4, H, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(4, H, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(4, H, D, generator=g).to(torch.bfloat16)
+    cu = [0, 3, 4]
+    slab_k = torch.zeros(2, H, 48, D, dtype=torch.bfloat16)
+    slab_v = torch.zeros_like(slab_k)
+    slab_k[:, :, :32] = pk.transpose(0, 1)
+    slab_v[:, :, :32] = pv.transpose(0, 1)
+    ref, _, _, _ = oracle.prefill_chunked(q, k, v, cu, prefix, slab_k, slab_v, 0.3)
+    bt = np.array([[0, 1, 2], [0, 1, 3]], np.int32)  # blocks 0, 1 shared
+    kp = torch.zeros(4, H, 16, D, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    for i in range(2):
+        kp[i] = pk[16 * i:16 * (i + 1)].transpose(0, 1)
+        vp[i] = pv[16 * i:16 * (i + 1)].transpose(0, 1)
+    out, kpi, _ = oracle.prefill_chunked_paged(q, k, v, cu, prefix, kp, vp, bt, 0.3)
+    assert np.array_equal(out, ref)
+    kb = k.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(kpi[2][:, :3], kb[0:3].transpose(1, 0, 2))  # request 0's new tokens
+    assert np.array_equal(kpi[3][:, :1], kb[3:4].transpose(1, 0, 2))  # request 1's new token
+
+
+def test_paged_rejects_bad_block_ids():
+    q, k, v, cu, kc, vc = _chunked_case(93, [2], [20], 32, 2, 2, 32)
+    kp = _paged_from_slab(kc, np.array([[0, 1]]), 2)
+    with pytest.raises(Exception):
+        oracle.prefill_chunked_paged(q, k, v, cu, [20], kp, kp, np.array([[0, 2]], np.int32), 0.1)
+    with pytest.raises(Exception):
+        oracle.prefill_chunked_paged(q, k, v, cu, [20], kp, kp, np.array([[-1, 0]], np.int32), 0.1)
