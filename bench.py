@@ -185,6 +185,33 @@ def bench_chunked(args, wl, P):
 
     mss, launchess = timed(step_split, args.steps, args.warmup)
     msds, launchesds = timed(decode_split, args.steps, args.warmup)
+
+    # and over a paged cache: the same contents in 16-token blocks placed by
+    # a seeded random permutation of the pool, located through a block table
+    B = 1 + R
+    mb = wl.cap // 16
+    perm = torch.randperm(B * mb, generator=torch.Generator().manual_seed(7)).to(dev)
+    bt = perm.view(B, mb).to(torch.int32).contiguous()
+
+    def to_pages(slab):
+        pages = torch.empty((B * mb, H, 16, D), dtype=slab.dtype, device=dev)
+        pages[perm] = slab.view(B, H, mb, 16, D).permute(0, 2, 1, 3, 4).reshape(B * mb, H, 16, D)
+        return pages
+
+    kp, vp = to_pages(kc), to_pages(vc)
+    btd = bt[1:].contiguous()
+
+    def step_paged():
+        P.prefill_attn_chunked_splitkv_paged(q, k, v, cu, kp, vp, bt, out, pre, scale=st.scale,
+                                             max_seqlen=wl.chunk_len, workspace=ws)
+
+    def decode_paged():
+        P.prefill_attn_chunked_splitkv_paged(qd, kd, vd, cud, kp, vp, btd, outd, pred, scale=st.scale,
+                                             max_seqlen=1, workspace=wsd)
+
+    msp, launchesp = timed(step_paged, args.steps, args.warmup)
+    msdp, launchesdp = timed(decode_paged, args.steps, args.warmup)
+    del kp, vp
     value = flops / (ms * 1e-3) / 1e12
     return {
         "metric": METRIC,
@@ -216,6 +243,12 @@ def bench_chunked(args, wl, P):
                     "decode_only_us_mean": round(sum(launchesds) / len(launchesds) * 1e3, 2),
                     "decode_kv_read_gbps": round(dec_bytes / (msds * 1e-3) / 1e9, 1),
                     "decode_frac_of_hbm_8tbs": round(dec_bytes / (msds * 1e-3) / 8e12, 4)},
+        "splitkv_paged": {"ms_per_step": round(msp, 5),
+                          "tflops": round(flops / (msp * 1e-3) / 1e12, 2),
+                          "launch_us_mean": round(sum(launchesp) / len(launchesp) * 1e3, 2),
+                          "decode_only_us_mean": round(sum(launchesdp) / len(launchesdp) * 1e3, 2),
+                          "decode_kv_read_gbps": round(dec_bytes / (msdp * 1e-3) / 1e9, 1),
+                          "block_tokens": 16, "blocks": B * mb},
         "roofline": None,
         "cpu_baseline": None,
     }

@@ -65,7 +65,7 @@ typedef enum {
     PA_ERR_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
     PA_ERR_ALIAS = 6,     /* an output pointer equals an input or another output pointer */
     PA_ERR_SEQLENS = 7,   /* check mode: cu_seqlens[0] != 0, decreasing, or a length > max_seqlen */
-    PA_ERR_CAPACITY = 8,  /* check mode: a prefix length < 0 or prefix + length > cache_capacity */
+    PA_ERR_CAPACITY = 8,  /* check mode: a prefix length < 0, prefix + length > cache_capacity, or a block id outside the pool */
     PA_ERR_HIP = 9,       /* a HIP runtime call failed; see pa_last_hip_error() */
     PA_ERR_WORKSPACE = 10 /* split-KV: workspace_bytes below prefill_attn_splitkv_workspace_size() */
 } pa_status;
@@ -219,6 +219,44 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t *q, const uint16_t *k, con
                                        int32_t cache_capacity, uint16_t *out, float scale,
                                        hipStream_t stream, const int32_t *prefix_lens,
                                        void *workspace, size_t workspace_bytes);
+
+/*
+ * Split-KV chunked prefill over a paged KV cache [P2 §4.2 and P5 §3.4: the
+ * cache is cut into fixed 16-token blocks that need not be contiguous, a
+ * block table maps each request's logical blocks to physical ones, and
+ * requests with a common prefix can point at the same blocks; P4 §4.1 shows
+ * a block as a small tokens x heads x head_dim array].  Same computation as
+ * prefill_attn_chunked_splitkv; only where cache positions live differs.
+ *
+ *   k_cache, v_cache     bf16 [num_blocks, HK, 16, D] device: block n holds 16
+ *                        consecutive positions of one request, head-major.
+ *   block_table          int32 [num_seqs, max_blocks_per_seq] device: position
+ *                        j of sequence b is row j % 16 of block
+ *                        block_table[b][j / 16].  Every block a sequence
+ *                        touches (positions below prefix_lens[b] + len_b)
+ *                        must be in [0, num_blocks); the blocks receiving new
+ *                        tokens must not be shared with another sequence of
+ *                        the call.  Entries past those are not read.
+ *   num_blocks           blocks in the pool (>= 1).
+ *   max_blocks_per_seq   columns of block_table (>= 1); the capacity per
+ *                        sequence is 16 * max_blocks_per_seq positions.
+ *   workspace            prefill_attn_splitkv_workspace_size(num_seqs,
+ *                        num_tokens, num_heads, head_dim,
+ *                        16 * max_blocks_per_seq) bytes at least.
+ *   other arguments      as prefill_attn_chunked_splitkv.
+ *
+ * Errors as prefill_attn_chunked_splitkv, plus PA_ERR_NULL for a NULL block
+ * table, PA_ERR_SHAPE for num_blocks or max_blocks_per_seq < 1, PA_ERR_ALIAS
+ * if block_table equals an output or the workspace; check mode also returns
+ * PA_ERR_CAPACITY for a block id outside the pool.
+ */
+pa_status prefill_attn_chunked_splitkv_paged(
+    const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *cu_seqlens,
+    int32_t num_seqs, int32_t max_seqlen, int32_t num_tokens, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, uint16_t *k_cache, uint16_t *v_cache,
+    int32_t num_blocks, const int32_t *block_table, int32_t max_blocks_per_seq, uint16_t *out,
+    float scale, hipStream_t stream, const int32_t *prefix_lens, void *workspace,
+    size_t workspace_bytes);
 
 /*
  * Workspace bytes prefill_attn_chunked_splitkv needs for these sizes (host

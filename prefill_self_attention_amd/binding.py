@@ -48,6 +48,10 @@ def load() -> ctypes.CDLL:
     lib.prefill_attn_chunked_splitkv.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p, p,
                                                  i32, p, ctypes.c_float, p, p, p, ctypes.c_size_t]
     lib.prefill_attn_chunked_splitkv.restype = ctypes.c_int
+    lib.prefill_attn_chunked_splitkv_paged.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                                       p, p, i32, p, i32, p, ctypes.c_float, p,
+                                                       p, p, ctypes.c_size_t]
+    lib.prefill_attn_chunked_splitkv_paged.restype = ctypes.c_int
     lib.prefill_attn_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.prefill_attn_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -257,6 +261,49 @@ def prefill_attn_varlen_int8(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_s
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
         ctypes.c_float(scale), _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out
+
+
+def prefill_attn_chunked_splitkv_paged(q, k, v, cu_seqlens, k_cache, v_cache, block_table, out,
+                                       prefix_lens, scale=None, max_seqlen=None, stream=None,
+                                       workspace=None):
+    """Split-KV chunked prefill over a paged cache (see prefill_attn.h).
+
+    k_cache, v_cache: bf16 [num_blocks, HK, 16, D] device; block_table: int32
+    [B, max_blocks_per_seq] device.  Other arguments as
+    prefill_attn_chunked_splitkv.  Returns out.
+    """
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    for n, t in (("cu_seqlens", cu_seqlens), ("prefix_lens", prefix_lens),
+                 ("block_table", block_table)):
+        _check_tensor(n, t, torch.int32)
+    H, HK, D = _heads(q, k, v)
+    N = q.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    if k_cache.dim() != 4 or k_cache.shape[1] != HK or k_cache.shape[2] != 16 or \
+            k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [num_blocks, HK, 16, D]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    nb, mb = k_cache.shape[0], block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    need = splitkv_workspace_size(B, N, H, D, 16 * mb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_tensor("workspace", workspace, torch.uint8)
+    st = load().prefill_attn_chunked_splitkv_paged(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), N, H, HK, D,
+        _ptr(k_cache), _ptr(v_cache), int(nb), _ptr(block_table), int(mb), _ptr(out),
+        ctypes.c_float(scale), _stream(stream), _ptr(prefix_lens), _ptr(workspace),
+        workspace.numel())
     if st != PA_OK:
         raise PrefillAttnError(st)
     return out

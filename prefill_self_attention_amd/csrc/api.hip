@@ -93,6 +93,30 @@ pa_status check_metadata(const int32_t* cu, int32_t num_seqs, int32_t max_seqlen
   return PA_OK;
 }
 
+// Check mode, paged cache: every block a sequence touches (positions below
+// prefix + length) names a block of the pool.
+pa_status check_block_table(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
+                            const int32_t* bt, int32_t max_blocks, int32_t num_blocks,
+                            hipStream_t stream) {
+  std::vector<int32_t> hcu(num_seqs + 1), hpre(num_seqs), hbt((size_t)num_seqs * max_blocks);
+  hipError_t e = hipMemcpyAsync(hcu.data(), cu, sizeof(int32_t) * (num_seqs + 1),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(hpre.data(), prefix, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(hbt.data(), bt, sizeof(int32_t) * hbt.size(), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t used = ((int64_t)hpre[b] + hcu[b + 1] - hcu[b] + pa::kPageRows - 1) / pa::kPageRows;
+    for (int64_t i = 0; i < used; ++i) {
+      const int32_t blk = hbt[(size_t)b * max_blocks + i];
+      if (blk < 0 || blk >= num_blocks) return PA_ERR_CAPACITY;
+    }
+  }
+  return PA_OK;
+}
+
 struct Int8Cache {
   int8_t* kq;
   int8_t* vq;
@@ -153,9 +177,9 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_split_occ[kMaxDevices][3];
-std::atomic<int> g_dec_occ[kMaxDevices][3][4];
+std::atomic<int> g_dec_occ[kMaxDevices][3][4][2];
 
-pa_status split_grid(int head_dim, int heads_per_unit, int* fwd_grid, int* dec_grid,
+pa_status split_grid(int head_dim, int heads_per_unit, bool paged, int* fwd_grid, int* dec_grid,
                      int* merge_grid) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -175,11 +199,11 @@ pa_status split_grid(int head_dim, int heads_per_unit, int* fwd_grid, int* dec_g
     g_split_occ[dev][di].store(occ, std::memory_order_relaxed);
   }
   const int gi = heads_per_unit == 1 ? 0 : heads_per_unit == 2 ? 1 : heads_per_unit == 4 ? 2 : 3;
-  int docc = g_dec_occ[dev][di][gi].load(std::memory_order_relaxed);
+  int docc = g_dec_occ[dev][di][gi][paged].load(std::memory_order_relaxed);
   if (docc <= 0) {
-    docc = pa::splitkv_decode_blocks_per_cu(head_dim, heads_per_unit);
+    docc = pa::splitkv_decode_blocks_per_cu(head_dim, heads_per_unit, paged);
     if (docc <= 0) return hip_fail(hipErrorInvalidConfiguration);
-    g_dec_occ[dev][di][gi].store(docc, std::memory_order_relaxed);
+    g_dec_occ[dev][di][gi][paged].store(docc, std::memory_order_relaxed);
   }
   *fwd_grid = cus * occ;
   *dec_grid = cus * docc;
@@ -199,14 +223,20 @@ size_t prefill_attn_splitkv_workspace_size(int32_t num_seqs, int32_t num_tokens,
   return pa::split_layout(num_seqs, num_tokens, num_heads, head_dim, cache_capacity).bytes;
 }
 
-pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                       const int32_t* cu_seqlens, int32_t num_seqs,
-                                       int32_t max_seqlen, int32_t num_tokens, int32_t num_heads,
-                                       int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
-                                       uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
-                                       float scale, hipStream_t stream,
-                                       const int32_t* prefix_lens, void* workspace,
-                                       size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Split-KV chunked call; block_table non-NULL selects the paged cache
+// ([num_blocks, HK, 16, D], cache_capacity = 16 * max_blocks_per_seq).
+pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                      int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, uint16_t* k_cache, uint16_t* v_cache,
+                      int32_t cache_capacity, uint16_t* out, float scale, hipStream_t stream,
+                      const int32_t* prefix_lens, void* workspace, size_t workspace_bytes,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      int32_t num_blocks) {
   pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
                               k_cache, v_cache, out, scale);
   if (st != PA_OK) return st;
@@ -232,6 +262,11 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
   if (check_mode()) {
     st = check_metadata(cu_seqlens, num_seqs, max_seqlen, prefix_lens, cache_capacity, stream);
     if (st != PA_OK) return st;
+    if (block_table) {
+      st = check_block_table(cu_seqlens, prefix_lens, num_seqs, block_table, max_blocks_per_seq,
+                             num_blocks, stream);
+      if (st != PA_OK) return st;
+    }
     int32_t last = 0;
     hipError_t e = hipMemcpyAsync(&last, cu_seqlens + num_seqs, sizeof(int32_t),
                                   hipMemcpyDeviceToHost, stream);
@@ -240,8 +275,9 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
     if (last > num_tokens) return PA_ERR_SEQLENS;
   }
   const int gc = pa::splitkv_heads_per_unit(num_heads, num_kv_heads);
+  const bool paged = block_table != nullptr;
   int fwd_grid = 0, dec_grid = 0, merge_grid = 0;
-  st = split_grid(head_dim, gc, &fwd_grid, &dec_grid, &merge_grid);
+  st = split_grid(head_dim, gc, paged, &fwd_grid, &dec_grid, &merge_grid);
   if (st != PA_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
@@ -269,12 +305,50 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
   p.split_grid = fwd_grid;
   p.dec_items = reinterpret_cast<const int4*>(ws + L.off_dec);
   p.dec_grid = dec_grid;
+  p.block_table = block_table;
+  p.bt_stride = max_blocks_per_seq;
   hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, ws, stream);
-  if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, stream);
-  if (e == hipSuccess) e = pa::launch_splitkv_decode(p, head_dim, gc, stream);
+  if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, paged, stream);
+  if (e == hipSuccess) e = pa::launch_splitkv_decode(p, head_dim, gc, paged, stream);
   if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const int32_t* cu_seqlens, int32_t num_seqs,
+                                       int32_t max_seqlen, int32_t num_tokens, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
+                                       uint16_t* v_cache, int32_t cache_capacity, uint16_t* out,
+                                       float scale, hipStream_t stream,
+                                       const int32_t* prefix_lens, void* workspace,
+                                       size_t workspace_bytes) {
+  return splitkv_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_tokens, num_heads,
+                     num_kv_heads, head_dim, k_cache, v_cache, cache_capacity, out, scale, stream,
+                     prefix_lens, workspace, workspace_bytes, nullptr, 0, 0);
+}
+
+pa_status prefill_attn_chunked_splitkv_paged(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
+    int32_t num_seqs, int32_t max_seqlen, int32_t num_tokens, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache, uint16_t* v_cache,
+    int32_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq, uint16_t* out,
+    float scale, hipStream_t stream, const int32_t* prefix_lens, void* workspace,
+    size_t workspace_bytes) {
+  if (!block_table) return PA_ERR_NULL;
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_blocks_per_seq > (1 << 26)) return PA_ERR_SHAPE;
+  if ((const void*)block_table == (const void*)k_cache ||
+      (const void*)block_table == (const void*)v_cache || (const void*)block_table == (const void*)out ||
+      (const void*)block_table == workspace)
+    return PA_ERR_ALIAS;
+  return splitkv_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_tokens, num_heads,
+                     num_kv_heads, head_dim, k_cache, v_cache, max_blocks_per_seq * pa::kPageRows,
+                     out, scale, stream, prefix_lens, workspace, workspace_bytes, block_table,
+                     max_blocks_per_seq, num_blocks);
 }
 
 pa_status prefill_attn_varlen_gqa(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -40,7 +40,14 @@ struct FwdParams {
   int8_t* vq;
   float* ks;
   float* vs;
+  // paged cache (split-KV chunked only): kc/vc are [num_blocks, HK, 16, D];
+  // cache position j of sequence b is row j % 16 of block
+  // block_table[b * bt_stride + j / 16]
+  const int32_t* block_table;
+  int32_t bt_stride;
 };
+
+constexpr int kPageRows = 16;  // tokens per cache block
 
 // Query rows per block, and work-groups per (head, sequence) for a maximum length.
 int fwd_block_rows();
@@ -73,17 +80,17 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
                                int32_t num_tokens, const SplitLayout& L, void* ws,
                                hipStream_t stream);
-hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
                                 int head_dim, int grid, hipStream_t stream);
 // Length-1 rows of the split-KV call: a memory-bound pass over their
 // segments; `heads_per_unit` query heads (1, 2, 4 or 8, dividing
 // num_heads / num_kv_heads) share each load of a K/V row.
-hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit,
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit, bool paged,
                                  hipStream_t stream);
-int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit);
+int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit, bool paged);
 int splitkv_heads_per_unit(int num_heads, int num_kv_heads);
 // Resident work-groups per compute unit of the split attention kernel (0 on error).
-int fwd_split_blocks_per_cu(int head_dim);
+int fwd_split_blocks_per_cu(int head_dim);  // same for the paged variant
 
 }  // namespace pa

@@ -297,7 +297,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // one of the nseg segments of its keys.  A block with one segment is stored
 // as usual; otherwise its rows get a partial result (normalised O in fp32 and
 // log2 of its sum of weights), merged by a later pass.
-template <int D, bool kChunked, bool kSplit, bool kInt8 = false>
+template <int D, bool kChunked, bool kSplit, bool kInt8 = false, bool kPaged = false>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z, int seg, int nseg) {
   using C = Cfg<D>;
   // Every LDS read in the main loop is inline asm (lds_read_* above), so the
@@ -342,6 +342,17 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
                                       : (int64_t)seq_start * HK * D + (int64_t)hk * len * D;
   const float c = p.scale_log2;          // |scale| * log2(e), > 0
   const uint32_t lds0 = lds_addr(lds);
+  // Paged cache ["大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.2:
+  // 16-token blocks located through a block table]: position kp of this
+  // (sequence, K/V head) is row kp % 16 of block bt_row[kp / 16], blocks
+  // [num_blocks, HK, 16, D].
+  const int32_t* __restrict__ bt_row = kPaged ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
+  auto cache_elem = [&](int kp) __attribute__((always_inline)) -> int64_t {
+    if constexpr (kPaged)
+      return (((int64_t)bt_row[kp / kPageRows] * HK + hk) * kPageRows + kp % kPageRows) * D;
+    else
+      return cache_base + (int64_t)kp * D;
+  };
 
   // ---------------------------------------------------------------- staging
   // Wave gw of a group issues instructions j = 4 i + gw (i < kInstPerWave) per
@@ -353,7 +364,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   const int lslot = lane % C::kCpr;
 
   auto row_ptr = [&](const uint16_t* __restrict__ in, const uint16_t* cache, int kp) __attribute__((always_inline)) {
-    if (kChunked && kp < pre) return cache + cache_base + (int64_t)kp * D;
+    if (kChunked && kp < pre) return cache + cache_elem(kp);
     return in + (int64_t)(seq_start + kp - pre) * row_stride;
   };
 
@@ -364,7 +375,20 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
     const bool full = t0 + kBN <= blk.key_end;
     const bool all_new = !kChunked || t0 >= pre;
     const bool all_cached = kChunked && t0 + kBN <= pre;
-    if (full && (all_new || all_cached)) {
+    if (kPaged && full && all_cached) {
+      // the rows of one load instruction (4, 8 or 16) lie in one block
+#pragma unroll
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int r0 = t0 + j * C::kRowsPerInst;
+        const int bi = __builtin_amdgcn_readfirstlane(r0 / kPageRows);
+        const int64_t base = (((int64_t)bt_row[bi] * HK + hk) * kPageRows + r0 % kPageRows) * D;
+        const int row = j * C::kRowsPerInst + lrow;
+        const uint32_t off = (uint32_t)(lrow * D + 8 * chunk_slot<D>(row, lslot));
+        __builtin_amdgcn_global_load_lds((const void*)(p.kc + base + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(p.vc + base + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
+      }
+    } else if (full && (all_new || all_cached)) {
       const int64_t step = all_new ? row_stride : (int64_t)D;
       const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
                                    : p.kc + cache_base + (int64_t)t0 * D;
@@ -428,7 +452,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
           }
         }
       } else if (mine) {
-        const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
+        const int64_t dst = cache_elem(kp) + 8 * ch;
         *(u32x4_t*)(p.kc + dst) = kr[i];
         *(u32x4_t*)(p.vc + dst) = vr[i];
       }
@@ -768,7 +792,7 @@ void prefill_fwd_kernel(FwdParams p) {
 // Split-KV chunked prefill: a persistent grid walks the planned items, item i
 // of head h being step i * H + h; with the grid a multiple of H (and of the 8
 // XCDs) a work-group keeps one head, and all of a head's items run on one XCD.
-template <int D>
+template <int D, bool kPaged>
 __global__ __launch_bounds__(kThreads)
 void prefill_fwd_split_kernel(FwdParams p) {
   const int H = p.num_heads;
@@ -776,7 +800,7 @@ void prefill_fwd_split_kernel(FwdParams p) {
   const int grid = p.split_grid;
   for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += grid) {
     const int4 it = p.items[g / H];
-    fwd_item<D, true, true>(p, (int)(g % H), it.x, it.y, it.z, it.w);
+    fwd_item<D, true, true, false, kPaged>(p, (int)(g % H), it.x, it.y, it.z, it.w);
     __syncthreads();  // the next item's first loads reuse the merge buffers
   }
 }
@@ -802,12 +826,19 @@ hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_di
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.split_grid);
+template <int D>
+void split_d(const FwdParams& p, bool paged, hipStream_t stream) {
+  if (paged)
+    hipLaunchKernelGGL((prefill_fwd_split_kernel<D, true>), dim3(p.split_grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_fwd_split_kernel<D, false>), dim3(p.split_grid), dim3(kThreads), 0, stream, p);
+}
+
+hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream) {
   switch (head_dim) {
-    case 32: hipLaunchKernelGGL(prefill_fwd_split_kernel<32>, grid, dim3(kThreads), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(prefill_fwd_split_kernel<64>, grid, dim3(kThreads), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(prefill_fwd_split_kernel<128>, grid, dim3(kThreads), 0, stream, p); break;
+    case 32: split_d<32>(p, paged, stream); break;
+    case 64: split_d<64>(p, paged, stream); break;
+    case 128: split_d<128>(p, paged, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -817,9 +848,9 @@ int fwd_split_blocks_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (head_dim) {
-    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<32>, kThreads, 0); break;
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<64>, kThreads, 0); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<128>, kThreads, 0); break;
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<32, false>, kThreads, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<64, false>, kThreads, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<128, false>, kThreads, 0); break;
     default: break;
   }
   return e == hipSuccess ? n : 0;

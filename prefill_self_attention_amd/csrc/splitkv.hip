@@ -252,7 +252,7 @@ constexpr int kDecUnroll = 4;        // key steps whose loads are issued togethe
 constexpr float kDecRescale = 8.0f;  // lazy rescale headroom, log2 units
 constexpr float kDecMInit = -1.0e30f;
 
-template <int D, int GC>
+template <int D, int GC, bool kPaged>
 __global__ __launch_bounds__(kDecThreads)
 void splitkv_decode_kernel(FwdParams p) {
   constexpr int LPK = D / 8, KPI = 64 / LPK;
@@ -286,6 +286,9 @@ void splitkv_decode_kernel(FwdParams p) {
     const uint16_t* kn = p.k + ((int64_t)tok * HK + hk) * D + 8 * dch;  // the row's own key
     const uint16_t* vn = p.v + ((int64_t)tok * HK + hk) * D + 8 * dch;
     const int wc = min(w1, pre);  // the wave's cached keys are [w0, wc); key pre comes from k, v
+    // paged cache: block bt_row[j / 16] of [num_blocks, HK, 16, D] holds position j
+    const int32_t* __restrict__ bt_row = kPaged ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
+    const int last_sb = wc > w0 ? (wc - 1) / KPI * KPI : w0;  // last step's first key
     float qf[GC][8], o[GC][8], m[GC], l[GC];
 #pragma unroll
     for (int gi = 0; gi < GC; ++gi) {
@@ -308,9 +311,20 @@ void splitkv_decode_kernel(FwdParams p) {
     auto load = [&](int kb, uint4 (&kr)[kDecUnroll], uint4 (&vr)[kDecUnroll]) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
-        const uint32_t off = (uint32_t)min(kb + u * KPI + kslot, wc - 1) * D + 8 * dch;
-        kr[u] = *(const uint4*)(kc + off);
-        vr[u] = *(const uint4*)(vc + off);
+        if constexpr (kPaged) {
+          // a step's KPI keys (KPI divides 16, steps start at multiples of
+          // KPI) lie in one block: one scalar block id per step
+          const int sb = min(kb + u * KPI, last_sb);
+          const int kq = min(sb + kslot, wc - 1);
+          const int64_t base = (((int64_t)bt_row[sb / kPageRows] * HK + hk) * kPageRows) * D;
+          const uint32_t off = (uint32_t)(kq % kPageRows) * D + 8 * dch;
+          kr[u] = *(const uint4*)(p.kc + base + off);
+          vr[u] = *(const uint4*)(p.vc + base + off);
+        } else {
+          const uint32_t off = (uint32_t)min(kb + u * KPI + kslot, wc - 1) * D + 8 * dch;
+          kr[u] = *(const uint4*)(kc + off);
+          vr[u] = *(const uint4*)(vc + off);
+        }
       }
     };
     auto consume_one = [&](bool ok, const uint4 kr, const uint4 vr) __attribute__((always_inline)) {
@@ -428,8 +442,10 @@ void splitkv_decode_kernel(FwdParams p) {
     // the segment holding the row's own position writes its K/V to the cache,
     // once per K/V head (the unit of the group's first query heads)
     if (wave == 1 && lane < LPK && s == ns - 1 && h0 == hk * G) {
-      *(uint4*)(p.kc + (crow + pre) * D + 8 * dch) = *(const uint4*)kn;
-      *(uint4*)(p.vc + (crow + pre) * D + 8 * dch) = *(const uint4*)vn;
+      const int64_t row = kPaged ? ((int64_t)bt_row[pre / kPageRows] * HK + hk) * kPageRows + pre % kPageRows
+                                 : crow + pre;
+      *(uint4*)(p.kc + row * D + 8 * dch) = *(const uint4*)kn;
+      *(uint4*)(p.vc + row * D + 8 * dch) = *(const uint4*)vn;
     }
     __syncthreads();  // red is rewritten by the next unit
   }
@@ -498,48 +514,48 @@ int splitkv_heads_per_unit(int num_heads, int num_kv_heads) {
 }
 
 namespace {
-template <int D>
+template <int D, bool kPaged>
 hipError_t decode_d(const FwdParams& p, int gc, hipStream_t stream) {
   const dim3 grid(p.dec_grid), block(kDecThreads);
   switch (gc) {
-    case 1: hipLaunchKernelGGL((splitkv_decode_kernel<D, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((splitkv_decode_kernel<D, 2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((splitkv_decode_kernel<D, 4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((splitkv_decode_kernel<D, 8>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((splitkv_decode_kernel<D, 1, kPaged>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((splitkv_decode_kernel<D, 2, kPaged>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((splitkv_decode_kernel<D, 4, kPaged>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((splitkv_decode_kernel<D, 8, kPaged>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-template <int D>
+template <int D, bool kPaged>
 int decode_occ(int gc) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (gc) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 1>, kDecThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 2>, kDecThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 4>, kDecThreads, 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 8>, kDecThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 1, kPaged>, kDecThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 2, kPaged>, kDecThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 4, kPaged>, kDecThreads, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, splitkv_decode_kernel<D, 8, kPaged>, kDecThreads, 0); break;
     default: break;
   }
   return e == hipSuccess ? n : 0;
 }
 }  // namespace
 
-hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit,
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit, bool paged,
                                  hipStream_t stream) {
   switch (head_dim) {
-    case 32: return decode_d<32>(p, heads_per_unit, stream);
-    case 64: return decode_d<64>(p, heads_per_unit, stream);
-    case 128: return decode_d<128>(p, heads_per_unit, stream);
+    case 32: return paged ? decode_d<32, true>(p, heads_per_unit, stream) : decode_d<32, false>(p, heads_per_unit, stream);
+    case 64: return paged ? decode_d<64, true>(p, heads_per_unit, stream) : decode_d<64, false>(p, heads_per_unit, stream);
+    case 128: return paged ? decode_d<128, true>(p, heads_per_unit, stream) : decode_d<128, false>(p, heads_per_unit, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit) {
+int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit, bool paged) {
   switch (head_dim) {
-    case 32: return decode_occ<32>(heads_per_unit);
-    case 64: return decode_occ<64>(heads_per_unit);
-    case 128: return decode_occ<128>(heads_per_unit);
+    case 32: return paged ? decode_occ<32, true>(heads_per_unit) : decode_occ<32, false>(heads_per_unit);
+    case 64: return paged ? decode_occ<64, true>(heads_per_unit) : decode_occ<64, false>(heads_per_unit);
+    case 128: return paged ? decode_occ<128, true>(heads_per_unit) : decode_occ<128, false>(heads_per_unit);
     default: return 0;
   }
 }

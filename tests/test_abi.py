@@ -33,6 +33,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "prefill_attn_varlen", "prefill_attn_chunked", "prefill_attn_varlen_gqa",
         "prefill_attn_chunked_gqa", "prefill_attn_chunked_splitkv", "prefill_attn_varlen_int8",
+        "prefill_attn_chunked_splitkv_paged",
         "prefill_attn_splitkv_workspace_size", "pa_status_string", "pa_set_check_mode",
         "pa_last_hip_error"])
 
@@ -138,6 +139,27 @@ def test_splitkv_rejections(lib):
     assert need > 0
     assert splitkv(lib, ws_bytes=need - 1) == 10
     assert P.pa_status_string(10).startswith("PA_ERR_WORKSPACE")
+
+
+def paged(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64, kc=A[4],
+          vc=A[5], nb=8, bt=A[9], mb=4, out=A[6], scale=0.125, pre=A[7], N=16, HK=None, ws=A[8],
+          ws_bytes=WS):
+    return lib.prefill_attn_chunked_splitkv_paged(q, k, v, cu, B, maxlen, N, H,
+                                                  H if HK is None else HK, D, kc, vc, nb, bt, mb,
+                                                  out, ctypes.c_float(scale), None, pre, ws,
+                                                  ws_bytes)
+
+
+def test_paged_rejections(lib):
+    assert paged(lib, bt=None) == 1
+    assert paged(lib, nb=0) == 2
+    assert paged(lib, mb=0) == 2
+    assert paged(lib, bt=A[6]) == 6     # table is out
+    assert paged(lib, bt=A[8]) == 6     # table is the workspace
+    assert paged(lib, ws=None) == 1
+    assert paged(lib, pre=None) == 1
+    assert paged(lib, q=A[0] + 2) == 5
+    assert paged(lib, B=0) == 0 and paged(lib, N=0) == 0
 
 
 def test_splitkv_workspace_size():
