@@ -229,3 +229,17 @@ def test_splitkv_check_mode_rejects_tokens_beyond_num_tokens():
     finally:
         P().pa_set_check_mode(prev)
     assert bool(torch.all(out == 0)), "v = 0 gives out = 0"
+
+
+def test_splitkv_thousands_of_rows():
+    """2,100 sequences (the plan takes 1,024 per round): decode rows with
+    contexts 0..1,090 (one or two segments), empty sequences and one chunk."""
+    rng = np.random.default_rng(970)
+    B = 2100
+    lengths = [1] * B
+    prefix = rng.integers(0, 1091, B).tolist()
+    for b in (5, 1500, 2099):
+        lengths[b] = 0
+    lengths[1024] = 60          # a chunk in the second round
+    prefix[1024] = 1000
+    check_case(lengths, prefix, 1100, 2, 1, 32, 971, "splitkv 2100 rows")
