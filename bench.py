@@ -131,9 +131,9 @@ def bench_chunked(args, wl, P):
     share as GB/s of cached K/V read."""
     import torch
     dev = torch.device("cuda:0")
-    H, D, R = wl.num_heads, wl.head_dim, len(wl.contexts)
+    H, HK, D, R = wl.num_heads, wl.num_kv_heads, wl.head_dim, len(wl.contexts)
     t = wl.tensors()
-    kc = torch.zeros((1 + R, H, wl.cap, D), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((1 + R, HK, wl.cap, D), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
     for r, ctx in enumerate(wl.contexts):
         kc[1 + r, :, :ctx] = t["pre_k"][r].to(dev)
@@ -168,7 +168,7 @@ def bench_chunked(args, wl, P):
         P.prefill_attn_chunked(qd, kd, vd, cud, kcd, vcd, outd, pred, scale=st.scale, max_seqlen=1)
 
     msd, launchesd = timed(decode, args.steps, args.warmup)
-    dec_bytes = 2.0 * sum(c_ + 1 for c_ in wl.contexts) * H * D * 2  # K and V of every context row read
+    dec_bytes = 2.0 * sum(c_ + 1 for c_ in wl.contexts) * HK * D * 2  # K and V of every context row, once per K/V head
 
     # the same step and decode rows through the split-KV path (plan, attention
     # over key segments, merge), workspaces allocated before timing
@@ -194,8 +194,8 @@ def bench_chunked(args, wl, P):
     bt = perm.view(B, mb).to(torch.int32).contiguous()
 
     def to_pages(slab):
-        pages = torch.empty((B * mb, H, 16, D), dtype=slab.dtype, device=dev)
-        pages[perm] = slab.view(B, H, mb, 16, D).permute(0, 2, 1, 3, 4).reshape(B * mb, H, 16, D)
+        pages = torch.empty((B * mb, HK, 16, D), dtype=slab.dtype, device=dev)
+        pages[perm] = slab.view(B, HK, mb, 16, D).permute(0, 2, 1, 3, 4).reshape(B * mb, HK, 16, D)
         return pages
 
     kp, vp = to_pages(kc), to_pages(vc)
@@ -228,7 +228,7 @@ def bench_chunked(args, wl, P):
         "data": "synthetic",
         "config": {"workload": args.workload,
                    "step": "chunk %d of %d (prefix %d) + %d decode rows" % (c, wl.num_chunks, c * wl.chunk_len, R),
-                   "tokens": int(q.shape[0]), "num_heads": H, "head_dim": D, "causal": True,
+                   "tokens": int(q.shape[0]), "num_heads": H, "num_kv_heads": HK, "head_dim": D, "causal": True,
                    "kv_cache_write": True, "scale": st.scale},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "launch_us": {"mean": round(sum(launches) / len(launches) * 1e3, 2),

@@ -152,7 +152,7 @@ class ChunkedStep:
     Sequence 0 is chunk ``chunk`` of a ``prompt_len`` prompt (``chunk_len``
     new tokens, prefix ``chunk * chunk_len``); sequences 1..R are decode rows
     (1 new token each, prefix = that row's cached context).  The cache is
-    [1 + R, H, cap, D].
+    [1 + R, HK, cap, D].
     """
     chunk: int
     prompt_len: int
@@ -162,10 +162,13 @@ class ChunkedStep:
     head_dim: int
     cap: int
     scale: float = 0.0
+    num_kv_heads: int = 0  # 0: as many as num_heads
 
     def __post_init__(self):
         if not self.scale:
             self.scale = default_scale(self.head_dim)
+        if not self.num_kv_heads:
+            self.num_kv_heads = self.num_heads
 
     @property
     def lengths(self) -> List[int]:
@@ -187,16 +190,18 @@ class ChunkedStep:
 class ChunkedWorkload:
     """Chunked prefill of one long prompt beside decode rows (all bf16 N(0,1)).
 
-    Value draw order from ``seed``: prompt q, k, v [prompt_len, H, D]; decode
-    rows' q, k, v [R, H, D]; then each decode row's cached prefix, K then V,
-    [H, ctx_r, D].
+    Value draw order from ``seed``: prompt q [prompt_len, H, D], k, v
+    [prompt_len, HK, D]; decode rows' q [R, H, D], k, v [R, HK, D]; then each
+    decode row's cached prefix, K then V, [HK, ctx_r, D].  HK = num_kv_heads
+    (default H).
     """
 
     def __init__(self, prompt_len=8192, chunk_len=512, rows=64, num_heads=32,
-                 head_dim=128, seed=4, ctx_lo=256, ctx_hi=4096, cap=None):
+                 head_dim=128, seed=4, ctx_lo=256, ctx_hi=4096, cap=None, num_kv_heads=None):
         self.prompt_len = prompt_len
         self.chunk_len = chunk_len
         self.num_heads = num_heads
+        self.num_kv_heads = num_kv_heads or num_heads
         self.head_dim = head_dim
         self.seed = seed
         self.contexts = decode_contexts(seed, rows, ctx_lo, ctx_hi) if rows else []
@@ -207,7 +212,7 @@ class ChunkedWorkload:
     def step(self, c: int) -> ChunkedStep:
         n = min(self.chunk_len, self.prompt_len - c * self.chunk_len)
         st = ChunkedStep(c, self.prompt_len, self.chunk_len, self.contexts,
-                         self.num_heads, self.head_dim, self.cap, self.scale)
+                         self.num_heads, self.head_dim, self.cap, self.scale, self.num_kv_heads)
         if n != self.chunk_len:
             raise ValueError("prompt length must be a multiple of the chunk length")
         return st
@@ -215,18 +220,18 @@ class ChunkedWorkload:
     def tensors(self):
         """Returns dict with prompt q/k/v, decode q/k/v and per-row prefix K/V lists."""
         g = generator(self.seed)
-        H, D = self.num_heads, self.head_dim
+        H, HK, D = self.num_heads, self.num_kv_heads, self.head_dim
         pq = randn_bf16(g, (self.prompt_len, H, D))
-        pk = randn_bf16(g, (self.prompt_len, H, D))
-        pv = randn_bf16(g, (self.prompt_len, H, D))
+        pk = randn_bf16(g, (self.prompt_len, HK, D))
+        pv = randn_bf16(g, (self.prompt_len, HK, D))
         R = len(self.contexts)
         dq = randn_bf16(g, (R, H, D))
-        dk = randn_bf16(g, (R, H, D))
-        dv = randn_bf16(g, (R, H, D))
+        dk = randn_bf16(g, (R, HK, D))
+        dv = randn_bf16(g, (R, HK, D))
         pre_k, pre_v = [], []
         for ctx in self.contexts:
-            pre_k.append(randn_bf16(g, (H, ctx, D)))
-            pre_v.append(randn_bf16(g, (H, ctx, D)))
+            pre_k.append(randn_bf16(g, (HK, ctx, D)))
+            pre_v.append(randn_bf16(g, (HK, ctx, D)))
         return dict(pq=pq, pk=pk, pv=pv, dq=dq, dk=dk, dv=dv, pre_k=pre_k, pre_v=pre_v)
 
 
@@ -244,6 +249,8 @@ def workload(name: str):
         return Varlen(name, loguniform_lengths(5), 32, 128, seed=5)
     if name == "single_T2048_H32_KV8_D128":
         return Varlen(name, [2048], 32, 128, seed=6, num_kv_heads=8)
+    if name == "chunked_8192x512_plus_64_decode_H32_KV8_D128":
+        return ChunkedWorkload(seed=7, num_kv_heads=8)
     raise KeyError(name)
 
 
@@ -254,4 +261,5 @@ WORKLOADS = [
     "chunked_8192x512_plus_64_decode_H32_D128",
     "longmix_65536_plus_32768_H32_D128",
     "single_T2048_H32_KV8_D128",
+    "chunked_8192x512_plus_64_decode_H32_KV8_D128",
 ]
