@@ -368,53 +368,46 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
     return in + (int64_t)(seq_start + kp - pre) * row_stride;
   };
 
-  auto issue_tile = [&](const Block blk, int t, int k_off, int v_off) __attribute__((always_inline)) {
+  // Instruction i (< kInstPerWave) of this wave's share of the loads of tile
+  // t of blk (K and V): one 1 KB global-to-LDS load per matrix.
+  auto issue_part = [&](const Block blk, int t, int k_off, int v_off, int i) __attribute__((always_inline)) {
     const int t0 = t * kBN;
     uint8_t* const k_dst = lds + k_off;
     uint8_t* const v_dst = lds + v_off;
     const bool full = t0 + kBN <= blk.key_end;
     const bool all_new = !kChunked || t0 >= pre;
     const bool all_cached = kChunked && t0 + kBN <= pre;
+    const int j = 4 * i + gw;
+    const int row = j * C::kRowsPerInst + lrow;
     if (kPaged && full && all_cached) {
       // the rows of one load instruction (4, 8 or 16) lie in one block
-#pragma unroll
-      for (int i = 0; i < C::kInstPerWave; ++i) {
-        const int j = 4 * i + gw;
-        const int r0 = t0 + j * C::kRowsPerInst;
-        const int bi = __builtin_amdgcn_readfirstlane(r0 / kPageRows);
-        const int64_t base = (((int64_t)bt_row[bi] * HK + hk) * kPageRows + r0 % kPageRows) * D;
-        const int row = j * C::kRowsPerInst + lrow;
-        const uint32_t off = (uint32_t)(lrow * D + 8 * chunk_slot<D>(row, lslot));
-        __builtin_amdgcn_global_load_lds((const void*)(p.kc + base + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(p.vc + base + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
-      }
+      const int r0 = t0 + j * C::kRowsPerInst;
+      const int bi = __builtin_amdgcn_readfirstlane(r0 / kPageRows);
+      const int64_t base = (((int64_t)bt_row[bi] * HK + hk) * kPageRows + r0 % kPageRows) * D;
+      const uint32_t off = (uint32_t)(lrow * D + 8 * chunk_slot<D>(row, lslot));
+      __builtin_amdgcn_global_load_lds((const void*)(p.kc + base + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(p.vc + base + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
     } else if (full && (all_new || all_cached)) {
       const int64_t step = all_new ? row_stride : (int64_t)D;
       const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
                                    : p.kc + cache_base + (int64_t)t0 * D;
       const uint16_t* vt = all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
                                    : p.vc + cache_base + (int64_t)t0 * D;
-#pragma unroll
-      for (int i = 0; i < C::kInstPerWave; ++i) {
-        const int j = 4 * i + gw;
-        const int row = j * C::kRowsPerInst + lrow;
-        const uint32_t off = (uint32_t)(row * step + 8 * chunk_slot<D>(row, lslot));
-        __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
-      }
+      const uint32_t off = (uint32_t)(row * step + 8 * chunk_slot<D>(row, lslot));
+      __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
     } else {
-#pragma unroll
-      for (int i = 0; i < C::kInstPerWave; ++i) {
-        const int j = 4 * i + gw;
-        const int row = j * C::kRowsPerInst + lrow;
-        const int kp = min(t0 + row, blk.key_end - 1);
-        const int col = 8 * chunk_slot<D>(row, lslot);
-        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(kin, p.kc, kp) + col),
-                                         (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(vin, p.vc, kp) + col),
-                                         (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
-      }
+      const int kp = min(t0 + row, blk.key_end - 1);
+      const int col = 8 * chunk_slot<D>(row, lslot);
+      __builtin_amdgcn_global_load_lds((const void*)(row_ptr(kin, p.kc, kp) + col),
+                                       (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(row_ptr(vin, p.vc, kp) + col),
+                                       (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
     }
+  };
+  auto issue_tile = [&](const Block blk, int t, int k_off, int v_off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::kInstPerWave; ++i) issue_part(blk, t, k_off, v_off, i);
   };
 
   // copy the tile's new-token rows of blk from LDS to the cache (group-wide)
@@ -542,8 +535,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
     }
   }
 
-  // S^T = K Q^T for one 64-key tile (two 32-key blocks), K from LDS at k_off.
-  auto score = [&](int k_off, f32x16_t (&s)[2]) __attribute__((always_inline)) {
+  // S^T = K Q^T for one 64-key tile (two 32-key blocks), K from LDS at k_off;
+  // hook(step) runs after each 16-d step's MFMAs (the next tile's loads are
+  // spread there).
+  auto score = [&](int k_off, f32x16_t (&s)[2], auto&& hook) __attribute__((always_inline)) {
     constexpr int NK = D / 16;
     uint32_t kb_addr[C::kKReadBases];
 #pragma unroll
@@ -566,6 +561,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks][0]), st.q[ks], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks][1]), st.q[ks], s[1], 0, 0, 0);
       if constexpr (ks + kAhead < NK) rd(std::integral_constant<int, ks + kAhead>{});
+      hook(ks_tag);
     });
   };
 
@@ -621,8 +617,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   };
 
   // O^T += V^T P^T for one tile, V from LDS at v_off; 16-key steps g outer,
-  // the D/32 accumulators inner (no back-to-back dependent MFMAs).
-  auto pv = [&](int v_off, const bf16x8_t (&pb)[4]) __attribute__((always_inline)) {
+  // the D/32 accumulators inner (no back-to-back dependent MFMAs); hook(g)
+  // runs after each step's MFMAs.
+  auto pv = [&](int v_off, const bf16x8_t (&pb)[4], auto&& hook) __attribute__((always_inline)) {
     constexpr int NV = C::kVReadsPerStep;
     const uint32_t va0 = lds0 + v_off + vbase[0];
     const uint32_t va1 = lds0 + v_off + vbase[1];
@@ -649,6 +646,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
         st.o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[g], st.o[mb], 0, 0, 0);
       });
       if constexpr (g + 2 < 4) rd(std::integral_constant<int, g + 2>{});
+      hook(g_tag);
     });
   };
 
@@ -684,14 +682,31 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   bf16x8_t p_prev[4];
   bool have_prev = false;
   int v_prev = 2, v_cur = 0, v_next = 1;  // upper V ring: tiles j-1, j, j+1
+  // The next tile's loads (kInstPerWave instructions per matrix and wave) are
+  // spread between a tile's MFMA steps, so the vector memory path drains
+  // them while the matrix cores work instead of stalling the issuing waves.
+  auto no_hook = [](auto) __attribute__((always_inline)) {};
+  auto spread = [&](bool active, const Block nb, int nt, int nk, int nv, auto steps_tag) __attribute__((always_inline)) {
+    constexpr int kSteps = decltype(steps_tag)::value;
+    return [&, active, nb, nt, nk, nv](auto step_tag) __attribute__((always_inline)) {
+      constexpr int st_ = decltype(step_tag)::value;
+      static_for<0, C::kInstPerWave>([&](auto i_tag) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_tag)::value;
+        if constexpr ((i + 1) * kSteps / C::kInstPerWave - 1 == st_)
+          if (active) issue_part(nb, nt, nk, nv, i);
+      });
+    };
+  };
   for (int j = 0; j <= n_up; ++j) {
     if (upper) {
-      if (j + 1 < n_up) {
-        const Pick nx = pick_tile(j + 1, true, n_up, e_lo, e_hi, z, qb_hi);
-        issue_tile(make_block(nx.qb, len, pre), tb + nx.t, C::kUpperK + ((j + 1) & 1) * C::kTileBytes,
-                   C::kUpperV + v_next * C::kTileBytes);
-      }
-      if (have_prev) pv(C::kUpperV + v_prev * C::kTileBytes, p_prev);
+      const bool load_next = j + 1 < n_up;
+      const Pick nx = pick_tile(j + 1, true, n_up, e_lo, e_hi, z, qb_hi);
+      const Block nb = make_block(nx.qb, len, pre);
+      const int nk = C::kUpperK + ((j + 1) & 1) * C::kTileBytes, nv = C::kUpperV + v_next * C::kTileBytes;
+      if (have_prev)
+        pv(C::kUpperV + v_prev * C::kTileBytes, p_prev, spread(load_next, nb, tb + nx.t, nk, nv, std::integral_constant<int, 4>{}));
+      else if (load_next)
+        issue_tile(nb, tb + nx.t, nk, nv);
       have_prev = false;
       if (j < n_up) {
         const Block blk = bhi;
@@ -702,7 +717,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
         tile_use(blk, t, use, mask);
         if (use) {
           f32x16_t s[2];
-          score(C::kUpperK + (j & 1) * C::kTileBytes, s);
+          score(C::kUpperK + (j & 1) * C::kTileBytes, s, no_hook);
           if (mask)
             softmax(s, blk, t, std::true_type{}, p_prev);
           else
@@ -715,10 +730,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       v_cur = v_next;
       v_next = r;
     } else if (j < n_lo) {
-      if (j + 1 < n_lo) {
-        const Pick nx = pick_tile(j + 1, false, n_up, e_lo, e_hi, z, qb_hi);
-        issue_tile(make_block(nx.qb, len, pre), tb + nx.t, lower_k(j + 1), lower_k(j + 1) + C::kTileBytes);
-      }
+      const bool load_next = j + 1 < n_lo;
+      const Pick nx = pick_tile(j + 1, false, n_up, e_lo, e_hi, z, qb_hi);
+      const Block nb = make_block(nx.qb, len, pre);
+      const int nk = lower_k(j + 1), nv = lower_k(j + 1) + C::kTileBytes;
       const Pick pk = pick_tile(j, false, n_up, e_lo, e_hi, z, qb_hi);
       const Block blk = make_block(pk.qb, len, pre);
       const int t = tb + pk.t;
@@ -733,12 +748,14 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       if (use) {
         f32x16_t s[2];
         bf16x8_t pb[4];
-        score(lower_k(j), s);
+        score(lower_k(j), s, spread(load_next, nb, tb + nx.t, nk, nv, std::integral_constant<int, D / 16>{}));
         if (mask)
           softmax(s, blk, t, std::true_type{}, pb);
         else
           softmax(s, blk, t, std::false_type{}, pb);
-        pv(lower_k(j) + C::kTileBytes, pb);
+        pv(lower_k(j) + C::kTileBytes, pb, no_hook);
+      } else if (load_next) {
+        issue_tile(nb, tb + nx.t, nk, nv);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
