@@ -44,8 +44,10 @@ METRIC = "prefill attention TFLOP/s + % bf16 MFMA peak (T=2048,H=32,D=128); KV G
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU's clocks ramp up over the first few hundred launches after idle;
+    # the default warmup lets the timed steps run at the sustained clock
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="single_T2048_H32_D128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
