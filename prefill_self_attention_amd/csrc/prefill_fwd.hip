@@ -405,9 +405,61 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
                                        (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
     }
   };
+  // All of this wave's loads of tile t of blk, issued together (for a paged
+  // cache with the three cases decided once per tile; the two forms compile
+  // to different register allocations, each the better one for its kernels).
   auto issue_tile = [&](const Block blk, int t, int k_off, int v_off) __attribute__((always_inline)) {
+    if constexpr (!kPaged) {
 #pragma unroll
-    for (int i = 0; i < C::kInstPerWave; ++i) issue_part(blk, t, k_off, v_off, i);
+      for (int i = 0; i < C::kInstPerWave; ++i) issue_part(blk, t, k_off, v_off, i);
+      return;
+    }
+    const int t0 = t * kBN;
+    uint8_t* const k_dst = lds + k_off;
+    uint8_t* const v_dst = lds + v_off;
+    const bool full = t0 + kBN <= blk.key_end;
+    const bool all_new = !kChunked || t0 >= pre;
+    const bool all_cached = kChunked && t0 + kBN <= pre;
+    if (kPaged && full && all_cached) {
+      // the rows of one load instruction (4, 8 or 16) lie in one block
+#pragma unroll
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int r0 = t0 + j * C::kRowsPerInst;
+        const int bi = __builtin_amdgcn_readfirstlane(r0 / kPageRows);
+        const int64_t base = (((int64_t)bt_row[bi] * HK + hk) * kPageRows + r0 % kPageRows) * D;
+        const int row = j * C::kRowsPerInst + lrow;
+        const uint32_t off = (uint32_t)(lrow * D + 8 * chunk_slot<D>(row, lslot));
+        __builtin_amdgcn_global_load_lds((const void*)(p.kc + base + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(p.vc + base + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
+      }
+    } else if (full && (all_new || all_cached)) {
+      const int64_t step = all_new ? row_stride : (int64_t)D;
+      const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                   : p.kc + cache_base + (int64_t)t0 * D;
+      const uint16_t* vt = all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                   : p.vc + cache_base + (int64_t)t0 * D;
+#pragma unroll
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int row = j * C::kRowsPerInst + lrow;
+        const uint32_t off = (uint32_t)(row * step + 8 * chunk_slot<D>(row, lslot));
+        __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kInstPerWave; ++i) {
+        const int j = 4 * i + gw;
+        const int row = j * C::kRowsPerInst + lrow;
+        const int kp = min(t0 + row, blk.key_end - 1);
+        const int col = 8 * chunk_slot<D>(row, lslot);
+        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(kin, p.kc, kp) + col),
+                                         (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(row_ptr(vin, p.vc, kp) + col),
+                                         (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
+      }
+    }
   };
 
   // copy the tile's new-token rows of blk from LDS to the cache (group-wide)
@@ -703,10 +755,14 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       const Pick nx = pick_tile(j + 1, true, n_up, e_lo, e_hi, z, qb_hi);
       const Block nb = make_block(nx.qb, len, pre);
       const int nk = C::kUpperK + ((j + 1) & 1) * C::kTileBytes, nv = C::kUpperV + v_next * C::kTileBytes;
-      if (have_prev)
+      // paged caches keep the burst at the start of the interval: their
+      // per-instruction block lookups inside the MFMA steps cost more
+      // registers than the spread saves
+      if (have_prev && !kPaged)
         pv(C::kUpperV + v_prev * C::kTileBytes, p_prev, spread(load_next, nb, tb + nx.t, nk, nv, std::integral_constant<int, 4>{}));
       else if (load_next)
         issue_tile(nb, tb + nx.t, nk, nv);
+      if (have_prev && kPaged) pv(C::kUpperV + v_prev * C::kTileBytes, p_prev, no_hook);
       have_prev = false;
       if (j < n_up) {
         const Block blk = bhi;
@@ -734,6 +790,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       const Pick nx = pick_tile(j + 1, false, n_up, e_lo, e_hi, z, qb_hi);
       const Block nb = make_block(nx.qb, len, pre);
       const int nk = lower_k(j + 1), nv = lower_k(j + 1) + C::kTileBytes;
+      if (kPaged && load_next) issue_tile(nb, tb + nx.t, nk, nv);
       const Pick pk = pick_tile(j, false, n_up, e_lo, e_hi, z, qb_hi);
       const Block blk = make_block(pk.qb, len, pre);
       const int t = tb + pk.t;
@@ -748,13 +805,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       if (use) {
         f32x16_t s[2];
         bf16x8_t pb[4];
-        score(lower_k(j), s, spread(load_next, nb, tb + nx.t, nk, nv, std::integral_constant<int, D / 16>{}));
+        score(lower_k(j), s, spread(load_next && !kPaged, nb, tb + nx.t, nk, nv, std::integral_constant<int, D / 16>{}));
         if (mask)
           softmax(s, blk, t, std::true_type{}, pb);
         else
           softmax(s, blk, t, std::false_type{}, pb);
         pv(lower_k(j) + C::kTileBytes, pb, no_hook);
-      } else if (load_next) {
+      } else if (load_next && !kPaged) {
         issue_tile(nb, tb + nx.t, nk, nv);
       }
     }
