@@ -132,12 +132,19 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
     }
     __syncthreads();  // wsum is rewritten by the next round
     if (c.items + c.dec > 0) {
-      for (int qb = 0; qb * kQueryBlock < len; ++qb) {
-        const int q0 = qb * kQueryBlock;
-        const int qend = min(q0 + kQueryBlock, len);
-        const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
-        for (int s = 0; s < ns; ++s) {
+      // items segment by segment, the blocks of one segment adjacent: with
+      // item i of head h run as step i * H + h of a grid that is a multiple of
+      // H and of the 8 XCDs, the blocks reading one segment's K/V tiles then
+      // run at the same time on one XCD and share its L2
+      const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
+      const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
+      const int ns_max = min((ntiles_last + seg_tiles - 1) / seg_tiles, max_segs);
+      for (int s = 0; s < ns_max; ++s)
+        for (int qb = 0; qb < nqb; ++qb) {
+          const int qend = min(qb * kQueryBlock + kQueryBlock, len);
+          const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
+          const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
+          if (s >= ns) continue;
           if (len == 1) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
             ++off_d;
@@ -146,6 +153,11 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
             ++off_i;
           }
         }
+      for (int qb = 0; qb < nqb; ++qb) {
+        const int q0 = qb * kQueryBlock;
+        const int qend = min(q0 + kQueryBlock, len);
+        const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
+        const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
