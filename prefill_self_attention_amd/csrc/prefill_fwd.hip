@@ -315,9 +315,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   const bool has_lo = !kSplit && z < qb_hi;
   const Block blo = make_block(z, len, pre);
   const Block bhi = make_block(qb_hi, len, pre);
-  const int tb = kSplit ? seg * p.seg_tiles : 0;  // first key tile of the item
+  // split mode: segment seg of nseg covers tiles [seg * n / nseg, (seg + 1) * n / nseg)
+  const int tb = kSplit ? seg * bhi.ntiles / nseg : 0;  // first key tile of the item
   const int e_lo = has_lo ? blo.ntiles : 0;
-  const int e_hi = kSplit ? min(p.seg_tiles, bhi.ntiles - tb) : bhi.ntiles;
+  const int e_hi = kSplit ? (seg + 1) * bhi.ntiles / nseg - tb : bhi.ntiles;
   const int n_up = (e_lo + e_hi + 1) / 2;  // tiles of the upper group
   const int n_lo = e_lo + e_hi - n_up;     // tiles of the lower group (<= n_up)
 

@@ -64,6 +64,15 @@ struct SeqPlan {
   int items, dec, merges;
 };
 
+// Segments of a block whose keys span ntiles tiles: decode rows (one query)
+// take segments of about seg_tiles tiles; blocks of several rows, whose
+// partial outputs are 128 rows each, about 2 * seg_tiles.  At most max_segs.
+// Segment s covers tiles [s * ntiles / ns, (s + 1) * ntiles / ns).
+__device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs) {
+  const int target = decode_row ? seg_tiles : 2 * seg_tiles;
+  return min((ntiles + target - 1) / target, max_segs);
+}
+
 // Segments of every query block of one sequence (work items; a length-1
 // sequence's go to the decode list), and the merge entries of the blocks with
 // more than one segment.  Segment counts are capped at max_segs, so malformed
@@ -73,7 +82,7 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs) {
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-    const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
+    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
     if (ns < 1) continue;
     if (len == 1)
       r.dec += ns;
@@ -138,12 +147,12 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       // run at the same time on one XCD and share its L2
       const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
       const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
-      const int ns_max = min((ntiles_last + seg_tiles - 1) / seg_tiles, max_segs);
+      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs);
       for (int s = 0; s < ns_max; ++s)
         for (int qb = 0; qb < nqb; ++qb) {
           const int qend = min(qb * kQueryBlock + kQueryBlock, len);
           const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-          const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
+          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
           if (s >= ns) continue;
           if (len == 1) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
@@ -157,7 +166,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = min((ntiles + seg_tiles - 1) / seg_tiles, max_segs);
+        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
@@ -277,7 +286,7 @@ void splitkv_decode_kernel(FwdParams p) {
   const int units = H / GC;
   const int64_t steps = (int64_t)p.hdr[2] * units;
   const float c = p.scale_log2;
-  const int seg_keys = p.seg_tiles * kKeyTile;
+
   const float neg_inf = -__builtin_huge_valf();
 
   for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += p.dec_grid) {
@@ -287,8 +296,9 @@ void splitkv_decode_kernel(FwdParams p) {
     const int b = it.x, s = it.y, ns = it.z;
     const int tok = p.cu[b];
     const int pre = p.prefix[b];
-    const int k0 = s * seg_keys;
-    const int k1 = min(k0 + seg_keys, pre + 1);  // keys [k0, k1) of this segment
+    const int ntiles = (pre + 1 + kKeyTile - 1) / kKeyTile;
+    const int k0 = s * ntiles / ns * kKeyTile;
+    const int k1 = min((s + 1) * ntiles / ns * kKeyTile, pre + 1);  // keys [k0, k1) of this segment
     const int per = ((k1 - k0 + 3) / 4 + KPI - 1) / KPI * KPI;
     const int w0 = k0 + wave * per;
     const int w1 = min(w0 + per, k1);            // this wave's keys
