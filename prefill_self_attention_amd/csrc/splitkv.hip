@@ -64,12 +64,14 @@ struct SeqPlan {
   int items, dec, merges;
 };
 
-// Segments of a block whose keys span ntiles tiles: decode rows (one query)
-// take segments of about seg_tiles tiles; blocks of several rows, whose
-// partial outputs are 128 rows each, about 2 * seg_tiles.  At most max_segs.
+// Segments of a block whose keys span ntiles tiles: decode rows (one query,
+// HBM-bound) take segments of about seg_tiles tiles; blocks of several rows
+// (MFMA-bound, 128-row partial outputs) about 4 * seg_tiles -- longer
+// segments measured faster there (fewer partials to write and merge), and
+// shorter ones for decode rows (more units in flight).  At most max_segs.
 // Segment s covers tiles [s * ntiles / ns, (s + 1) * ntiles / ns).
 __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs) {
-  const int target = decode_row ? seg_tiles : 2 * seg_tiles;
+  const int target = decode_row ? seg_tiles : 4 * seg_tiles;
   return min((ntiles + target - 1) / target, max_segs);
 }
 
