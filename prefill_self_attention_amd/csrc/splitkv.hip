@@ -332,15 +332,23 @@ void splitkv_decode_kernel(FwdParams p) {
 
     // cached keys kb + u KPI + kslot of a group of kDecUnroll steps; positions
     // past the wave's last cached key load that key again (and are masked)
-    auto load = [&](int kb, uint4 (&kr)[kDecUnroll], uint4 (&vr)[kDecUnroll]) __attribute__((always_inline)) {
+    // paged cache: a step's KPI keys (KPI divides 16, steps start at
+    // multiples of KPI) lie in one block, one scalar block id per step; the
+    // ids of a group are fetched a group ahead of its loads
+    auto fetch = [&](int kb, int (&ids)[kDecUnroll]) __attribute__((always_inline)) {
+      if constexpr (kPaged) {
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) ids[u] = bt_row[min(kb + u * KPI, last_sb) / kPageRows];
+      }
+    };
+    auto load = [&](int kb, uint4 (&kr)[kDecUnroll], uint4 (&vr)[kDecUnroll], const int (&ids)[kDecUnroll])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
         if constexpr (kPaged) {
-          // a step's KPI keys (KPI divides 16, steps start at multiples of
-          // KPI) lie in one block: one scalar block id per step
           const int sb = min(kb + u * KPI, last_sb);
           const int kq = min(sb + kslot, wc - 1);
-          const int64_t base = (((int64_t)bt_row[sb / kPageRows] * HK + hk) * kPageRows) * D;
+          const int64_t base = (((int64_t)ids[u] * HK + hk) * kPageRows) * D;
           const uint32_t off = (uint32_t)(kq % kPageRows) * D + 8 * dch;
           kr[u] = *(const uint4*)(p.kc + base + off);
           vr[u] = *(const uint4*)(p.vc + base + off);
@@ -388,12 +396,17 @@ void splitkv_decode_kernel(FwdParams p) {
     if (w0 < wc) {
       constexpr int kStep = kDecUnroll * KPI;
       uint4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
-      load(w0, ka, va);
+      int ida[kDecUnroll], idb[kDecUnroll];
+      fetch(w0, ida);
+      fetch(w0 + kStep, idb);
+      load(w0, ka, va, ida);
       for (int kb = w0;; kb += 2 * kStep) {
-        load(kb + kStep, kb2, vb2);
+        fetch(kb + 2 * kStep, ida);
+        load(kb + kStep, kb2, vb2, idb);
         consume(kb, ka, va);
         if (kb + kStep >= wc) break;
-        load(kb + 2 * kStep, ka, va);
+        fetch(kb + 3 * kStep, idb);
+        load(kb + 2 * kStep, ka, va, ida);
         consume(kb + kStep, kb2, vb2);
         if (kb + 2 * kStep >= wc) break;
       }
