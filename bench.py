@@ -10,8 +10,10 @@ before the timed region.  Prints one JSON line.
   value     = algorithmic FLOPs per step / mean step time (TFLOP/s); the
               algorithmic FLOPs count 4*D per causal (query, key) pair per head
               (QK^T and PV, 2*D each), the masked half excluded.
-  roofline  = the same FLOPs / the mean kernel duration from HIP events on the
-              launch stream, against the dense bf16 MFMA peak (2.5 PFLOP/s);
+  roofline  = the same FLOPs / the kernel's average launch duration (the timed
+              steps are single launches, back to back between two HIP events
+              on the launch stream), against the dense bf16 MFMA peak
+              (2.5 PFLOP/s);
               traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE and
               WRITE_SIZE counters (profiles/), scaled by a copy-kernel
               calibration, or null if the kernel source changed since.
@@ -106,24 +108,43 @@ def cpu_baseline(w, q, k, v, flops):
                       % (w.num_tokens, w.num_heads, w.head_dim)}
 
 
-def timed(fn, steps, warmup):
-    """Mean and sorted per-launch times (ms) of fn on the current stream."""
+def timed_steps(fn, steps, warmup):
+    """Mean time (ms) of one call of fn: `steps` calls back to back on the
+    current stream, bracketed by two events (nothing recorded between them)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def launch_times(fn, steps):
+    """Sorted per-call times (ms), each call between its own pair of events.
+    A separate pass: the event records between calls serialise the stream and
+    add a few microseconds per call, so these are not used for the step time."""
+    import torch
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record(stream)
         fn()
         b.record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, sorted(a.elapsed_time(b) for a, b in evs)
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def timed(fn, steps, warmup):
+    """Mean time per call (ms, back to back) and sorted per-call times."""
+    ms = timed_steps(fn, steps, warmup)
+    return ms, launch_times(fn, steps)
 
 
 def bench_chunked(args, wl, P):
@@ -156,7 +177,7 @@ def bench_chunked(args, wl, P):
     def step():
         P.prefill_attn_chunked(q, k, v, cu, kc, vc, out, pre, scale=st.scale, max_seqlen=wl.chunk_len)
 
-    ms, launches = timed(step, args.steps, args.warmup)
+    ms = timed_steps(step, args.steps, args.warmup)
     pairs = causal_pairs(st.lengths, st.prefix_lens)
     flops = 4.0 * D * H * pairs
     # decode rows alone: rows 1..R of the cache, one new token each
@@ -169,7 +190,7 @@ def bench_chunked(args, wl, P):
     def decode():
         P.prefill_attn_chunked(qd, kd, vd, cud, kcd, vcd, outd, pred, scale=st.scale, max_seqlen=1)
 
-    msd, launchesd = timed(decode, args.steps, args.warmup)
+    msd = timed_steps(decode, args.steps, args.warmup)
     dec_bytes = 2.0 * sum(c_ + 1 for c_ in wl.contexts) * HK * D * 2  # K and V of every context row, once per K/V head
 
     # the same step and decode rows through the split-KV path (plan, attention
@@ -185,8 +206,8 @@ def bench_chunked(args, wl, P):
         P.prefill_attn_chunked_splitkv(qd, kd, vd, cud, kcd, vcd, outd, pred, scale=st.scale,
                                        max_seqlen=1, workspace=wsd)
 
-    mss, launchess = timed(step_split, args.steps, args.warmup)
-    msds, launchesds = timed(decode_split, args.steps, args.warmup)
+    mss = timed_steps(step_split, args.steps, args.warmup)
+    msds = timed_steps(decode_split, args.steps, args.warmup)
 
     # and over a paged cache: the same contents in 16-token blocks placed by
     # a seeded random permutation of the pool, located through a block table
@@ -211,8 +232,8 @@ def bench_chunked(args, wl, P):
         P.prefill_attn_chunked_splitkv_paged(qd, kd, vd, cud, kp, vp, btd, outd, pred, scale=st.scale,
                                              max_seqlen=1, workspace=wsd)
 
-    msp, launchesp = timed(step_paged, args.steps, args.warmup)
-    msdp, launchesdp = timed(decode_paged, args.steps, args.warmup)
+    msp = timed_steps(step_paged, args.steps, args.warmup)
+    msdp = timed_steps(decode_paged, args.steps, args.warmup)
     del kp, vp
     value = flops / (ms * 1e-3) / 1e12
     return {
@@ -233,22 +254,21 @@ def bench_chunked(args, wl, P):
                    "tokens": int(q.shape[0]), "num_heads": H, "num_kv_heads": HK, "head_dim": D, "causal": True,
                    "kv_cache_write": True, "scale": st.scale},
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "launch_us": {"mean": round(sum(launches) / len(launches) * 1e3, 2),
-                      "median": round(launches[len(launches) // 2] * 1e3, 2)},
+        "us_per_step": round(ms * 1e3, 2),
         "decode_only": {"rows": R, "context_tokens": sum(wl.contexts),
-                        "launch_us_mean": round(sum(launchesd) / len(launchesd) * 1e3, 2),
+                        "us_per_step": round(msd * 1e3, 2),
                         "kv_read_gbps": round(dec_bytes / (msd * 1e-3) / 1e9, 1),
                         "frac_of_hbm_8tbs": round(dec_bytes / (msd * 1e-3) / 8e12, 4)},
         "splitkv": {"ms_per_step": round(mss, 5),
                     "tflops": round(flops / (mss * 1e-3) / 1e12, 2),
-                    "launch_us_mean": round(sum(launchess) / len(launchess) * 1e3, 2),
-                    "decode_only_us_mean": round(sum(launchesds) / len(launchesds) * 1e3, 2),
+                    "us_per_step": round(mss * 1e3, 2),
+                    "decode_only_us_per_step": round(msds * 1e3, 2),
                     "decode_kv_read_gbps": round(dec_bytes / (msds * 1e-3) / 1e9, 1),
                     "decode_frac_of_hbm_8tbs": round(dec_bytes / (msds * 1e-3) / 8e12, 4)},
         "splitkv_paged": {"ms_per_step": round(msp, 5),
                           "tflops": round(flops / (msp * 1e-3) / 1e12, 2),
-                          "launch_us_mean": round(sum(launchesp) / len(launchesp) * 1e3, 2),
-                          "decode_only_us_mean": round(sum(launchesdp) / len(launchesdp) * 1e3, 2),
+                          "us_per_step": round(msp * 1e3, 2),
+                          "decode_only_us_per_step": round(msdp * 1e3, 2),
                           "decode_kv_read_gbps": round(dec_bytes / (msdp * 1e-3) / 1e9, 1),
                           "block_tokens": 16, "blocks": B * mb},
         "roofline": None,
@@ -296,30 +316,15 @@ def main():
     def step():
         P.prefill_attn_varlen(qd, kd, vd, cu, kc, vc, out, scale=w.scale, max_seqlen=max_seqlen)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for a, b in evs:
-        a.record(stream)
-        step()
-        b.record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    # the timed region: K steps back to back (one kernel launch each) between
+    # two events; its mean is also the kernel's average launch duration
+    ms_per_step = timed_steps(step, args.steps, args.warmup)
+    # per-launch spread, from a separate pass with events around every launch
+    launch_ms = launch_times(step, args.steps)
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
-    ms_per_step = total_ms / args.steps
 
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    achieved = value
 
     # the same step writing an INT8 cache (codes + one float scale per token
     # and K/V head) instead of the bf16 cache
@@ -332,7 +337,7 @@ def main():
         P.prefill_attn_varlen_int8(qd, kd, vd, cu, kq8, vq8, ks8, vs8, out, scale=w.scale,
                                    max_seqlen=max_seqlen)
 
-    ms8, launches8 = timed(step_int8, args.steps, args.warmup)
+    ms8 = timed_steps(step_int8, args.steps, args.warmup)
     cache8_bytes = 2.0 * N * HK * (D + 4)
     traffic, traffic_note = read_traffic() if args.workload == "single_T2048_H32_D128" else (None, "n/a")
 
@@ -356,6 +361,8 @@ def main():
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kv_write_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "algorithmic_hbm_gbps": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        # each launch between its own events (separate pass; the event records
+        # add a few microseconds per launch)
         "launch_us": {"mean": round(mean_launch_ms * 1e3, 2),
                       "median": round(launch_ms[len(launch_ms) // 2] * 1e3, 2),
                       "p99": round(launch_ms[min(len(launch_ms) - 1,
@@ -364,7 +371,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
-        "int8_cache": {"launch_us_mean": round(sum(launches8) / len(launches8) * 1e3, 2),
+        "int8_cache": {"us_per_step": round(ms8 * 1e3, 2),
                        "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2),
                        "cache_bytes_written": cache8_bytes,
                        "bf16_cache_bytes": kv_bytes},

@@ -370,35 +370,52 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   };
 
   // Instruction i (< kInstPerWave) of this wave's share of the loads of tile
-  // t of blk (K and V): one 1 KB global-to-LDS load per matrix.
+  // t of blk (K and V): one 1 KB global-to-LDS load per matrix.  The tile's
+  // position and its case are made wave-uniform (readfirstlane), so the case
+  // is a scalar branch; unless the tile mixes cached and new rows, a load is a
+  // scalar base (the tile's first row) plus a 32-bit per-lane byte offset.
+  // Instruction i's rows are 4 i kRowsPerInst past instruction 0's, a
+  // multiple of 8 rows, so they share its swizzle slots.
+  const int lrow0 = gw * C::kRowsPerInst + lrow;  // row of instruction 0
+  const uint32_t lane_new = 2u * (uint32_t)(lrow0 * row_stride + 8 * chunk_slot<D>(lrow0, lslot));
+  const uint32_t lane_cached = 2u * (uint32_t)(lrow0 * D + 8 * chunk_slot<D>(lrow0, lslot));
   auto issue_part = [&](const Block blk, int t, int k_off, int v_off, int i) __attribute__((always_inline)) {
-    const int t0 = t * kBN;
+    const int t0 = __builtin_amdgcn_readfirstlane(t * kBN);
+    const int key_end = __builtin_amdgcn_readfirstlane(blk.key_end);
     uint8_t* const k_dst = lds + k_off;
     uint8_t* const v_dst = lds + v_off;
-    const bool full = t0 + kBN <= blk.key_end;
+    const bool full = t0 + kBN <= key_end;
     const bool all_new = !kChunked || t0 >= pre;
     const bool all_cached = kChunked && t0 + kBN <= pre;
     const int j = 4 * i + gw;
     const int row = j * C::kRowsPerInst + lrow;
-    if (kPaged && full && all_cached) {
-      // the rows of one load instruction (4, 8 or 16) lie in one block
+    if (kPaged && all_cached) {
+      // (all_cached implies full) the rows of one load instruction (4, 8 or
+      // 16) lie in one block
       const int r0 = t0 + j * C::kRowsPerInst;
       const int bi = __builtin_amdgcn_readfirstlane(r0 / kPageRows);
       const int64_t base = (((int64_t)bt_row[bi] * HK + hk) * kPageRows + r0 % kPageRows) * D;
       const uint32_t off = (uint32_t)(lrow * D + 8 * chunk_slot<D>(row, lslot));
       __builtin_amdgcn_global_load_lds((const void*)(p.kc + base + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(p.vc + base + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
-    } else if (full && (all_new || all_cached)) {
-      const int64_t step = all_new ? row_stride : (int64_t)D;
-      const uint16_t* kt = all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
-                                   : p.kc + cache_base + (int64_t)t0 * D;
-      const uint16_t* vt = all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
-                                   : p.vc + cache_base + (int64_t)t0 * D;
-      const uint32_t off = (uint32_t)(row * step + 8 * chunk_slot<D>(row, lslot));
+    } else if (all_new || all_cached) {
+      // all_cached implies full; a tile of new rows past the block's last key
+      // reads that key instead (every LDS row holds finite data)
+      const uint8_t* kt = (const uint8_t*)(all_new ? kin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                                   : p.kc + cache_base + (int64_t)t0 * D);
+      const uint8_t* vt = (const uint8_t*)(all_new ? vin + (int64_t)(seq_start + t0 - pre) * row_stride
+                                                   : p.vc + cache_base + (int64_t)t0 * D);
+      uint32_t off;  // bytes from the tile's first row
+      if (full)
+        off = (all_new ? lane_new : lane_cached) + (uint32_t)(4 * i * C::kRowsPerInst) * 2u *
+                                                       (uint32_t)(all_new ? row_stride : (int64_t)D);
+      else
+        off = 2u * (uint32_t)(min(row, key_end - 1 - t0) * row_stride + 8 * chunk_slot<D>(row, lslot));
       __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vt + off), (lds_void_t*)(v_dst + 1024 * j), 16, 0, 0);
     } else {
-      const int kp = min(t0 + row, blk.key_end - 1);
+      // a tile holding both cached and new rows (once per chunked sequence)
+      const int kp = min(t0 + row, key_end - 1);
       const int col = 8 * chunk_slot<D>(row, lslot);
       __builtin_amdgcn_global_load_lds((const void*)(row_ptr(kin, p.kc, kp) + col),
                                        (lds_void_t*)(k_dst + 1024 * j), 16, 0, 0);
@@ -740,8 +757,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   // them while the matrix cores work instead of stalling the issuing waves.
   auto no_hook = [](auto) __attribute__((always_inline)) {};
   auto spread = [&](bool active, const Block nb, int nt, int nk, int nv, auto steps_tag) __attribute__((always_inline)) {
-    constexpr int kSteps = decltype(steps_tag)::value;
-    return [&, active, nb, nt, nk, nv](auto step_tag) __attribute__((always_inline)) {
+    return [&, active, nb, nt, nk, nv, steps_tag](auto step_tag) __attribute__((always_inline)) {
+      constexpr int kSteps = decltype(steps_tag)::value;
       constexpr int st_ = decltype(step_tag)::value;
       static_for<0, C::kInstPerWave>([&](auto i_tag) __attribute__((always_inline)) {
         constexpr int i = decltype(i_tag)::value;
