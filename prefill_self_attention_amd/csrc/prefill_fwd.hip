@@ -515,9 +515,11 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
           }
         }
       } else if (mine) {
+        // streaming stores: this launch never reads these rows back, so they
+        // should not take L2 lines from the K/V tiles other work-groups reuse
         const int64_t dst = cache_elem(kp) + 8 * ch;
-        *(u32x4_t*)(p.kc + dst) = kr[i];
-        *(u32x4_t*)(p.vc + dst) = vr[i];
+        __builtin_nontemporal_store(kr[i], (u32x4_t*)(p.kc + dst));
+        __builtin_nontemporal_store(vr[i], (u32x4_t*)(p.vc + dst));
       }
     }
   };
@@ -548,14 +550,28 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
     const int row = qrow0 + ql;
     const float inv = 1.f / row_sum_halves(l_part);
     if (row >= len_rows) return;
-    uint16_t* dst = p.out + ((int64_t)(seq_start + row) * H + h) * D + 4 * hh;
+    // Lane (row, hh) holds d = 32 mb + 8 cc + 4 hh + [0, 4).  Lanes l and l^32
+    // (the same row) trade pieces so that the hh = 0 lane holds the 8
+    // consecutive d of chunk 2 cp and the hh = 1 lane those of chunk 2 cp + 1:
+    // 16-byte stores, 32 contiguous bytes of a row per lane pair.
+    uint16_t* dst = p.out + ((int64_t)(seq_start + row) * H + h) * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        u32x2_t w = {pack_bf16x2(st.o[mb][4 * cc + 0] * inv, st.o[mb][4 * cc + 1] * inv),
-                     pack_bf16x2(st.o[mb][4 * cc + 2] * inv, st.o[mb][4 * cc + 3] * inv)};
-        *(u32x2_t*)(dst + 32 * mb + 8 * cc) = w;
+      for (int cp = 0; cp < 2; ++cp) {
+        const int ca = 2 * cp, cb = 2 * cp + 1;
+        const uint32_t a0 = pack_bf16x2(st.o[mb][4 * ca + 0] * inv, st.o[mb][4 * ca + 1] * inv);
+        const uint32_t a1 = pack_bf16x2(st.o[mb][4 * ca + 2] * inv, st.o[mb][4 * ca + 3] * inv);
+        const uint32_t b0 = pack_bf16x2(st.o[mb][4 * cb + 0] * inv, st.o[mb][4 * cb + 1] * inv);
+        const uint32_t b1 = pack_bf16x2(st.o[mb][4 * cb + 2] * inv, st.o[mb][4 * cb + 3] * inv);
+        // hh = 0 sends its chunk-cb piece, hh = 1 its chunk-ca piece; lanes
+        // 0-31 find the partner's value in the second result, 32-63 in the first
+        const uint32_t s0 = hh ? a0 : b0, s1 = hh ? a1 : b1;
+        const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+        const uint32_t o0 = hh ? r0[0] : r0[1], o1 = hh ? r1[0] : r1[1];
+        const u32x4_t w = hh ? u32x4_t{o0, o1, b0, b1} : u32x4_t{a0, a1, o0, o1};
+        *(u32x4_t*)(dst + 32 * mb + 8 * (hh ? cb : ca)) = w;
       }
   };
 
