@@ -507,8 +507,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
         const float va = group_max<C::kCpr>(absmax8(vr[i]));
         if (mine) {
           const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
-          *(u32x2_t*)(p.kq + dst) = quantize8(kr[i], ka);
-          *(u32x2_t*)(p.vq + dst) = quantize8(vr[i], va);
+          __builtin_nontemporal_store(quantize8(kr[i], ka), (u32x2_t*)(p.kq + dst));
+          __builtin_nontemporal_store(quantize8(vr[i], va), (u32x2_t*)(p.vq + dst));
           if (ch == 0) {
             p.ks[cache_base / D + kp] = int8_scale(ka);
             p.vs[cache_base / D + kp] = int8_scale(va);
