@@ -19,6 +19,16 @@ before the timed region.  Prints one JSON line.
               calibration, or null if the kernel source changed since.
   cpu_baseline = the float64 oracle on the host cores over the same workload.
 
+Context fields (not part of value): launch_us (each launch between its own
+events), cold_launch_us (after a 1 GiB fill that evicts L2 and the Infinity
+Cache), kv_write_standalone_copy (the cache write alone as a plain torch copy),
+gemm_bf16_context (a large hipBLASLt bf16 GEMM at the run's clock),
+gpu_clocks_power (amd-smi before and after the timed steps, when available),
+int8_cache (the same step writing the INT8 cache).  The chunked workloads
+report the heaviest step one-pass, split-KV and paged, the decode rows alone,
+and every step summed (all_steps_splitkv) with the prompt's chunks alone
+against one varlen call over the whole prompt.
+
 Options: --gpus N (only 1 is supported: the path runs on one GPU),
 --steps K, --warmup W, --workload NAME, --no-cpu-baseline, --copy-calib
 (runs only a 1 GiB device copy, for the counter calibration).
@@ -147,6 +157,91 @@ def timed(fn, steps, warmup):
     return ms, launch_times(fn, steps)
 
 
+def cold_launch_times(fn, steps, flush_bytes=1 << 30):
+    """Sorted per-call times (ms) with L2 and the 256 MB Infinity Cache evicted
+    before every call by a 1 GiB device fill (outside the events)."""
+    import torch
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        flush.zero_()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    del flush
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def stats_us(ms_sorted):
+    n = len(ms_sorted)
+    return {"median": round(ms_sorted[n // 2] * 1e3, 2),
+            "p99": round(ms_sorted[min(n - 1, int(math.ceil(0.99 * n)) - 1)] * 1e3, 2)}
+
+
+def smi_under_load(fn, ms_per_call, seconds=1.5):
+    """amd-smi clocks and power sampled from a side thread while about
+    `seconds` of back-to-back calls of fn run (after all timed passes)."""
+    import threading
+    import time as _t
+    import torch
+    res = {}
+
+    def sample():
+        _t.sleep(0.4)
+        res["s"] = smi_sample()
+
+    th = threading.Thread(target=sample)
+    th.start()
+    for _ in range(max(1, int(seconds / (ms_per_call * 1e-3)))):
+        fn()
+    torch.cuda.synchronize()
+    th.join()
+    return res.get("s")
+
+
+def gemm_context(n=8192, steps=20):
+    """A large plain bf16 GEMM through torch (hipBLASLt), back to back: the
+    matrix rate this part sustains at the clock of the run, as context for the
+    published dense peak (not a roofline denominator)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda", generator=g)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda", generator=g)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    ms = timed_steps(lambda: torch.matmul(a, b, out=c), steps, 5)
+    del a, b, c
+    return {"shape": [n, n, n], "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
+def smi_sample():
+    """GPU clocks and power from amd-smi, best effort (None when unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    found = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            for kk, vv in x.items():
+                walk(vv, path + [str(kk)])
+        elif isinstance(x, list):
+            for i, vv in enumerate(x):
+                walk(vv, path + [str(i)])
+        elif len(path) >= 3 and path[-1] == "value" and len(found) < 12:
+            # current clock of each graphics partition, and socket power
+            if (path[-3].startswith("gfx") and path[-2] == "clk") or "socket_power" in path[-2]:
+                found["/".join(path[-3:-1])] = x
+
+    walk(d, [])
+    return found or None
+
+
 def bench_chunked(args, wl, P):
     """The heaviest step of the chunked workload (last 512-token chunk of the
     8192-token prompt beside the 64 decode rows) and, separately, the 64
@@ -235,6 +330,54 @@ def bench_chunked(args, wl, P):
     msp = timed_steps(step_paged, args.steps, args.warmup)
     msdp = timed_steps(decode_paged, args.steps, args.warmup)
     del kp, vp
+
+    # every step c = 0 .. 15 through split-KV, summed (the cache already holds
+    # the prompt's earlier chunks; a step rewrites its own chunk with the same
+    # values), and the prompt's chunks alone (no decode rows) summed against
+    # one varlen call over the whole 8192-token prompt: the chunking overhead
+    L = wl.chunk_len
+    pqd, pkd, pvd = t["pq"].to(dev), t["pk"].to(dev), t["pv"].to(dev)
+    dq_, dk_, dv_ = t["dq"].to(dev), t["dk"].to(dev), t["dv"].to(dev)
+    reps = 50
+    step_us, chunk_us = [], []
+    out1 = torch.empty((L, H, D), dtype=torch.bfloat16, device=dev)
+    outs = torch.empty((L + R, H, D), dtype=torch.bfloat16, device=dev)
+    cu1 = torch.tensor([0, L], dtype=torch.int32, device=dev)
+    for c_ in range(wl.num_chunks):
+        stc = wl.step(c_)
+        sl_ = slice(c_ * L, (c_ + 1) * L)
+        qs, ks_, vs_ = (torch.cat([a[sl_], b_]) for a, b_ in ((pqd, dq_), (pkd, dk_), (pvd, dv_)))
+        cus = torch.tensor(stc.cu_seqlens, dtype=torch.int32, device=dev)
+        pres = torch.tensor(stc.prefix_lens, dtype=torch.int32, device=dev)
+        pre1 = torch.tensor([c_ * L], dtype=torch.int32, device=dev)
+
+        def one_step():
+            P.prefill_attn_chunked_splitkv(qs, ks_, vs_, cus, kc, vc, outs, pres, scale=st.scale,
+                                           max_seqlen=L, workspace=ws)
+
+        def one_chunk():
+            P.prefill_attn_chunked_splitkv(pqd[sl_], pkd[sl_], pvd[sl_], cu1, kc[:1], vc[:1], out1, pre1,
+                                           scale=st.scale, max_seqlen=L, workspace=ws)
+
+        step_us.append(timed_steps(one_step, reps, 10) * 1e3)
+        chunk_us.append(timed_steps(one_chunk, reps, 10) * 1e3)
+    kc1 = torch.empty_like(pkd)
+    vc1 = torch.empty_like(pvd)
+    out_full = torch.empty_like(pqd)
+    cu_full = torch.tensor([0, wl.prompt_len], dtype=torch.int32, device=dev)
+
+    def one_shot():
+        P.prefill_attn_varlen(pqd, pkd, pvd, cu_full, kc1, vc1, out_full, scale=st.scale, max_seqlen=wl.prompt_len)
+
+    one_shot_us = timed_steps(one_shot, reps, 10) * 1e3
+    prompt_flops = 4.0 * D * H * causal_pairs([wl.prompt_len])
+    all_steps = {"steps": wl.num_chunks, "sum_us": round(sum(step_us), 1),
+                 "per_step_us": [round(x, 1) for x in step_us],
+                 "prompt_chunks_alone_sum_us": round(sum(chunk_us), 1),
+                 "one_shot_varlen_us": round(one_shot_us, 1),
+                 "chunking_overhead": round(sum(chunk_us) / one_shot_us, 3),
+                 "one_shot_tflops": round(prompt_flops / (one_shot_us * 1e-6) / 1e12, 1)}
+    del kc1, vc1, out_full, pqd, pkd, pvd
     value = flops / (ms * 1e-3) / 1e12
     return {
         "metric": METRIC,
@@ -271,6 +414,7 @@ def bench_chunked(args, wl, P):
                           "decode_only_us_per_step": round(msdp * 1e3, 2),
                           "decode_kv_read_gbps": round(dec_bytes / (msdp * 1e-3) / 1e9, 1),
                           "block_tokens": 16, "blocks": B * mb},
+        "all_steps_splitkv": all_steps,
         "roofline": None,
         "cpu_baseline": None,
     }
@@ -338,6 +482,22 @@ def main():
                                    max_seqlen=max_seqlen)
 
     ms8 = timed_steps(step_int8, args.steps, args.warmup)
+
+    # cold: every launch after a 1 GiB fill that evicts L2 and the Infinity Cache
+    cold_ms = cold_launch_times(step, min(args.steps, 100))
+    # the cache write on its own, as a plain torch copy of k and v into the
+    # cache layout (per sequence [HK, len, D]): read + write bytes per time
+    kv_copy = None
+    if len(w.lengths) == 1:
+        kcv, vcv = kc.view(HK, N, D), vc.view(HK, N, D)
+
+        def kv_copy_step():
+            kcv.copy_(kd.transpose(0, 1))
+            vcv.copy_(vd.transpose(0, 1))
+
+        msc = timed_steps(kv_copy_step, args.steps, 20)
+        kv_copy = {"us_per_step": round(msc * 1e3, 2), "gbps_read_plus_write": round(2 * kv_bytes / (msc * 1e-3) / 1e9, 1)}
+    gemm = gemm_context()
     cache8_bytes = 2.0 * N * HK * (D + 4)
     traffic, traffic_note = read_traffic() if args.workload == "single_T2048_H32_D128" else (None, "n/a")
 
@@ -371,6 +531,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_note": traffic_note,
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes},
+        "cold_launch_us": stats_us(cold_ms),
+        "kv_write_standalone_copy": kv_copy,
+        "gemm_bf16_context": dict(gemm, pct_of_published_peak=round(100.0 * gemm["tflops"] / PEAK_BF16_TFLOPS, 1),
+                                  attention_pct_of_it=round(100.0 * value / gemm["tflops"], 1)),
+        "gpu_clocks_power_under_load": smi_under_load(step, ms_per_step),
         "int8_cache": {"us_per_step": round(ms8 * 1e3, 2),
                        "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2),
                        "cache_bytes_written": cache8_bytes,

@@ -311,7 +311,10 @@ def test_chunked_workload_16_steps():
 
 
 def test_longmix_sampled():
-    """Log-uniform lengths summing to 65536 plus one 32768-token sequence."""
+    """Log-uniform lengths summing to 65536 plus one 32768-token sequence: every
+    row of each sequence up to 2048 tokens, and of each longer one 256 evenly
+    spaced rows plus the block and tile edges at its start and end; all heads;
+    the whole cache bit for bit."""
     w = I.workload("longmix_65536_plus_32768_H32_D128")
     say("case %s: drawing inputs" % w.name)
     q, k, v = w.tensors()
@@ -319,10 +322,13 @@ def test_longmix_sampled():
     rows = []
     for b, L in enumerate(w.lengths):
         s = w.cu_seqlens[b]
-        loc = [0, 1, 63, 64, 127, 128, 129, L // 2, L - 2, L - 1]
-        loc += list(np.linspace(0, L - 1, 8).astype(int))
+        if L <= 2048:
+            rows += range(s, s + L)
+            continue
+        loc = [0, 1, 63, 64, 127, 128, 129, L // 2, L - 129, L - 128, L - 65, L - 64, L - 2, L - 1]
+        loc += list(np.linspace(0, L - 1, 256).astype(int))
         rows += sorted(set(s + x for x in loc if 0 <= x < L))
-    say("  oracle on %d sampled rows" % len(rows))
+    say("  oracle on %d sampled rows (about half a minute)" % len(rows))
     ref = oracle.prefill_rows(q, k, v, w.cu_seqlens, w.scale, rows)
     assert_close(out[rows], ref, w.name)
     n = w.num_tokens * w.num_heads * w.head_dim
