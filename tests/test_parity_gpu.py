@@ -339,6 +339,42 @@ def test_longmix_sampled():
     assert all(guards_intact(x) for x in wholes)
 
 
+def test_offsets_beyond_4gib():
+    """640 sequences of 1024 tokens, 32 query heads over 8 K/V heads: q and out
+    span 5.4 GB, so the last sequences' rows sit beyond every 32-bit byte
+    offset.  Inputs are drawn on the device from a seeded generator; three
+    sequences (first, middle, last) are copied back and checked against the
+    oracle on sampled rows, with their whole cache blocks bit for bit."""
+    B, T, H, HK, D = 640, 1024, 32, 8, 128
+    N = B * T
+    g = torch.Generator(device="cuda").manual_seed(1300)
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    say("case offsets beyond 4 GiB: drawing %d tokens on the device" % N)
+    q, k, v = draw((N, H, D)), draw((N, HK, D)), draw((N, HK, D))
+    cu = torch.arange(0, N + 1, T, dtype=torch.int32, device="cuda")
+    kc = torch.empty(N * HK * D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(q)
+    scale = I.default_scale(D)
+    P().prefill_attn_varlen(q, k, v, cu, kc, vc, out, scale=scale, max_seqlen=T)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 127, 128, 511, 1000, 1022, 1023]
+    for b in (0, B // 2, B - 1):
+        s = b * T
+        qs, ks, vs = q[s:s + T].cpu(), k[s:s + T].cpu(), v[s:s + T].cpu()
+        ref = oracle.prefill_rows(qs, ks, vs, [0, T], scale, rows)
+        assert_close(out[s:s + T][rows], ref, "sequence %d (out byte offset %d)" % (b, s * H * D * 2))
+        z = np.zeros(T * HK * D, np.uint16)
+        kimg, vimg = oracle.cache_image(ks, vs, [0, T], z, z)
+        blk = slice(s * HK * D, (s + T) * HK * D)
+        np.testing.assert_array_equal(bits(kc[blk]), kimg, err_msg="k cache of sequence %d" % b)
+        np.testing.assert_array_equal(bits(vc[blk]), vimg, err_msg="v cache of sequence %d" % b)
+    del q, k, v, kc, vc, out
+
+
 # ---------------------------------------------------------------- check mode
 
 def test_check_mode_rejects_bad_metadata():
