@@ -208,8 +208,10 @@ pa_status prefill_attn_varlen_int8(const uint16_t *q, const uint16_t *k, const u
  *
  * Errors as prefill_attn_chunked_gqa, plus PA_ERR_NULL for a NULL workspace,
  * PA_ERR_ALIGN, PA_ERR_ALIAS if the workspace equals another pointer,
- * PA_ERR_SHAPE for num_tokens < 0, and PA_ERR_WORKSPACE when workspace_bytes
- * is too small.  B == 0, max_seqlen == 0 or num_tokens == 0 enqueue nothing.
+ * PA_ERR_SHAPE for num_tokens < 0 or cache_capacity * head_dim >= 2^32 (one
+ * (sequence, K/V head) row of the cache must span fewer than 2^32 elements;
+ * 33.5M positions at D = 128), and PA_ERR_WORKSPACE when workspace_bytes is
+ * too small.  B == 0, max_seqlen == 0 or num_tokens == 0 enqueue nothing.
  */
 pa_status prefill_attn_chunked_splitkv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                        const int32_t *cu_seqlens, int32_t num_seqs,

@@ -251,6 +251,8 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   }
   if (!aligned16(workspace)) return PA_ERR_ALIGN;
   if (cache_capacity < 1 || num_tokens < 0) return PA_ERR_SHAPE;
+  // the decode pass addresses positions of one slab row with 32-bit element offsets
+  if (!block_table && (int64_t)cache_capacity * head_dim > (int64_t)UINT32_MAX) return PA_ERR_SHAPE;
   if (num_kv_heads < 1 || num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   int nqb = 0;
   st = check_grid(num_seqs, max_seqlen, num_heads, &nqb);

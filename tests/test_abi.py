@@ -139,6 +139,10 @@ def test_splitkv_rejections(lib):
     assert need > 0
     assert splitkv(lib, ws_bytes=need - 1) == 10
     assert P.pa_status_string(10).startswith("PA_ERR_WORKSPACE")
+    # a slab row of 2^32 or more elements is refused before anything else is looked at
+    assert splitkv(lib, cap=(1 << 25), D=128) == 2
+    assert splitkv(lib, cap=(1 << 27), D=32) == 2
+    assert splitkv(lib, cap=(1 << 25) - 1, D=128, ws_bytes=0) == 10
 
 
 def paged(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64, kc=A[4],
