@@ -60,6 +60,12 @@ def _load():
     lib.oracle_prefill_chunked_paged.restype = ctypes.c_int
     lib.oracle_quantize_rows_int8.argtypes = [p, ctypes.c_int64, i32, p, p]
     lib.oracle_quantize_rows_int8.restype = ctypes.c_int
+    lib.oracle_quantize_rows_fp8.argtypes = [p, ctypes.c_int64, i32, p, p]
+    lib.oracle_quantize_rows_fp8.restype = ctypes.c_int
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -260,6 +266,43 @@ def cache_image_int8(k, v, cu_seqlens):
     kimg, vimg = cache_image(k, v, cu_seqlens, z, z)
     kq, ks = quantize_rows_int8(kimg.reshape(N * HK, D))
     vq, vs = quantize_rows_int8(vimg.reshape(N * HK, D))
+    return kq.reshape(-1), ks.reshape(-1), vq.reshape(-1), vs.reshape(-1)
+
+
+def e4m3_encode(x):
+    """The E4M3 code of a float32 value, round to nearest, ties to even (see oracle.c)."""
+    return int(_load().oracle_e4m3_encode(float(np.float32(x))))
+
+
+def e4m3_decode(code):
+    """The value an E4M3 code stands for (NaN for S.1111.111)."""
+    return float(_load().oracle_e4m3_decode(int(code) & 0xFF))
+
+
+def quantize_rows_fp8(x):
+    """FP8 (E4M3) codes and float32 scales of bf16 rows (the last axis is one
+    row): symmetric, one scale per row, scale = amax/448, code =
+    E4M3(x * 448/amax) in float32 (see oracle.c).  Returns (codes uint8
+    x.shape, scales float32 x.shape[:-1])."""
+    a = _u16(x)
+    d = a.shape[-1]
+    rows = a.size // d if d else 0
+    codes = np.zeros(a.shape, np.uint8)
+    scales = np.zeros(a.shape[:-1], np.float32)
+    rc = _load().oracle_quantize_rows_fp8(_ptr(a), rows, d, _ptr(codes), _ptr(scales))
+    _check(rc, "quantize_rows_fp8")
+    return codes, scales
+
+
+def cache_image_fp8(k, v, cu_seqlens):
+    """FP8 varlen cache image, laid out as cache_image_int8.  Returns
+    (k_codes, k_scales, v_codes, v_scales): N*HK*D uint8 and N*HK float32."""
+    kk = _u16(k)
+    N, HK, D = kk.shape
+    z = np.zeros(N * HK * D, np.uint16)
+    kimg, vimg = cache_image(k, v, cu_seqlens, z, z)
+    kq, ks = quantize_rows_fp8(kimg.reshape(N * HK, D))
+    vq, vs = quantize_rows_fp8(vimg.reshape(N * HK, D))
     return kq.reshape(-1), ks.reshape(-1), vq.reshape(-1), vs.reshape(-1)
 
 

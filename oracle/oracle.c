@@ -435,6 +435,86 @@ int oracle_quantize_rows_int8(const uint16_t *x, int64_t rows, int32_t d,
 }
 
 /*
+ * FP8 rows for a quantised KV cache [P2 §4.3: K and V quantised, Q kept, one
+ * scale per token among the granularities listed; FP8 halves the cache as
+ * INT8 does].  The pages name no FP8 encoding; the reading taken here is the
+ * OCP 8-bit E4M3 format ("e4m3fn"): a sign bit, 4 exponent bits with bias 7
+ * and 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; there
+ * are no infinities, S.1111.111 is NaN and the largest finite magnitude is
+ * 1.75 * 2^8 = 448.  Symmetric, one float32 scale per (token, K/V head) row:
+ *     amax  = max_d |x_d|
+ *     scale = amax / 448                      (float32 division)
+ *     code  = E4M3(x_d * (448 / amax))        (float32 division and product,
+ *                                              then round to nearest E4M3
+ *                                              value, ties to even)
+ * A row with amax < 2^-100 gets scale 0 and codes of x_d * 0: zeros that keep
+ * x_d's sign.  The dequantised value is decode(code) * scale.  The encoding
+ * step is exact: the float32 product widens to double exactly, and the
+ * rounding is done on integers of at most four bits.
+ */
+static uint8_t e4m3_rne(float xf)
+{
+    const uint8_t s = signbit(xf) ? 0x80 : 0x00;
+    if (isnan(xf)) return s | 0x7f;
+    const double a = fabs((double)xf);
+    if (a == 0.0) return s;
+    if (a < 0x1p-6) {                          /* subnormal: steps of 2^-9 */
+        const double q = nearbyint(a * 512.0); /* ties to even; 8 = smallest normal */
+        return s | (uint8_t)q;
+    }
+    int e;
+    const double m = 2.0 * frexp(a, &e);       /* a = m * 2^(e-1), m in [1, 2) */
+    e -= 1;
+    double q = nearbyint((m - 1.0) * 8.0);     /* mantissa steps of 1/8, ties to even */
+    if (q == 8.0) {
+        e += 1;
+        q = 0.0;
+    }
+    if (e > 8 || (e == 8 && q == 7.0)) return s | 0x7f; /* beyond 448: NaN */
+    return s | (uint8_t)(((e + 7) << 3) | (int)q);
+}
+
+/* The value an E4M3 code stands for (NaN for S.1111.111). */
+double oracle_e4m3_decode(uint8_t c)
+{
+    const double sgn = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sgn * ldexp((double)m, -9);
+    return sgn * ldexp(1.0 + m / 8.0, e - 7);
+}
+
+uint8_t oracle_e4m3_encode(float x) { return e4m3_rne(x); }
+
+int oracle_quantize_rows_fp8(const uint16_t *x, int64_t rows, int32_t d,
+                             uint8_t *codes, float *scales)
+{
+    if (rows < 0 || d < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * d;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < d; ++i) {
+            const float a = fabsf((float)bf16_bits_to_double(xr[i]));
+            if (a > amax) amax = a;
+        }
+        float inv = 0.0f;
+        if (amax >= 0x1p-100f) {
+            scales[r] = amax / 448.0f;
+            inv = 448.0f / amax;
+        } else {
+            scales[r] = 0.0f;
+        }
+        uint8_t *cr = codes + r * d;
+        for (int32_t i = 0; i < d; ++i) {
+            const float t = (float)bf16_bits_to_double(xr[i]) * inv;
+            cr[i] = e4m3_rne(t);
+        }
+    }
+    return 0;
+}
+
+/*
  * Chunked prefill over a paged cache: as oracle_prefill_chunked, with the
  * prefix read from and the new tokens' K/V written to the blocks the block
  * table names (layout above).  k_cache / v_cache are [num_blocks, HK, 16, D];

@@ -538,6 +538,118 @@ def test_int8_cache_image_layout_bruteforce():
                 assert np.array_equal(vq[row * D:(row + 1) * D], cv[0]) and vs[row] == sv[0]
 
 
+# ---------------------------------------------------------------- FP8 rows
+# FP8 cache rows ("大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.3
+# lists low-precision cache formats; the encoding is the OCP 8-bit E4M3 format
+# by reading): sign, 4 exponent bits with bias 7, 3 mantissa bits,
+# subnormals m/8 * 2^-6, no infinities, S.1111.111 NaN, largest finite 448.
+
+def test_e4m3_textbook_values():
+    """Code values fixed by the format definition."""
+    D = oracle.e4m3_decode
+    assert D(0x00) == 0.0 and np.signbit(D(0x80)) and D(0x80) == 0.0
+    assert D(0x38) == 1.0 and D(0xB8) == -1.0
+    assert D(0x7E) == 448.0 and D(0xFE) == -448.0
+    assert D(0x3F) == 1.875 and D(0x40) == 2.0 and D(0x30) == 0.5
+    assert D(0x08) == 2.0 ** -6 and D(0x01) == 2.0 ** -9 and D(0x07) == 7 * 2.0 ** -9
+    assert np.isnan(D(0x7F)) and np.isnan(D(0xFF))
+    # 126 finite positive magnitudes, strictly increasing with the code
+    vals = [D(c) for c in range(0x00, 0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+
+
+def test_e4m3_every_code_round_trips():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c, hex(c)
+
+
+def test_e4m3_midpoints_round_to_even():
+    """Between neighbouring codes: the exact midpoint goes to the code with an
+    even mantissa, anything off it to the nearer code (both signs)."""
+    D, E = oracle.e4m3_decode, oracle.e4m3_encode
+    for c in range(0x00, 0x7E):
+        lo, hi = D(c), D(c + 1)
+        mid = (lo + hi) / 2  # exact in float32: at most five significant bits
+        assert np.float32(mid) == mid
+        even = c if c % 2 == 0 else c + 1
+        assert E(mid) == even and E(-mid) == even | 0x80, hex(c)
+        assert E(np.nextafter(np.float32(mid), np.float32(0))) == c
+        assert E(np.nextafter(np.float32(mid), np.float32(1e30))) == c + 1
+
+
+def test_e4m3_beyond_the_largest_value():
+    """448 is the largest finite value: the midpoint 464 rounds to it (even
+    mantissa), anything that would round past it is NaN (no infinities).  The
+    row quantiser never produces such values (|x| * 448 / amax <= 448 up to
+    float32 rounding)."""
+    E = oracle.e4m3_encode
+    assert E(448.0) == 0x7E and E(460.0) == 0x7E and E(464.0) == 0x7E
+    assert E(np.nextafter(np.float32(464.0), np.float32(1e30))) == 0x7F
+    assert E(-500.0) == 0xFF and E(1e30) == 0x7F
+
+
+def test_fp8_row_hand_example():
+    """amax = 448: scale 1 and every code is the E4M3 rounding of x itself."""
+    x = _bf16([[448, -1, 0.3, 1.0625, 1.1875, 2.0 ** -10, -3 * 2.0 ** -10, 0]])
+    codes, scales = oracle.quantize_rows_fp8(x)
+    assert scales.tolist() == [1.0]
+    assert codes[0].tolist() == [0x7E, 0xB8, 0x2A, 0x38, 0x3A, 0x00, 0x82, 0x00]
+
+
+@pytest.mark.parametrize("sigma", [1e-3, 1.0, 300.0])
+def test_fp8_properties_random_rows(sigma):
+    g = torch.Generator().manual_seed(91)
+    x = (torch.randn(64, 128, generator=g) * sigma).to(torch.bfloat16)
+    codes, scales = oracle.quantize_rows_fp8(x)
+    xf = x.double().numpy()
+    amax = np.abs(xf).max(axis=1)
+    assert np.array_equal(scales, (amax.astype(np.float32) / np.float32(448)).astype(np.float32))
+    dec = np.vectorize(oracle.e4m3_decode)(codes.astype(np.int64))
+    assert np.all(np.isfinite(dec))
+    # error: half a mantissa step (2^-4 relative) for normals, half the
+    # subnormal step 2^-10 in code units otherwise, plus float32 rounding
+    y = xf * (448.0 / amax[:, None])
+    err = np.abs(dec - y)
+    assert np.all(err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 2.0 ** -20) + np.abs(y) * 2.0 ** -22)
+    # each row's largest |x| encodes as +-448
+    top = codes[np.arange(64), np.abs(xf).argmax(axis=1)]
+    assert np.all((top & 0x7F) == 0x7E)
+    # odd symmetry: -x flips exactly the sign bits
+    cn, sn = oracle.quantize_rows_fp8(-x)
+    assert np.array_equal(sn, scales) and np.array_equal(cn, codes ^ 0x80)
+
+
+def test_fp8_zero_and_tiny_rows():
+    x = torch.zeros(3, 16, dtype=torch.bfloat16)
+    x[1, 3] = 1e-35
+    x[2, :] = -2.0 ** -110
+    codes, scales = oracle.quantize_rows_fp8(x)
+    assert scales.tolist() == [0.0, 0.0, 0.0]
+    assert np.all(codes[0] == 0) and np.all(codes[1] == 0)
+    assert np.all(codes[2] == 0x80)  # x * 0 keeps the sign
+
+
+def test_fp8_cache_image_layout_bruteforce():
+    lengths, HK, D = [3, 1, 5], 2, 32
+    g = torch.Generator().manual_seed(79)
+    N = sum(lengths)
+    k = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(N, HK, D, generator=g).to(torch.bfloat16)
+    cu = [0, 3, 4, 9]
+    kq, ks, vq, vs = oracle.cache_image_fp8(k, v, cu)
+    assert kq.dtype == np.uint8 and kq.shape == (N * HK * D,) and ks.shape == (N * HK,)
+    for b, L in enumerate(lengths):
+        for hk in range(HK):
+            for t in range(L):
+                row = cu[b] * HK + hk * L + t
+                ck, sk = oracle.quantize_rows_fp8(k[cu[b] + t, hk].view(1, D))
+                cv, sv = oracle.quantize_rows_fp8(v[cu[b] + t, hk].view(1, D))
+                assert np.array_equal(kq[row * D:(row + 1) * D], ck[0]) and ks[row] == sk[0]
+                assert np.array_equal(vq[row * D:(row + 1) * D], cv[0]) and vs[row] == sv[0]
+
+
 # ---------------------------------------------------------------- paged cache
 # Paged KV cache ("大模型推理优化：Prefill、Decode与KV Cache的工程实践" §4.2,
 # untitled page www.zwxr.cn/news/300951 §3.4: 16-token blocks, not contiguous,
