@@ -24,7 +24,7 @@ events), cold_launch_us (after a 1 GiB fill that evicts L2 and the Infinity
 Cache), kv_write_standalone_copy (the cache write alone as a plain torch copy),
 gemm_bf16_context (a large hipBLASLt bf16 GEMM at the run's clock),
 gpu_clocks_power (amd-smi before and after the timed steps, when available),
-int8_cache (the same step writing the INT8 cache).  The chunked workloads
+int8_cache and fp8_cache (the same step writing an INT8 or E4M3 cache).  The chunked workloads
 report the heaviest step one-pass, split-KV and paged, the decode rows alone,
 and every step summed (all_steps_splitkv) with the prompt's chunks alone
 against one varlen call over the whole prompt.
@@ -483,6 +483,15 @@ def main():
 
     ms8 = timed_steps(step_int8, args.steps, args.warmup)
 
+    # and an FP8 (E4M3) cache, same layout
+    kf8, vf8 = kq8.view(torch.uint8), vq8.view(torch.uint8)
+
+    def step_fp8():
+        P.prefill_attn_varlen_fp8(qd, kd, vd, cu, kf8, vf8, ks8, vs8, out, scale=w.scale,
+                                  max_seqlen=max_seqlen)
+
+    msf8 = timed_steps(step_fp8, args.steps, args.warmup)
+
     # cold: every launch after a 1 GiB fill that evicts L2 and the Infinity Cache
     cold_ms = cold_launch_times(step, min(args.steps, 100))
     # the cache write on its own, as a plain torch copy of k and v into the
@@ -540,6 +549,10 @@ def main():
                        "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2),
                        "cache_bytes_written": cache8_bytes,
                        "bf16_cache_bytes": kv_bytes},
+        "fp8_cache": {"us_per_step": round(msf8 * 1e3, 2),
+                      "tflops": round(flops / (msf8 * 1e-3) / 1e12, 2),
+                      "cache_bytes_written": cache8_bytes,
+                      "format": "OCP E4M3, one float scale per (token, K/V head)"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -185,6 +185,26 @@ pa_status prefill_attn_varlen_int8(const uint16_t *q, const uint16_t *k, const u
                                    hipStream_t stream);
 
 /*
+ * Varlen prefill writing an FP8 KV cache: as prefill_attn_varlen_int8 with
+ * one-byte codes in the OCP 8-bit E4M3 format [P2 §4.3 lists low-precision
+ * cache formats; the E4M3 encoding is this library's reading]: a sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, no
+ * infinities, S.1111.111 NaN, largest finite magnitude 448.  Per (token, K/V
+ * head) row:
+ *     scale = amax / 448,  code = E4M3(x * (448 / amax)),
+ * the product in float32, the code the nearest E4M3 value with ties to even
+ * (a row whose amax is below 2^-100 gets scale 0 and the codes of x * 0,
+ * zeros that keep x's sign); the value it stands for is E4M3 value * scale.
+ * Layout, scales, arguments and errors as prefill_attn_varlen_int8.
+ */
+pa_status prefill_attn_varlen_fp8(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const int32_t *cu_seqlens, int32_t num_seqs,
+                                  int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, uint8_t *k_cache, uint8_t *v_cache,
+                                  float *k_scale, float *v_scale, uint16_t *out, float scale,
+                                  hipStream_t stream);
+
+/*
  * Split-KV chunked prefill.  Same result and cache writes as
  * prefill_attn_chunked_gqa, computed so that long key ranges do not serialise
  * on one work-group: in a chunked step a prompt chunk is batched with decode

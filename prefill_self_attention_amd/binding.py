@@ -45,6 +45,9 @@ def load() -> ctypes.CDLL:
     lib.prefill_attn_varlen_int8.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p,
                                              ctypes.c_float, p]
     lib.prefill_attn_varlen_int8.restype = ctypes.c_int
+    lib.prefill_attn_varlen_fp8.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, p,
+                                             ctypes.c_float, p]
+    lib.prefill_attn_varlen_fp8.restype = ctypes.c_int
     lib.prefill_attn_chunked_splitkv.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, p, p,
                                                  i32, p, ctypes.c_float, p, p, p, ctypes.c_size_t]
     lib.prefill_attn_chunked_splitkv.restype = ctypes.c_int
@@ -231,6 +234,35 @@ def prefill_attn_chunked_splitkv(q, k, v, cu_seqlens, k_cache, v_cache, out, pre
     return out
 
 
+def _varlen_quant(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_scale, out, scale, max_seqlen,
+                  stream, code_dtype, entry, what):
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(n, t, code_dtype)
+    for n, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(n, t, torch.float32)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    H, HK, D = _heads(q, k, v)
+    N = q.shape[0]
+    if k_cache.numel() < N * HK * D or v_cache.numel() < N * HK * D or \
+            k_scale.numel() < N * HK or v_scale.numel() < N * HK:
+        raise ValueError("%s cache needs N*HK*D codes and N*HK scales per matrix" % what)
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    st = getattr(load(), entry)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+        ctypes.c_float(scale), _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out
+
+
 def prefill_attn_varlen_int8(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_scale, out,
                              scale=None, max_seqlen=None, stream=None):
     """Varlen causal prefill writing an INT8 KV cache (see prefill_attn.h).
@@ -240,30 +272,20 @@ def prefill_attn_varlen_int8(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_s
     of N*HK elements (one scale per token and K/V head).  Returns out.
     """
     import torch
-    for n, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-        _check_tensor(n, t, torch.bfloat16)
-    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _check_tensor(n, t, torch.int8)
-    for n, t in (("k_scale", k_scale), ("v_scale", v_scale)):
-        _check_tensor(n, t, torch.float32)
-    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
-    H, HK, D = _heads(q, k, v)
-    N = q.shape[0]
-    if k_cache.numel() < N * HK * D or v_cache.numel() < N * HK * D or \
-            k_scale.numel() < N * HK or v_scale.numel() < N * HK:
-        raise ValueError("INT8 cache needs N*HK*D codes and N*HK scales per matrix")
-    B = cu_seqlens.shape[0] - 1
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if max_seqlen is None:
-        max_seqlen = _max_seqlen(cu_seqlens)
-    st = load().prefill_attn_varlen_int8(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), H, HK, D,
-        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
-        ctypes.c_float(scale), _stream(stream))
-    if st != PA_OK:
-        raise PrefillAttnError(st)
-    return out
+    return _varlen_quant(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_scale, out, scale, max_seqlen,
+                         stream, torch.int8, "prefill_attn_varlen_int8", "INT8")
+
+
+def prefill_attn_varlen_fp8(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_scale, out,
+                            scale=None, max_seqlen=None, stream=None):
+    """Varlen causal prefill writing an FP8 (E4M3) KV cache (see prefill_attn.h).
+
+    As prefill_attn_varlen_int8 with uint8 code tensors holding E4M3 bytes.
+    Returns out.
+    """
+    import torch
+    return _varlen_quant(q, k, v, cu_seqlens, k_cache, v_cache, k_scale, v_scale, out, scale, max_seqlen,
+                         stream, torch.uint8, "prefill_attn_varlen_fp8", "FP8")
 
 
 def prefill_attn_chunked_splitkv_paged(q, k, v, cu_seqlens, k_cache, v_cache, block_table, out,

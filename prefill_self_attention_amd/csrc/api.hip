@@ -117,18 +117,21 @@ pa_status check_block_table(const int32_t* cu, const int32_t* prefix, int32_t nu
   return PA_OK;
 }
 
-struct Int8Cache {
-  int8_t* kq;
-  int8_t* vq;
+// a quantised varlen cache: one-byte codes laid out as the bf16 cache, one
+// float scale per (token, K/V head) row
+struct QuantCache {
+  void* kq;
+  void* vq;
   float* ks;
   float* vs;
+  bool fp8;  // E4M3 codes; otherwise INT8
 };
 
 pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
               int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
               int32_t head_dim, uint16_t* kc, uint16_t* vc, int32_t cap, uint16_t* out,
               float scale, hipStream_t stream, const int32_t* prefix,
-              const Int8Cache* i8 = nullptr) {
+              const QuantCache* qc = nullptr) {
   if (num_kv_heads < 1 || num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   int nqb = 0;
   pa_status st = check_grid(num_seqs, max_seqlen, num_heads, &nqb);
@@ -159,12 +162,13 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634, 0x1p-100);
   p.neg_q = scale < 0.f ? 1 : 0;
   hipError_t e;
-  if (i8) {
-    p.kq = i8->kq;
-    p.vq = i8->vq;
-    p.ks = i8->ks;
-    p.vs = i8->vs;
-    e = pa::launch_prefill_fwd_int8(p, num_seqs, head_dim, stream);
+  if (qc) {
+    p.kq = static_cast<int8_t*>(qc->kq);
+    p.vq = static_cast<int8_t*>(qc->vq);
+    p.ks = qc->ks;
+    p.vs = qc->vs;
+    e = qc->fp8 ? pa::launch_prefill_fwd_fp8(p, num_seqs, head_dim, stream)
+                : pa::launch_prefill_fwd_int8(p, num_seqs, head_dim, stream);
   } else {
     e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
   }
@@ -383,17 +387,18 @@ pa_status prefill_attn_chunked_gqa(const uint16_t* q, const uint16_t* k, const u
              k_cache, v_cache, cache_capacity, out, scale, stream, prefix_lens);
 }
 
-pa_status prefill_attn_varlen_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const int32_t* cu_seqlens, int32_t num_seqs,
-                                   int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
-                                   int32_t head_dim, int8_t* k_cache, int8_t* v_cache,
-                                   float* k_scale, float* v_scale, uint16_t* out, float scale,
-                                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+pa_status quant_run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens,
+                    int32_t num_seqs, int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                    uint16_t* out, float scale, hipStream_t stream, bool fp8) {
   if (!k_scale || !v_scale) return PA_ERR_NULL;
   // the bf16 checks cover q, k, v, cu, out and the code buffers
   pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
-                              reinterpret_cast<const uint16_t*>(k_cache),
-                              reinterpret_cast<const uint16_t*>(v_cache), out, scale);
+                              static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                              out, scale);
   if (st != PA_OK) return st;
   if (!aligned16(k_scale) || !aligned16(v_scale)) return PA_ERR_ALIGN;
   const void* outs[5] = {k_cache, v_cache, out, k_scale, v_scale};
@@ -404,9 +409,32 @@ pa_status prefill_attn_varlen_int8(const uint16_t* q, const uint16_t* k, const u
     for (int j = i + 1; j < 5; ++j)
       if (outs[i] == outs[j]) return PA_ERR_ALIAS;
   }
-  const Int8Cache i8{k_cache, v_cache, k_scale, v_scale};
+  const QuantCache qc{k_cache, v_cache, k_scale, v_scale, fp8};
   return run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_kv_heads, head_dim,
-             nullptr, nullptr, 0, out, scale, stream, nullptr, &i8);
+             nullptr, nullptr, 0, out, scale, stream, nullptr, &qc);
+}
+}  // namespace
+
+extern "C" {
+
+pa_status prefill_attn_varlen_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int8_t* k_cache, int8_t* v_cache,
+                                   float* k_scale, float* v_scale, uint16_t* out, float scale,
+                                   hipStream_t stream) {
+  return quant_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_kv_heads, head_dim, k_cache,
+                   v_cache, k_scale, v_scale, out, scale, stream, false);
+}
+
+pa_status prefill_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_seqlens, int32_t num_seqs,
+                                  int32_t max_seqlen, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, uint8_t* k_cache, uint8_t* v_cache,
+                                  float* k_scale, float* v_scale, uint16_t* out, float scale,
+                                  hipStream_t stream) {
+  return quant_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, num_kv_heads, head_dim, k_cache,
+                   v_cache, k_scale, v_scale, out, scale, stream, true);
 }
 
 pa_status prefill_attn_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -56,7 +56,8 @@ int fwd_grid_blocks(int max_seqlen);
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream);
-// Varlen with an INT8 cache (kq, vq, ks, vs instead of kc, vc).
+// Varlen with an INT8 or an FP8 (E4M3) cache (kq, vq, ks, vs instead of kc, vc).
+hipError_t launch_prefill_fwd_fp8(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,
                                    hipStream_t stream);
 

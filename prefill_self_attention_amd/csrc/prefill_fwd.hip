@@ -208,6 +208,30 @@ __device__ __forceinline__ u32x2_t quantize8(const u32x4_t w, float amax) {
   return r;
 }
 
+// FP8 rows: the OCP 8-bit E4M3 format (sign, 4 exponent bits with bias 7, 3
+// mantissa bits, subnormals, no infinities, largest finite 448), one float
+// scale per row as for INT8: scale = amax / 448, code = E4M3(x * (448 /
+// amax)), the product in float32 and the conversion rounding to nearest with
+// ties to even (v_cvt_pk_fp8_f32 on this part); rows with amax < 2^-100 get
+// scale 0 and the codes of x * 0 (zeros keeping x's sign).
+__device__ __forceinline__ float fp8_scale(float amax) { return amax >= kInt8MinAmax ? amax / 448.0f : 0.0f; }
+__device__ __forceinline__ u32x2_t quantize_fp8(const u32x4_t w, float amax) {
+  const float inv = amax >= kInt8MinAmax ? 448.0f / amax : 0.0f;
+  u32x2_t r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w[2 * i]) * inv, bf16_hi(w[2 * i]) * inv, 0, false);
+    r[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w[2 * i + 1]) * inv, bf16_hi(w[2 * i + 1]) * inv, lo,
+                                                     true);
+  }
+  return r;
+}
+
+// cache formats of the varlen kernel's cache write
+constexpr int kCacheBf16 = 0;
+constexpr int kCacheInt8 = 1;
+constexpr int kCacheFp8 = 2;
+
 template <int D>
 struct Cfg {
   static constexpr int kCpr = D / 8;                    // 16-byte chunks per row
@@ -297,7 +321,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // one of the nseg segments of its keys.  A block with one segment is stored
 // as usual; otherwise its rows get a partial result (normalised O in fp32 and
 // log2 of its sum of weights), merged by a later pass.
-template <int D, bool kChunked, bool kSplit, bool kInt8 = false, bool kPaged = false>
+template <int D, bool kChunked, bool kSplit, int kCache = kCacheBf16, bool kPaged = false>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z, int seg, int nseg) {
   using C = Cfg<D>;
   // Every LDS read in the main loop is inline asm (lds_read_* above), so the
@@ -501,17 +525,22 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
       const int row = idx / C::kCpr, ch = idx % C::kCpr;
       const int kp = t0 + row;
       const bool mine = kp >= blk.own_lo && kp < blk.key_end;
-      if constexpr (kInt8) {
+      if constexpr (kCache != kCacheBf16) {
         // the row's absolute maximum over its kCpr lanes (all lanes take part)
         const float ka = group_max<C::kCpr>(absmax8(kr[i]));
         const float va = group_max<C::kCpr>(absmax8(vr[i]));
         if (mine) {
           const int64_t dst = cache_base + (int64_t)kp * D + 8 * ch;
-          __builtin_nontemporal_store(quantize8(kr[i], ka), (u32x2_t*)(p.kq + dst));
-          __builtin_nontemporal_store(quantize8(vr[i], va), (u32x2_t*)(p.vq + dst));
+          if constexpr (kCache == kCacheInt8) {
+            __builtin_nontemporal_store(quantize8(kr[i], ka), (u32x2_t*)(p.kq + dst));
+            __builtin_nontemporal_store(quantize8(vr[i], va), (u32x2_t*)(p.vq + dst));
+          } else {
+            __builtin_nontemporal_store(quantize_fp8(kr[i], ka), (u32x2_t*)(p.kq + dst));
+            __builtin_nontemporal_store(quantize_fp8(vr[i], va), (u32x2_t*)(p.vq + dst));
+          }
           if (ch == 0) {
-            p.ks[cache_base / D + kp] = int8_scale(ka);
-            p.vs[cache_base / D + kp] = int8_scale(va);
+            p.ks[cache_base / D + kp] = kCache == kCacheInt8 ? int8_scale(ka) : fp8_scale(ka);
+            p.vs[cache_base / D + kp] = kCache == kCacheInt8 ? int8_scale(va) : fp8_scale(va);
           }
         }
       } else if (mine) {
@@ -888,12 +917,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z
   }
 }
 
-template <int D, bool kChunked, bool kInt8 = false>
+template <int D, bool kChunked, int kCache = kCacheBf16>
 __global__ __launch_bounds__(kThreads)
 void prefill_fwd_kernel(FwdParams p) {
   // raw id builtins: the device library's id helpers are built with IEEE mode
   // on and would not inline into this IEEE-off kernel
-  fwd_item<D, kChunked, false, kInt8>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
+  fwd_item<D, kChunked, false, kCache>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
                                       __builtin_amdgcn_workgroup_id_z(), 0, 1);
 }
 
@@ -922,16 +951,26 @@ hipError_t launch_d(const FwdParams& p, int num_seqs, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,
-                                   hipStream_t stream) {
+namespace {
+template <int kCache>
+hipError_t launch_quant(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream) {
   const dim3 grid(p.num_heads, num_seqs, p.grid_z);
   switch (head_dim) {
-    case 32: hipLaunchKernelGGL((prefill_fwd_kernel<32, false, true>), grid, dim3(kThreads), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((prefill_fwd_kernel<64, false, true>), grid, dim3(kThreads), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((prefill_fwd_kernel<128, false, true>), grid, dim3(kThreads), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((prefill_fwd_kernel<32, false, kCache>), grid, dim3(kThreads), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((prefill_fwd_kernel<64, false, kCache>), grid, dim3(kThreads), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((prefill_fwd_kernel<128, false, kCache>), grid, dim3(kThreads), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream) {
+  return launch_quant<kCacheInt8>(p, num_seqs, head_dim, stream);
+}
+
+hipError_t launch_prefill_fwd_fp8(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream) {
+  return launch_quant<kCacheFp8>(p, num_seqs, head_dim, stream);
 }
 
 template <int D>

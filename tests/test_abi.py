@@ -33,6 +33,7 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "prefill_attn_varlen", "prefill_attn_chunked", "prefill_attn_varlen_gqa",
         "prefill_attn_chunked_gqa", "prefill_attn_chunked_splitkv", "prefill_attn_varlen_int8",
+        "prefill_attn_varlen_fp8",
         "prefill_attn_chunked_splitkv_paged",
         "prefill_attn_splitkv_workspace_size", "pa_status_string", "pa_set_check_mode",
         "pa_last_hip_error"])
@@ -91,17 +92,26 @@ def varlen_int8(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64,
                                         kc, vc, ks, vs, out, ctypes.c_float(scale), None)
 
 
-def test_int8_rejections(lib):
-    assert varlen_int8(lib, ks=None) == 1
-    assert varlen_int8(lib, vs=None) == 1
-    assert varlen_int8(lib, ks=A[7] + 4) == 5
-    assert varlen_int8(lib, vs=A[6]) == 6     # scale buffer is out
-    assert varlen_int8(lib, ks=A[0]) == 6     # scale buffer is q
-    assert varlen_int8(lib, HK=3) == 2
-    assert varlen_int8(lib, B=0) == 0 and varlen_int8(lib, maxlen=0) == 0
+def varlen_fp8(lib, q=A[0], k=A[1], v=A[2], cu=A[3], B=1, maxlen=16, H=2, D=64, kc=A[4],
+               vc=A[5], out=A[6], scale=0.125, ks=A[7], vs=A[8], HK=None):
+    return lib.prefill_attn_varlen_fp8(q, k, v, cu, B, maxlen, H, H if HK is None else HK, D,
+                                       kc, vc, ks, vs, out, ctypes.c_float(scale), None)
 
 
-@pytest.mark.parametrize("f", [varlen, chunked, splitkv, varlen_int8])
+@pytest.mark.parametrize("f", [varlen_int8, varlen_fp8])
+def test_quantised_cache_rejections(lib, f):
+    assert f(lib, ks=None) == 1
+    assert f(lib, vs=None) == 1
+    assert f(lib, ks=A[7] + 4) == 5
+    assert f(lib, vs=A[6]) == 6     # scale buffer is out
+    assert f(lib, ks=A[0]) == 6     # scale buffer is q
+    assert f(lib, kc=A[5]) == 6     # both code buffers the same
+    assert f(lib, HK=3) == 2
+    assert f(lib, D=48) == 3
+    assert f(lib, B=0) == 0 and f(lib, maxlen=0) == 0
+
+
+@pytest.mark.parametrize("f", [varlen, chunked, splitkv, varlen_int8, varlen_fp8])
 def test_host_rejections(lib, f):
     assert f(lib, q=None) == 1
     assert f(lib, out=None) == 1

@@ -34,7 +34,7 @@ def P():
 
 def make_problem(seed):
     """A varlen batch, a chunked batch (a chunk, decode rows) with its slab
-    cache, and the INT8 buffers, all on the device."""
+    cache, all on the device."""
     H, HK, D = 8, 2, 128
     g = I.generator(seed)
     lengths = [300, 1, 77, 1, 129]
@@ -70,6 +70,13 @@ def run_all(pb, ws):
     vs = torch.empty_like(ks)
     m.prefill_attn_varlen_int8(pb["q"], pb["k"], pb["v"], pb["cu"], kq, vq, ks, vs, out, max_seqlen=pb["max_len"])
     res["int8"] = (out, kq, vq, ks, vs)
+    out = torch.empty_like(pb["q"])
+    kf = torch.empty(N * HK * D, dtype=torch.uint8, device="cuda")
+    vf = torch.empty_like(kf)
+    ks = torch.empty(N * HK, dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    m.prefill_attn_varlen_fp8(pb["q"], pb["k"], pb["v"], pb["cu"], kf, vf, ks, vs, out, max_seqlen=pb["max_len"])
+    res["fp8"] = (out, kf, vf, ks, vs)
     out = torch.empty_like(pb["q"])
     kc, vc = pb["kc0"].clone(), pb["vc0"].clone()
     m.prefill_attn_chunked(pb["q"], pb["k"], pb["v"], pb["cu"], kc, vc, out, pb["pre"], max_seqlen=pb["max_len"])

@@ -1,6 +1,6 @@
 """Randomised GPU parity sweep: small batches with random lengths, prefixes,
 head groupings, head sizes and scales through every entry point of the C ABI
-(varlen, INT8-cache varlen, one-pass chunked, split-KV chunked over a slab
+(varlen, INT8- and FP8-cache varlen, one-pass chunked, split-KV chunked over a slab
 and over a paged pool), each against the float64 oracle: outputs to the
 parity bar of tests/gpu_util.py, caches bit for bit.  Seeded, so a failure
 names its case and reproduces."""
@@ -152,5 +152,16 @@ def test_random_varlen_paths(i):
     rk, rks, rv, rvs = oracle.cache_image_int8(k, v, cu)
     np.testing.assert_array_equal(kq.cpu().numpy(), rk)
     np.testing.assert_array_equal(vq.cpu().numpy(), rv)
+    np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    np.testing.assert_array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+
+    kf, vf = kq.view(torch.uint8), vq.view(torch.uint8)
+    out = torch.empty_like(qd)
+    P().prefill_attn_varlen_fp8(qd, kd, vd, cud, kf, vf, ks, vs, out, scale=c["scale"])
+    torch.cuda.synchronize()
+    assert_close(out, ref, "case %d varlen FP8" % i)
+    rk, rks, rv, rvs = oracle.cache_image_fp8(k, v, cu)
+    np.testing.assert_array_equal(kf.cpu().numpy(), rk)
+    np.testing.assert_array_equal(vf.cpu().numpy(), rv)
     np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
     np.testing.assert_array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
