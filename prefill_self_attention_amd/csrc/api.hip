@@ -3,6 +3,7 @@
 // Every step of the computation runs in the kernels of prefill_fwd.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -180,11 +181,24 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
 // work-groups per unit, queried once per device and head size.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
-std::atomic<int> g_split_occ[kMaxDevices][3];
+std::atomic<int> g_split_occ[kMaxDevices][3][2];
 std::atomic<int> g_dec_occ[kMaxDevices][3][4][2];
+// Share of the split-KV work-groups that starts on the attention items (the
+// rest start on the decode rows' units).
+constexpr int kItemsFirstPercent = 50;
+constexpr int kFuseMaxHeads = 2;
+constexpr bool kFusePaged = false;
 
-pa_status split_grid(int head_dim, int heads_per_unit, bool paged, int* fwd_grid, int* dec_grid,
-                     int* merge_grid) {
+// Whether the decode rows run inside the split attention launch.  There they
+// run beside the items, but with 8 waves per compute unit instead of 16; that
+// pays where a row's unit streams K/V (one query head per K/V head) and
+// costs where it computes (grouped heads: 4 or 8 query heads per load).
+bool fuse_decode(int heads_per_unit, bool paged) { return heads_per_unit <= kFuseMaxHeads && (kFusePaged || !paged); }
+
+// Work-groups of the split-KV attention launch (resident ones only: it is
+// persistent), the share of them that starts on the attention items when the
+// decode rows run in the same launch, and the merge grid.
+pa_status split_grid(int head_dim, bool fused, int* fwd_grid, int* items_first, int* merge_grid) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -196,22 +210,36 @@ pa_status split_grid(int head_dim, int heads_per_unit, bool paged, int* fwd_grid
     g_cus[dev].store(cus, std::memory_order_relaxed);
   }
   const int di = head_dim == 32 ? 0 : head_dim == 64 ? 1 : 2;
-  int occ = g_split_occ[dev][di].load(std::memory_order_relaxed);
+  int occ = g_split_occ[dev][di][fused].load(std::memory_order_relaxed);
   if (occ <= 0) {
-    occ = pa::fwd_split_blocks_per_cu(head_dim);
+    occ = pa::fwd_split_blocks_per_cu(head_dim, fused);
     if (occ <= 0) return hip_fail(hipErrorInvalidConfiguration);
-    g_split_occ[dev][di].store(occ, std::memory_order_relaxed);
-  }
-  const int gi = heads_per_unit == 1 ? 0 : heads_per_unit == 2 ? 1 : heads_per_unit == 4 ? 2 : 3;
-  int docc = g_dec_occ[dev][di][gi][paged].load(std::memory_order_relaxed);
-  if (docc <= 0) {
-    docc = pa::splitkv_decode_blocks_per_cu(head_dim, heads_per_unit, paged);
-    if (docc <= 0) return hip_fail(hipErrorInvalidConfiguration);
-    g_dec_occ[dev][di][gi][paged].store(docc, std::memory_order_relaxed);
+    g_split_occ[dev][di][fused].store(occ, std::memory_order_relaxed);
   }
   *fwd_grid = cus * occ;
-  *dec_grid = cus * docc;
+  // a multiple of 8: every XCD the same number
+  *items_first = std::min(*fwd_grid, std::max(8, *fwd_grid * kItemsFirstPercent / 100 / 8 * 8));
   *merge_grid = cus * 8;
+  return PA_OK;
+}
+
+// Work-groups of the separate decode launch: all resident ones.
+pa_status decode_grid(int head_dim, int heads_per_unit, bool paged, int* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  const int cus = g_cus[dev].load(std::memory_order_relaxed);  // set by split_grid
+  if (cus <= 0) return hip_fail(hipErrorInvalidConfiguration);
+  const int di = head_dim == 32 ? 0 : head_dim == 64 ? 1 : 2;
+  const int gi = heads_per_unit == 1 ? 0 : heads_per_unit == 2 ? 1 : heads_per_unit == 4 ? 2 : 3;
+  int occ = g_dec_occ[dev][di][gi][paged].load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    occ = pa::splitkv_decode_blocks_per_cu(head_dim, heads_per_unit, paged);
+    if (occ <= 0) return hip_fail(hipErrorInvalidConfiguration);
+    g_dec_occ[dev][di][gi][paged].store(occ, std::memory_order_relaxed);
+  }
+  *grid = cus * occ;
   return PA_OK;
 }
 
@@ -280,10 +308,15 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (e != hipSuccess) return hip_fail(e);
     if (last > num_tokens) return PA_ERR_SEQLENS;
   }
-  const int gc = pa::splitkv_heads_per_unit(num_heads, num_kv_heads);
   const bool paged = block_table != nullptr;
-  int fwd_grid = 0, dec_grid = 0, merge_grid = 0;
-  st = split_grid(head_dim, gc, paged, &fwd_grid, &dec_grid, &merge_grid);
+  const int gc = pa::splitkv_heads_per_unit(num_heads, num_kv_heads);
+  // only a batch that may hold both multi-token blocks and length-1 rows
+  // gains from running them together (one lone sequence, or rows of length
+  // at most 1, leave one kind of work empty)
+  const bool fused = fuse_decode(gc, paged) && num_seqs > 1 && max_seqlen > 1;
+  int fwd_grid = 0, items_first = 0, merge_grid = 0, dec_grid = 0;
+  st = split_grid(head_dim, fused, &fwd_grid, &items_first, &merge_grid);
+  if (st == PA_OK && !fused) st = decode_grid(head_dim, gc, paged, &dec_grid);
   if (st != PA_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
@@ -310,12 +343,17 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.max_segs = L.max_segs;
   p.split_grid = fwd_grid;
   p.dec_items = reinterpret_cast<const int4*>(ws + L.off_dec);
+  p.dec_heads = gc;
+  p.fuse_decode = fused ? 1 : 0;
+  p.items_first = fused ? items_first : fwd_grid;
+  p.counters = reinterpret_cast<unsigned long long*>(ws + L.off_ctr);
   p.dec_grid = dec_grid;
   p.block_table = block_table;
   p.bt_stride = max_blocks_per_seq;
-  hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, ws, stream);
+  hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L,
+                                         fused ? 4 : 1, ws, stream);
   if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, paged, stream);
-  if (e == hipSuccess) e = pa::launch_splitkv_decode(p, head_dim, gc, paged, stream);
+  if (e == hipSuccess && !fused) e = pa::launch_splitkv_decode(p, head_dim, paged, stream);
   if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
   if (e != hipSuccess) return hip_fail(e);
   return PA_OK;

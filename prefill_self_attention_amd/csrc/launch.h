@@ -33,7 +33,11 @@ struct FwdParams {
   int32_t max_segs;         // segments per block, at most
   int32_t split_grid;       // work-groups of the persistent split-KV launch
   const int4* dec_items;    // decode-row items: {sequence, segment, segments, 0}; hdr[2] of them
-  int32_t dec_grid;         // work-groups of the persistent decode launch
+  int32_t dec_heads;        // query heads per decode unit (1, 2, 4 or 8)
+  int32_t fuse_decode;      // 1: the split attention launch also runs the decode units
+  int32_t items_first;      // fused: work-groups [0, items_first) start on the items, the rest on decode units
+  unsigned long long* counters;  // kSplitCounters work counters, zeroed by the plan
+  int32_t dec_grid;         // work-groups of the separate decode launch (fuse_decode == 0)
   // INT8 cache (varlen only): codes in kq/vq laid out as kc/vc, one float
   // scale per (token, K/V head) row in ks/vs (the cache layout without D)
   int8_t* kq;
@@ -48,6 +52,7 @@ struct FwdParams {
 };
 
 constexpr int kPageRows = 16;  // tokens per cache block
+constexpr int kSplitCounters = 9;  // item queues of the 8 XCDs, then the decode units
 
 // Query rows per block, and work-groups per (head, sequence) for a maximum length.
 int fwd_block_rows();
@@ -70,28 +75,32 @@ struct SplitLayout {
   int64_t max_blocks;    // bound on the query blocks of the batch: N / 128 + B + 1
   int64_t max_items;     // max_blocks * max_segs
   int64_t max_dec_items; // num_seqs * max_segs
-  size_t off_hdr, off_items, off_dec, off_merges, off_lse, off_o, bytes;
+  size_t off_hdr, off_ctr, off_items, off_dec, off_merges, off_lse, off_o, bytes;
 };
 SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                          int32_t head_dim, int32_t cap);
 
-// Plan (one work-group): item list, merge list and their counts in the
-// workspace.  Then the persistent attention pass over the items, then the
-// merge of blocks with more than one segment.
+// Plan (one work-group): item list, decode list, merge list and their counts
+// in the workspace, work counters zeroed.  Then the persistent pass over the
+// items and the decode rows' units (both in one launch), then the merge of
+// blocks with more than one segment.
+// dec_seg_mult: a decode row's segments hold about dec_seg_mult * seg_tiles
+// tiles (longer ones when the rows run inside the attention launch).
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
-                               int32_t num_tokens, const SplitLayout& L, void* ws,
+                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult, void* ws,
                                hipStream_t stream);
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
                                 int head_dim, int grid, hipStream_t stream);
-// Length-1 rows of the split-KV call: a memory-bound pass over their
-// segments; `heads_per_unit` query heads (1, 2, 4 or 8, dividing
-// num_heads / num_kv_heads) share each load of a K/V row.
-hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit, bool paged,
-                                 hipStream_t stream);
-int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit, bool paged);
+// Query heads per decode unit of the length-1 rows: 1, 2, 4 or 8, dividing
+// num_heads / num_kv_heads; they share each load of a K/V row.
 int splitkv_heads_per_unit(int num_heads, int num_kv_heads);
-// Resident work-groups per compute unit of the split attention kernel (0 on error).
-int fwd_split_blocks_per_cu(int head_dim);  // same for the paged variant
+// The length-1 rows in a launch of their own (when fuse_decode is 0), and
+// its resident work-groups per compute unit.
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, bool paged, hipStream_t stream);
+int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit, bool paged);
+// Resident work-groups per compute unit of the split attention kernel, with
+// (fused) or without the decode rows (0 on error; the paged variants alike).
+int fwd_split_blocks_per_cu(int head_dim, bool fused);
 
 }  // namespace pa

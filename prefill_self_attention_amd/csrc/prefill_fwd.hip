@@ -71,6 +71,7 @@
 
 #include <type_traits>
 
+#include "decode_rows.h"
 #include "launch.h"
 
 namespace pa {
@@ -315,19 +316,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// The work-group's LDS: K/V tile buffers, then the merge buffers; the
+// split-KV kernel's decode units reuse it for their reductions.  One array
+// per fwd_item instantiation (kTag tells apart two kernels that run the same
+// item), so each is used by one kernel only and keeps a fixed LDS address.
+template <int D, bool kChunked, bool kSplit, int kCache, bool kPaged, int kTag>
+__device__ __forceinline__ auto fwd_lds() -> uint8_t (&)[Cfg<D>::kLdsBytes] {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg<D>::kLdsBytes];
+  return lds;
+}
+
 // One work item of a work-group: head h of sequence b, and either the pair of
 // query blocks (z, n-1-z) over all their keys or, in split mode (kSplit), the
 // single block z over key tiles [seg * seg_tiles, (seg + 1) * seg_tiles) --
 // one of the nseg segments of its keys.  A block with one segment is stored
 // as usual; otherwise its rows get a partial result (normalised O in fp32 and
 // log2 of its sum of weights), merged by a later pass.
-template <int D, bool kChunked, bool kSplit, int kCache = kCacheBf16, bool kPaged = false>
+template <int D, bool kChunked, bool kSplit, int kCache = kCacheBf16, bool kPaged = false, int kTag = 0>
 __device__ __forceinline__ void fwd_item(const FwdParams& p, int h, int b, int z, int seg, int nseg) {
   using C = Cfg<D>;
   // Every LDS read in the main loop is inline asm (lds_read_* above), so the
   // compiler places no wait for the direct loads in flight; each read is made
   // valid by an explicit lgkmcnt wait tied to its registers.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLdsBytes];
+  uint8_t (&lds)[C::kLdsBytes] = fwd_lds<D, kChunked, kSplit, kCache, kPaged, kTag>();
   const int64_t H = p.num_heads;
 
   const int seq_start = p.cu[b];
@@ -929,6 +940,7 @@ void prefill_fwd_kernel(FwdParams p) {
 // Split-KV chunked prefill: a persistent grid walks the planned items, item i
 // of head h being step i * H + h; with the grid a multiple of H (and of the 8
 // XCDs) a work-group keeps one head, and all of a head's items run on one XCD.
+// The decode rows then run in a launch of their own (splitkv.hip).
 template <int D, bool kPaged>
 __global__ __launch_bounds__(kThreads)
 void prefill_fwd_split_kernel(FwdParams p) {
@@ -937,8 +949,103 @@ void prefill_fwd_split_kernel(FwdParams p) {
   const int grid = p.split_grid;
   for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += grid) {
     const int4 it = p.items[g / H];
-    fwd_item<D, true, true, false, kPaged>(p, (int)(g % H), it.x, it.y, it.z, it.w);
+    fwd_item<D, true, true, kCacheBf16, kPaged>(p, (int)(g % H), it.x, it.y, it.z, it.w);
     __syncthreads();  // the next item's first loads reuse the merge buffers
+  }
+}
+
+// Split-KV chunked prefill with the decode rows in the same launch, so that
+// both kinds of planned work run at once.  The attention items (a query
+// block over one segment of its keys) are MFMA-bound; the decode units
+// (length-1 rows, decode_rows.h) are HBM-bound ["大模型 Prompt Prefill 阶段的高效
+// Batching 与算子排布" §3: a chunk runs beside decode rows in one step].
+// Work-groups [0, items_first) start on the items and the rest on the decode
+// units, so the matrix cores and the memory stream are busy together; a
+// work-group whose list runs dry joins the other.  Item step j of head h is
+// queued on XCD h % 8 and a work-group (on XCD w % 8 for work-group w) drains
+// its own XCD's queue first, so the query blocks of one head that read the
+// same K/V tiles share an L2.  Each work-group's first item or unit is fixed
+// by its number; the rest are handed out through counters the plan zeroed
+// (item j of queue x is R_x + counter x, R_x the work-groups of XCD x that
+// start on the items; decode unit g is U + counter 8, U the work-groups that
+// start on the units).  With no decode units all work-groups start on the
+// items, with no items all on the units.
+template <int D, bool kPaged>
+__global__ __launch_bounds__(kThreads)
+void prefill_fwd_mixed_kernel(FwdParams p) {
+  __shared__ unsigned long long taken;
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int wg = __builtin_amdgcn_workgroup_id_x();
+  const int H = p.num_heads;
+  const unsigned long long items = (uint32_t)p.hdr[0];
+  const unsigned long long units = (unsigned long long)(uint32_t)p.hdr[2] * (uint32_t)(H / p.dec_heads);
+  const int first = units == 0 ? p.split_grid : items == 0 ? 0 : p.items_first;  // work-groups starting on items
+  auto R = [&](int x) __attribute__((always_inline)) { return (unsigned long long)(uint32_t)((first - x + 7) / 8); };
+  const unsigned long long U = (uint32_t)(p.split_grid - first);
+  // base + the next value of counter i, the same in every wave, or `end` once
+  // base + counter has reached end.  The counter is read first: once a list
+  // is empty every work-group asks at about the same time, and loads do not
+  // queue behind each other at the L2 as read-modify-writes of one address do.
+  auto take = [&](int i, unsigned long long base, unsigned long long end) __attribute__((always_inline)) {
+    if (base >= end) return end;  // all of this list is handed out by number
+    if (tid == 0) {
+      unsigned long long c = __hip_atomic_load(p.counters + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (base + c < end) c = atomicAdd(p.counters + i, 1ull);
+      taken = base + c < end ? base + c : end;
+    }
+    __syncthreads();
+    const unsigned long long v = taken;
+    __syncthreads();  // taken is rewritten by the next call
+    return v;
+  };
+  // the items of queue x until it is empty, starting with the work-group's
+  // own if `own`
+  auto drain = [&](int x, bool own) __attribute__((always_inline)) {
+    const int nh = (H - x + 7) / 8;  // heads h = x (mod 8)
+    const unsigned long long end = items * nh;
+    for (unsigned long long j = own ? (uint32_t)wg / 8 : take(x, R(x), end); j < end; j = take(x, R(x), end)) {
+      const int4 it = p.items[j / nh];
+      fwd_item<D, true, true, kCacheBf16, kPaged, 1>(p, x + 8 * (int)(j % nh), it.x, it.y, it.z, it.w);
+      __syncthreads();  // the next item's first loads reuse the merge buffers
+    }
+  };
+  float* const red = reinterpret_cast<float*>(fwd_lds<D, true, true, kCacheBf16, kPaged, 1>());
+  static_assert(dec::red_floats<D, 8, kWaves>() * 4 <= Cfg<D>::kLdsBytes, "decode reduction exceeds LDS");
+  const bool items_first = wg < first;
+  for (int phase = 0; phase < 2; ++phase) {
+    if ((phase == 0) == items_first) {
+      // this XCD's queue, then the others that still hold items (all eight
+      // probed in one round trip once the own queue is empty)
+      uint32_t open = 1u << (wg & 7);
+      for (int i = 0; i < 8; ++i) {
+        if (i == 1) {
+          if (tid < 8) {
+            const int nh = (H - tid + 7) / 8;
+            const bool more = R(tid) + __hip_atomic_load(p.counters + tid, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT) < items * nh;
+            const unsigned long long mask = __ballot(more);
+            if (tid == 0) taken = mask;
+          }
+          __syncthreads();
+          open = (uint32_t)taken;
+          __syncthreads();
+        }
+        const int x = (wg + i) & 7;
+        if ((open >> x) & 1u) drain(x, phase == 0 && i == 0);
+      }
+    } else if (units > 0) {
+      // each unit takes the next unit's number while it runs
+      unsigned long long* const ctr = p.counters + 8;
+      for (unsigned long long g = phase == 0 ? (uint32_t)(wg - first) : take(8, U, units); g < units; g = U + taken) {
+        switch (p.dec_heads) {
+          case 1: dec::decode_unit<D, 1, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
+          case 2: dec::decode_unit<D, 2, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
+          case 4: dec::decode_unit<D, 4, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
+          default: dec::decode_unit<D, 8, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
+        }
+      }
+      __syncthreads();  // every wave has read taken before take() rewrites it
+    }
   }
 }
 
@@ -975,10 +1082,18 @@ hipError_t launch_prefill_fwd_fp8(const FwdParams& p, int num_seqs, int head_dim
 
 template <int D>
 void split_d(const FwdParams& p, bool paged, hipStream_t stream) {
-  if (paged)
-    hipLaunchKernelGGL((prefill_fwd_split_kernel<D, true>), dim3(p.split_grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((prefill_fwd_split_kernel<D, false>), dim3(p.split_grid), dim3(kThreads), 0, stream, p);
+  const dim3 grid(p.split_grid), block(kThreads);
+  if (p.fuse_decode) {
+    if (paged)
+      hipLaunchKernelGGL((prefill_fwd_mixed_kernel<D, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_fwd_mixed_kernel<D, false>), grid, block, 0, stream, p);
+  } else {
+    if (paged)
+      hipLaunchKernelGGL((prefill_fwd_split_kernel<D, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_fwd_split_kernel<D, false>), grid, block, 0, stream, p);
+  }
 }
 
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream) {
@@ -991,16 +1106,22 @@ hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged
   return hipGetLastError();
 }
 
-int fwd_split_blocks_per_cu(int head_dim) {
+template <int D>
+int split_occ(bool fused) {
   int n = 0;
-  hipError_t e = hipErrorInvalidValue;
-  switch (head_dim) {
-    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<32, false>, kThreads, 0); break;
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<64, false>, kThreads, 0); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<128, false>, kThreads, 0); break;
-    default: break;
-  }
+  const hipError_t e =
+      fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_mixed_kernel<D, false>, kThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_fwd_split_kernel<D, false>, kThreads, 0);
   return e == hipSuccess ? n : 0;
+}
+
+int fwd_split_blocks_per_cu(int head_dim, bool fused) {
+  switch (head_dim) {
+    case 32: return split_occ<32>(fused);
+    case 64: return split_occ<64>(fused);
+    case 128: return split_occ<128>(fused);
+    default: return 0;
+  }
 }
 
 int fwd_block_rows() { return kBM; }

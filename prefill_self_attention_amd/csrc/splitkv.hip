@@ -1,7 +1,7 @@
 // splitkv.hip -- split-KV chunked prefill: the plan that cuts every query
 // block's keys into segments, and the log-sum-exp merge of the segments'
-// partial results.  The attention over each segment runs in
-// prefill_fwd_split_kernel (prefill_fwd.hip).
+// partial results.  The attention over each segment, and the length-1 rows,
+// run in prefill_fwd_split_kernel (prefill_fwd.hip, decode_rows.h).
 //
 // Why: in a chunked-prefill step a prompt chunk runs beside many decode rows
 // ["大模型 Prompt Prefill 阶段的高效 Batching 与算子排布" §3], and decode
@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode_rows.h"
 #include "launch.h"
 
 namespace pa {
@@ -65,13 +66,17 @@ struct SeqPlan {
 };
 
 // Segments of a block whose keys span ntiles tiles: decode rows (one query,
-// HBM-bound) take segments of about seg_tiles tiles; blocks of several rows
-// (MFMA-bound, 128-row partial outputs) about 4 * seg_tiles -- longer
-// segments measured faster there (fewer partials to write and merge), and
-// shorter ones for decode rows (more units in flight).  At most max_segs.
-// Segment s covers tiles [s * ntiles / ns, (s + 1) * ntiles / ns).
-__device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs) {
-  const int target = decode_row ? seg_tiles : 4 * seg_tiles;
+// HBM-bound) take segments of about dec_mult * seg_tiles tiles; blocks of
+// several rows (MFMA-bound, 128-row partial outputs) about 4 * seg_tiles --
+// longer segments measured faster there (fewer partials to write and merge).
+// Decode rows in a launch of their own measured faster with short segments
+// (dec_mult 1: more units in flight), inside the attention launch with long
+// ones (dec_mult 4: its one work-group per compute unit pays a fixed cost per
+// unit).  At most max_segs.  Segment s covers tiles
+// [s * ntiles / ns, (s + 1) * ntiles / ns).
+__device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs,
+                                              int dec_mult) {
+  const int target = (decode_row ? dec_mult : 4) * seg_tiles;
   return min((ntiles + target - 1) / target, max_segs);
 }
 
@@ -79,12 +84,12 @@ __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int s
 // sequence's go to the decode list), and the merge entries of the blocks with
 // more than one segment.  Segment counts are capped at max_segs, so malformed
 // metadata cannot address outside the workspace.
-__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs) {
+__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult) {
   SeqPlan r{0, 0, 0};
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
+    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
     if (ns < 1) continue;
     if (len == 1)
       r.dec += ns;
@@ -100,12 +105,14 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs) {
 // the thread writes them.  hdr[0], hdr[1] receive the totals.
 __global__ __launch_bounds__(kPlanThreads)
 void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
-                         int num_seqs, int num_tokens, int seg_tiles, int max_segs,
+                         int num_seqs, int num_tokens, int seg_tiles, int max_segs, int dec_mult,
                          int64_t max_items, int64_t max_dec, int64_t max_merges,
                          int32_t* __restrict__ hdr, int4* __restrict__ items,
-                         int4* __restrict__ dec, int4* __restrict__ merges) {
+                         int4* __restrict__ dec, int4* __restrict__ merges,
+                         unsigned long long* __restrict__ counters) {
   __shared__ int wsum[3][kPlanThreads / 64];
   const int tid = __builtin_amdgcn_workitem_id_x();
+  if (tid < kSplitCounters) counters[tid] = 0;  // the attention pass hands out work through these
   const int lane = tid & 63, wave = tid >> 6;
   int64_t base_i = 0, base_d = 0, base_m = 0;
   for (int b0 = 0; b0 < num_seqs; b0 += kPlanThreads) {
@@ -118,7 +125,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       pre = prefix[b];
       // tokens outside [0, num_tokens) would index outside the partial buffers
       len = (start >= 0 && end <= num_tokens && end > start) ? end - start : 0;
-      c = count_seq(len, pre, seg_tiles, max_segs);
+      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult);
     }
     const int si = wave_incl_scan(c.items, lane);
     const int sd = wave_incl_scan(c.dec, lane);
@@ -149,12 +156,12 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       // run at the same time on one XCD and share its L2
       const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
       const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
-      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs);
+      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs, dec_mult);
       for (int s = 0; s < ns_max; ++s)
         for (int qb = 0; qb < nqb; ++qb) {
           const int qend = min(qb * kQueryBlock + kQueryBlock, len);
           const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
+          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
           if (s >= ns) continue;
           if (len == 1) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
@@ -168,7 +175,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs);
+        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
@@ -231,261 +238,19 @@ void splitkv_merge_kernel(const int32_t* __restrict__ hdr, const int4* __restric
   }
 }
 
-// ---------------------------------------------------------------- decode rows
-// A length-1 row is one query against its cached prefix plus itself: per key
-// 4 D flops against 4 D bytes of K and V, so the pass is bound by HBM, not by
-// the matrix cores.  It runs on the vector ALUs straight from 16-byte loads:
-// lane l of a wave owns the 8 elements d = 8 (l % LPK) + [0, 8) of key slot
-// l / LPK (LPK = D / 8 lanes per key, KPI = 64 / LPK keys per step); the
-// scores come from a DPP butterfly over each key's LPK lanes, and every key
-// slot keeps its own online-softmax state, combined across slots and waves at
-// the end of the unit.  A unit is (item, GC query heads of one K/V head):
-// each K/V row loaded serves all GC heads.
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over aligned groups of LPK (4, 8 or 16) lanes, result in every lane.
-template <int LPK>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp_f<0xB1>(x);                            // quad_perm [1,0,3,2]
-  x += dpp_f<0x4E>(x);                            // quad_perm [2,3,0,1]
-  if constexpr (LPK >= 8) x += dpp_f<0x141>(x);   // row_half_mirror
-  if constexpr (LPK >= 16) x += dpp_f<0x140>(x);  // row_mirror
-  return x;
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(const uint4 w, float (&f)[8]) {
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(u[i] << 16);
-    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
-
-__device__ __forceinline__ float lane_read(float x, int src) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(x)));
-}
-
+// Length-1 rows in a launch of their own (the split-KV call's choice when
+// the rows' work is not folded into the attention launch): four-wave
+// work-groups, several per compute unit, walk the decode units in a fixed
+// stride.
 constexpr int kDecThreads = 256;
-constexpr int kDecUnroll = 4;        // key steps whose loads are issued together
-constexpr float kDecRescale = 8.0f;  // lazy rescale headroom, log2 units
-constexpr float kDecMInit = -1.0e30f;
 
 template <int D, int GC, bool kPaged>
 __global__ __launch_bounds__(kDecThreads)
 void splitkv_decode_kernel(FwdParams p) {
-  constexpr int LPK = D / 8, KPI = 64 / LPK;
-  __shared__ float red[4][GC][2 + D];
-  const int tid = __builtin_amdgcn_workitem_id_x();
-  // wave-uniform in a scalar register: the key loop below is then a scalar loop
-  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kslot = lane / LPK, dch = lane % LPK;
-  const int H = p.num_heads, HK = p.num_kv_heads, G = H / HK;
-  const int units = H / GC;
-  const int64_t steps = (int64_t)p.hdr[2] * units;
-  const float c = p.scale_log2;
-
-  const float neg_inf = -__builtin_huge_valf();
-
-  for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += p.dec_grid) {
-    const int4 it = p.dec_items[g / units];
-    const int h0 = (int)(g % units) * GC;
-    const int hk = h0 / G;
-    const int b = it.x, s = it.y, ns = it.z;
-    const int tok = p.cu[b];
-    const int pre = p.prefix[b];
-    const int ntiles = (pre + 1 + kKeyTile - 1) / kKeyTile;
-    const int k0 = s * ntiles / ns * kKeyTile;
-    const int k1 = min((s + 1) * ntiles / ns * kKeyTile, pre + 1);  // keys [k0, k1) of this segment
-    const int per = ((k1 - k0 + 3) / 4 + KPI - 1) / KPI * KPI;
-    const int w0 = k0 + wave * per;
-    const int w1 = min(w0 + per, k1);            // this wave's keys
-    const int64_t crow = ((int64_t)b * HK + hk) * p.cap;
-    const uint16_t* __restrict__ kc = p.kc + crow * D;  // this (sequence, K/V head)'s cache
-    const uint16_t* __restrict__ vc = p.vc + crow * D;
-    const uint16_t* kn = p.k + ((int64_t)tok * HK + hk) * D + 8 * dch;  // the row's own key
-    const uint16_t* vn = p.v + ((int64_t)tok * HK + hk) * D + 8 * dch;
-    const int wc = min(w1, pre);  // the wave's cached keys are [w0, wc); key pre comes from k, v
-    // paged cache: block bt_row[j / 16] of [num_blocks, HK, 16, D] holds position j
-    const int32_t* __restrict__ bt_row = kPaged ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
-    const int last_sb = wc > w0 ? (wc - 1) / KPI * KPI : w0;  // last step's first key
-    float qf[GC][8], o[GC][8], m[GC], l[GC];
-#pragma unroll
-    for (int gi = 0; gi < GC; ++gi) {
-      uint4 w = *(const uint4*)(p.q + ((int64_t)tok * H + h0 + gi) * D + 8 * dch);
-      if (p.neg_q) {
-        w.x ^= 0x80008000u;
-        w.y ^= 0x80008000u;
-        w.z ^= 0x80008000u;
-        w.w ^= 0x80008000u;
-      }
-      bf16x8_to_f32(w, qf[gi]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[gi][i] = 0.f;
-      m[gi] = kDecMInit;
-      l[gi] = 0.f;
-    }
-
-    // cached keys kb + u KPI + kslot of a group of kDecUnroll steps; positions
-    // past the wave's last cached key load that key again (and are masked)
-    // paged cache: a step's KPI keys (KPI divides 16, steps start at
-    // multiples of KPI) lie in one block, one scalar block id per step; the
-    // ids of a group are fetched a group ahead of its loads
-    auto fetch = [&](int kb, int (&ids)[kDecUnroll]) __attribute__((always_inline)) {
-      if constexpr (kPaged) {
-#pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) ids[u] = bt_row[min(kb + u * KPI, last_sb) / kPageRows];
-      }
-    };
-    auto load = [&](int kb, uint4 (&kr)[kDecUnroll], uint4 (&vr)[kDecUnroll], const int (&ids)[kDecUnroll])
-        __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < kDecUnroll; ++u) {
-        if constexpr (kPaged) {
-          const int sb = min(kb + u * KPI, last_sb);
-          const int kq = min(sb + kslot, wc - 1);
-          const int64_t base = (((int64_t)ids[u] * HK + hk) * kPageRows) * D;
-          const uint32_t off = (uint32_t)(kq % kPageRows) * D + 8 * dch;
-          kr[u] = *(const uint4*)(p.kc + base + off);
-          vr[u] = *(const uint4*)(p.vc + base + off);
-        } else {
-          const uint32_t off = (uint32_t)min(kb + u * KPI + kslot, wc - 1) * D + 8 * dch;
-          kr[u] = *(const uint4*)(kc + off);
-          vr[u] = *(const uint4*)(vc + off);
-        }
-      }
-    };
-    auto consume_one = [&](bool ok, const uint4 kr, const uint4 vr) __attribute__((always_inline)) {
-      float kf[8], vf[8];
-      bf16x8_to_f32(kr, kf);
-      bf16x8_to_f32(vr, vf);
-#pragma unroll
-      for (int gi = 0; gi < GC; ++gi) {
-        float d0 = qf[gi][0] * kf[0], d1 = qf[gi][1] * kf[1];
-#pragma unroll
-        for (int i = 2; i < 8; i += 2) {
-          d0 = __builtin_fmaf(qf[gi][i], kf[i], d0);
-          d1 = __builtin_fmaf(qf[gi][i + 1], kf[i + 1], d1);
-        }
-        const float dot = group_sum<LPK>(d0 + d1);  // every lane, then the mask
-        const float sc = ok ? dot * c : neg_inf;
-        if (__any(sc > m[gi] + kDecRescale)) {
-          const float mn = fmaxf(m[gi], sc);
-          const float a = __builtin_amdgcn_exp2f(m[gi] - mn);
-          l[gi] *= a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[gi][i] *= a;
-          m[gi] = mn;
-        }
-        const float pe = __builtin_amdgcn_exp2f(sc - m[gi]);
-        l[gi] += pe;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[gi][i] = __builtin_fmaf(pe, vf[i], o[gi][i]);
-      }
-    };
-    auto consume = [&](int kb, const uint4 (&kr)[kDecUnroll], const uint4 (&vr)[kDecUnroll]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < kDecUnroll; ++u) consume_one(kb + u * KPI + kslot < wc, kr[u], vr[u]);
-    };
-    // two register sets: the next group's loads are in flight while a group
-    // is consumed
-    if (w0 < wc) {
-      constexpr int kStep = kDecUnroll * KPI;
-      uint4 ka[kDecUnroll], va[kDecUnroll], kb2[kDecUnroll], vb2[kDecUnroll];
-      int ida[kDecUnroll], idb[kDecUnroll];
-      fetch(w0, ida);
-      fetch(w0 + kStep, idb);
-      load(w0, ka, va, ida);
-      for (int kb = w0;; kb += 2 * kStep) {
-        fetch(kb + 2 * kStep, ida);
-        load(kb + kStep, kb2, vb2, idb);
-        consume(kb, ka, va);
-        if (kb + kStep >= wc) break;
-        fetch(kb + 3 * kStep, idb);
-        load(kb + 2 * kStep, ka, va, ida);
-        consume(kb + kStep, kb2, vb2);
-        if (kb + 2 * kStep >= wc) break;
-      }
-    }
-    if (w0 <= pre && pre < w1)  // the row's own key, in key slot 0
-      consume_one(kslot == 0, *(const uint4*)kn, *(const uint4*)vn);
-
-    // combine the KPI key slots of the wave (lanes l and l ^ x, x >= LPK)
-#pragma unroll
-    for (int x = LPK; x < 64; x <<= 1) {
-#pragma unroll
-      for (int gi = 0; gi < GC; ++gi) {
-        const float m2 = lane_read(m[gi], lane ^ x);
-        const float l2 = lane_read(l[gi], lane ^ x);
-        const float mn = fmaxf(m[gi], m2);
-        const float a = __builtin_amdgcn_exp2f(m[gi] - mn), a2 = __builtin_amdgcn_exp2f(m2 - mn);
-        l[gi] = l[gi] * a + l2 * a2;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[gi][i] = o[gi][i] * a + lane_read(o[gi][i], lane ^ x) * a2;
-        m[gi] = mn;
-      }
-    }
-    // then the four waves, through LDS
-    if (lane < LPK) {
-#pragma unroll
-      for (int gi = 0; gi < GC; ++gi) {
-        if (lane == 0) {
-          red[wave][gi][0] = m[gi];
-          red[wave][gi][1] = l[gi];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) red[wave][gi][2 + 8 * dch + i] = o[gi][i];
-      }
-    }
-    __syncthreads();
-    if (wave == 0 && lane < LPK) {
-#pragma unroll
-      for (int gi = 0; gi < GC; ++gi) {
-        float mm = red[0][gi][0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) mm = fmaxf(mm, red[w][gi][0]);
-        float ll = 0.f, oo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) oo[i] = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float a = __builtin_amdgcn_exp2f(red[w][gi][0] - mm);
-          ll = __builtin_fmaf(red[w][gi][1], a, ll);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) oo[i] = __builtin_fmaf(red[w][gi][2 + 8 * dch + i], a, oo[i]);
-        }
-        const float inv = ll > 0.f ? 1.f / ll : 0.f;
-        const int64_t row = (int64_t)tok * H + h0 + gi;
-        if (ns == 1) {
-          uint4 w;
-          w.x = pack_bf16x2(oo[0] * inv, oo[1] * inv);
-          w.y = pack_bf16x2(oo[2] * inv, oo[3] * inv);
-          w.z = pack_bf16x2(oo[4] * inv, oo[5] * inv);
-          w.w = pack_bf16x2(oo[6] * inv, oo[7] * inv);
-          *(uint4*)(p.out + row * D + 8 * dch) = w;
-        } else {
-          const int64_t slot = row * p.max_segs + s;
-          float* dst = p.part_o + slot * D + 8 * dch;
-          *(float4*)dst = make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
-          *(float4*)(dst + 4) = make_float4(oo[4] * inv, oo[5] * inv, oo[6] * inv, oo[7] * inv);
-          if (lane == 0) p.part_lse[slot] = ll > 0.f ? mm + __builtin_amdgcn_logf(ll) : neg_inf;
-        }
-      }
-    }
-    // the segment holding the row's own position writes its K/V to the cache,
-    // once per K/V head (the unit of the group's first query heads)
-    if (wave == 1 && lane < LPK && s == ns - 1 && h0 == hk * G) {
-      const int64_t row = kPaged ? ((int64_t)bt_row[pre / kPageRows] * HK + hk) * kPageRows + pre % kPageRows
-                                 : crow + pre;
-      *(uint4*)(p.kc + row * D + 8 * dch) = *(const uint4*)kn;
-      *(uint4*)(p.vc + row * D + 8 * dch) = *(const uint4*)vn;
-    }
-    __syncthreads();  // red is rewritten by the next unit
-  }
+  __shared__ float red[dec::red_floats<D, GC, kDecThreads / 64>()];
+  const int64_t steps = (int64_t)p.hdr[2] * (p.num_heads / GC);
+  for (int64_t g = __builtin_amdgcn_workgroup_id_x(); g < steps; g += p.dec_grid)
+    dec::decode_unit<D, GC, kPaged, kDecThreads / 64>(p, g, red, nullptr, nullptr);
 }
 
 }  // namespace
@@ -505,7 +270,8 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
   const int64_t max_merges = (int64_t)num_tokens / kMergeRows + num_seqs + 1;
   const size_t slots = (size_t)num_tokens * num_heads * L.max_segs;
   L.off_hdr = 0;
-  L.off_items = 256;
+  L.off_ctr = 256;
+  L.off_items = 512;
   L.off_dec = L.off_items + round256(16 * (size_t)L.max_items);
   L.off_merges = L.off_dec + round256(16 * (size_t)L.max_dec_items);
   L.off_lse = L.off_merges + round256(16 * (size_t)max_merges);
@@ -515,16 +281,17 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 }
 
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
-                               int32_t num_tokens, const SplitLayout& L, void* ws,
+                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult, void* ws,
                                hipStream_t stream) {
   char* base = static_cast<char*>(ws);
   const int64_t max_merges = (int64_t)(L.off_lse - L.off_merges) / 16;
   hipLaunchKernelGGL(splitkv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, prefix,
-                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, L.max_items, L.max_dec_items,
+                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, L.max_items, L.max_dec_items,
                      max_merges, reinterpret_cast<int32_t*>(base + L.off_hdr),
                      reinterpret_cast<int4*>(base + L.off_items),
                      reinterpret_cast<int4*>(base + L.off_dec),
-                     reinterpret_cast<int4*>(base + L.off_merges));
+                     reinterpret_cast<int4*>(base + L.off_merges),
+                     reinterpret_cast<unsigned long long*>(base + L.off_ctr));
   return hipGetLastError();
 }
 
@@ -545,16 +312,11 @@ hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const 
 
 namespace pa {
 
-int splitkv_heads_per_unit(int num_heads, int num_kv_heads) {
-  const int g = num_heads / num_kv_heads;
-  return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
-}
-
 namespace {
 template <int D, bool kPaged>
-hipError_t decode_d(const FwdParams& p, int gc, hipStream_t stream) {
+hipError_t decode_d(const FwdParams& p, hipStream_t stream) {
   const dim3 grid(p.dec_grid), block(kDecThreads);
-  switch (gc) {
+  switch (p.dec_heads) {
     case 1: hipLaunchKernelGGL((splitkv_decode_kernel<D, 1, kPaged>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((splitkv_decode_kernel<D, 2, kPaged>), grid, block, 0, stream, p); break;
     case 4: hipLaunchKernelGGL((splitkv_decode_kernel<D, 4, kPaged>), grid, block, 0, stream, p); break;
@@ -578,12 +340,11 @@ int decode_occ(int gc) {
 }
 }  // namespace
 
-hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, int heads_per_unit, bool paged,
-                                 hipStream_t stream) {
+hipError_t launch_splitkv_decode(const FwdParams& p, int head_dim, bool paged, hipStream_t stream) {
   switch (head_dim) {
-    case 32: return paged ? decode_d<32, true>(p, heads_per_unit, stream) : decode_d<32, false>(p, heads_per_unit, stream);
-    case 64: return paged ? decode_d<64, true>(p, heads_per_unit, stream) : decode_d<64, false>(p, heads_per_unit, stream);
-    case 128: return paged ? decode_d<128, true>(p, heads_per_unit, stream) : decode_d<128, false>(p, heads_per_unit, stream);
+    case 32: return paged ? decode_d<32, true>(p, stream) : decode_d<32, false>(p, stream);
+    case 64: return paged ? decode_d<64, true>(p, stream) : decode_d<64, false>(p, stream);
+    case 128: return paged ? decode_d<128, true>(p, stream) : decode_d<128, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -595,6 +356,11 @@ int splitkv_decode_blocks_per_cu(int head_dim, int heads_per_unit, bool paged) {
     case 128: return paged ? decode_occ<128, true>(heads_per_unit) : decode_occ<128, false>(heads_per_unit);
     default: return 0;
   }
+}
+
+int splitkv_heads_per_unit(int num_heads, int num_kv_heads) {
+  const int g = num_heads / num_kv_heads;
+  return g % 8 == 0 ? 8 : g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
 }
 
 }  // namespace pa

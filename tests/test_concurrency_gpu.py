@@ -86,6 +86,14 @@ def run_all(pb, ws):
     m.prefill_attn_chunked_splitkv(pb["q"], pb["k"], pb["v"], pb["cu"], kc, vc, out, pb["pre"],
                                    max_seqlen=pb["max_len"], workspace=ws)
     res["splitkv"] = (out, kc, vc)
+    # one query head per K/V head: the decode rows run inside the attention
+    # launch, whose work-groups take items and units from shared counters
+    q1 = pb["q"][:, :HK].contiguous()
+    out = torch.empty_like(q1)
+    kc, vc = pb["kc0"].clone(), pb["vc0"].clone()
+    m.prefill_attn_chunked_splitkv(q1, pb["k"], pb["v"], pb["cu"], kc, vc, out, pb["pre"],
+                                   max_seqlen=pb["max_len"], workspace=ws)
+    res["splitkv_mixed"] = (out, kc, vc)
     return res
 
 

@@ -61,7 +61,7 @@ def run_split(q, k, v, cu, pre, kc, vc, scale, ws=None, max_seqlen=None):
     return out
 
 
-def check_case(lengths, prefix, cap, H, HK, D, seed, what, scale=None):
+def check_case(lengths, prefix, cap, H, HK, D, seed, what, scale=None, max_seqlen=None):
     g = I.generator(seed)
     cu = I.cu_from_lengths(lengths)
     N, B = cu[-1], len(lengths)
@@ -75,7 +75,7 @@ def check_case(lengths, prefix, cap, H, HK, D, seed, what, scale=None):
         % (what, lengths, prefix, cap, H, HK, D, scale))
     whole, need = workspace_for(B, N, H, D, cap)
     kc, vc = kc0.cuda(), vc0.cuda()
-    out = run_split(q, k, v, cu, prefix, kc, vc, scale, ws=whole[:need])
+    out = run_split(q, k, v, cu, prefix, kc, vc, scale, ws=whole[:need], max_seqlen=max_seqlen)
     ref, kimg, vimg, _ = oracle.prefill_chunked(q, k, v, cu, prefix, kc0, vc0, scale)
     assert_close(out, ref, what)
     np.testing.assert_array_equal(bits(kc), kimg)
@@ -96,9 +96,10 @@ def test_splitkv_segment_edges_full(D):
     check_case(LENGTHS, PREFIX, 3000, 3, 3, D, 900 + D, "splitkv edges D=%d" % D)
 
 
-@pytest.mark.parametrize("H,HK,D", [(8, 2, 128), (4, 1, 64), (16, 2, 64), (6, 3, 32), (32, 1, 128)])
+@pytest.mark.parametrize("H,HK,D", [(8, 2, 128), (4, 1, 64), (16, 2, 64), (6, 3, 32), (32, 1, 128), (8, 4, 128)])
 def test_splitkv_grouped_heads(H, HK, D):
-    # decode rows share each K/V load among 4, 4, 8, 2 and 8 query heads
+    # decode rows share each K/V load among 4, 4, 8, 2, 8 and 2 query heads
+    # (1 or 2: the rows run inside the attention launch, else in their own)
     check_case([96, 1, 1, 33, 1], [1500, 3000, 1, 64, 2048], 3100, H, HK, D, 910 + H + D,
                "splitkv gqa H=%d HK=%d" % (H, HK))
 
@@ -112,6 +113,21 @@ def test_splitkv_decode_rows_only():
     """A batch of decode rows only (no prompt chunk), contexts across segment edges."""
     ctx = [0, 1, 63, 64, 1023, 1024, 1025, 2047, 2048, 4095, 5000]
     check_case([1] * len(ctx), ctx, 5001, 4, 4, 128, 960, "splitkv decode only")
+
+
+def test_splitkv_decode_rows_only_larger_max_seqlen():
+    """Only length-1 rows, but max_seqlen 4 (an upper bound, as the header
+    allows): the launch that runs decode rows beside attention items gets no
+    item, and every work-group starts on the decode units."""
+    ctx = [0, 1, 64, 1023, 1024, 2047, 4095, 5000, 333]
+    check_case([1] * len(ctx), ctx, 5001, 4, 4, 128, 965, "splitkv decode only, max_seqlen 4", max_seqlen=4)
+
+
+def test_splitkv_batch_without_decode_rows():
+    """Several multi-token sequences and no length-1 row: in the launch that
+    runs decode rows beside attention items every work-group starts on the
+    items (segments of 64 tiles: blocks with one, two and three segments)."""
+    check_case([100, 40, 260, 2], [1500, 0, 8000, 77], 8300, 4, 4, 128, 985, "splitkv no decode rows")
 
 
 def test_splitkv_long_context_many_segments():
