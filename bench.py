@@ -23,7 +23,6 @@ Context fields (not part of value): launch_us (each launch between its own
 events), cold_launch_us (after a 1 GiB fill that evicts L2 and the Infinity
 Cache), kv_write_standalone_copy (the cache write alone as a plain torch copy),
 gemm_bf16_context (a large hipBLASLt bf16 GEMM at the run's clock),
-gpu_clocks_power (amd-smi before and after the timed steps, when available),
 int8_cache and fp8_cache (the same step writing an INT8 or E4M3 cache).  The chunked workloads
 report the heaviest step one-pass, split-KV and paged, the decode rows alone,
 and every step summed (all_steps_splitkv) with the prompt's chunks alone
@@ -180,27 +179,6 @@ def stats_us(ms_sorted):
             "p99": round(ms_sorted[min(n - 1, int(math.ceil(0.99 * n)) - 1)] * 1e3, 2)}
 
 
-def smi_under_load(fn, ms_per_call, seconds=1.5):
-    """amd-smi clocks and power sampled from a side thread while about
-    `seconds` of back-to-back calls of fn run (after all timed passes)."""
-    import threading
-    import time as _t
-    import torch
-    res = {}
-
-    def sample():
-        _t.sleep(0.4)
-        res["s"] = smi_sample()
-
-    th = threading.Thread(target=sample)
-    th.start()
-    for _ in range(max(1, int(seconds / (ms_per_call * 1e-3)))):
-        fn()
-    torch.cuda.synchronize()
-    th.join()
-    return res.get("s")
-
-
 def gemm_context(n=8192, steps=20):
     """A large plain bf16 GEMM through torch (hipBLASLt), back to back: the
     matrix rate this part sustains at the clock of the run, as context for the
@@ -213,33 +191,6 @@ def gemm_context(n=8192, steps=20):
     ms = timed_steps(lambda: torch.matmul(a, b, out=c), steps, 5)
     del a, b, c
     return {"shape": [n, n, n], "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
-
-
-def smi_sample():
-    """GPU clocks and power from amd-smi, best effort (None when unavailable)."""
-    import subprocess
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], stdout=subprocess.PIPE,
-                           stderr=subprocess.DEVNULL, text=True, timeout=20)
-        d = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    found = {}
-
-    def walk(x, path):
-        if isinstance(x, dict):
-            for kk, vv in x.items():
-                walk(vv, path + [str(kk)])
-        elif isinstance(x, list):
-            for i, vv in enumerate(x):
-                walk(vv, path + [str(i)])
-        elif len(path) >= 3 and path[-1] == "value" and len(found) < 12:
-            # current clock of each graphics partition, and socket power
-            if (path[-3].startswith("gfx") and path[-2] == "clk") or "socket_power" in path[-2]:
-                found["/".join(path[-3:-1])] = x
-
-    walk(d, [])
-    return found or None
 
 
 def bench_chunked(args, wl, P):
@@ -544,7 +495,6 @@ def main():
         "kv_write_standalone_copy": kv_copy,
         "gemm_bf16_context": dict(gemm, pct_of_published_peak=round(100.0 * gemm["tflops"] / PEAK_BF16_TFLOPS, 1),
                                   attention_pct_of_it=round(100.0 * value / gemm["tflops"], 1)),
-        "gpu_clocks_power_under_load": smi_under_load(step, ms_per_step),
         "int8_cache": {"us_per_step": round(ms8 * 1e3, 2),
                        "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2),
                        "cache_bytes_written": cache8_bytes,
