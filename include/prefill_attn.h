@@ -213,9 +213,11 @@ pa_status prefill_attn_varlen_fp8(const uint16_t *q, const uint16_t *k, const ui
  * units idle.  Each query block's keys are cut into segments of at least 1024
  * keys; every segment is an independent work item, and a block with more
  * than one segment is finished by an fp32 log-sum-exp merge of the segments'
- * partial results.  Three kernels are enqueued on `stream`: plan, attention,
- * merge.  Rows differ from prefill_attn_chunked_gqa only by floating-point
- * rounding order.
+ * partial results.  Enqueued on `stream`: a plan, one persistent attention
+ * launch, a launch for the length-1 rows unless the attention launch runs
+ * them beside the chunk's blocks (B > 1, max_seqlen > 1, at most two query
+ * heads per K/V head, slab cache), and the merge.  Rows differ from
+ * prefill_attn_chunked_gqa only by floating-point rounding order.
  *
  *   num_tokens        N, the rows of q, k, v and out (host); cu_seqlens[B]
  *                     must not exceed it (check mode: PA_ERR_SEQLENS).
