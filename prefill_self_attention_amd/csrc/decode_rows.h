@@ -1,6 +1,6 @@
 // decode_rows.h -- the length-1 rows of the split-KV chunked call, one unit
-// at a time; included by prefill_fwd.hip, whose persistent split-KV kernel
-// runs these units beside the attention items.
+// at a time; included by prefill_fwd.hip (the mixed launch runs these units
+// beside the attention items) and splitkv.hip (the rows' own launch).
 //
 // A length-1 row is one query against its cached prefix plus itself
 // (untitled page www.zwxr.cn/news/300951 §3.3: decode attention reads every
@@ -8,11 +8,12 @@
 // V, so a unit is bound by HBM, not by the matrix cores.  It runs on the
 // vector ALUs straight from 16-byte loads: lane l of a wave owns the 8
 // elements d = 8 (l % LPK) + [0, 8) of key slot l / LPK (LPK = D / 8 lanes per
-// key, KPI = 64 / LPK keys per step); the scores come from a DPP butterfly
-// over each key's LPK lanes, and every key slot keeps its own online-softmax
-// state, combined across slots and then across the W waves at the end of the
-// unit.  A unit is (decode item, GC query heads of one K/V head): each K/V row
-// loaded serves all GC heads.
+// key, KPI = 64 / LPK keys per step); a lane's part of a score is four bf16
+// pair dot products (v_dot2_f32_bf16, q kept as bf16 pairs), the score a DPP
+// butterfly over the key's LPK lanes, and every key slot keeps its own
+// online-softmax state, combined across slots and then across the W waves at
+// the end of the unit.  A unit is (decode item, GC query heads of one K/V
+// head): each K/V row loaded serves all GC heads.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -114,7 +115,8 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float
   // paged cache: block bt_row[j / 16] of [num_blocks, HK, 16, D] holds position j
   const int32_t* __restrict__ bt_row = kPaged ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
   const int last_sb = wc > w0 ? (wc - 1) / KPI * KPI : w0;  // last step's first key
-  float qf[GC][8], o[GC][8], m[GC], l[GC];
+  bf16x2_t qp[GC][4];  // q as bf16 pairs: the dot products run on v_dot2_f32_bf16
+  float o[GC][8], m[GC], l[GC];
 #pragma unroll
   for (int gi = 0; gi < GC; ++gi) {
     uint4 w = *(const uint4*)(p.q + ((int64_t)tok * H + h0 + gi) * D + 8 * dch);
@@ -124,7 +126,10 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float
       w.z ^= 0x80008000u;
       w.w ^= 0x80008000u;
     }
-    bf16x8_to_f32(w, qf[gi]);
+    qp[gi][0] = __builtin_bit_cast(bf16x2_t, w.x);
+    qp[gi][1] = __builtin_bit_cast(bf16x2_t, w.y);
+    qp[gi][2] = __builtin_bit_cast(bf16x2_t, w.z);
+    qp[gi][3] = __builtin_bit_cast(bf16x2_t, w.w);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[gi][i] = 0.f;
     m[gi] = kMInit;
@@ -161,17 +166,17 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float
     }
   };
   auto consume_one = [&](bool ok, const uint4 kr, const uint4 vr) __attribute__((always_inline)) {
-    float kf[8], vf[8];
-    bf16x8_to_f32(kr, kf);
+    float vf[8];
     bf16x8_to_f32(vr, vf);
+    const bf16x2_t k0 = __builtin_bit_cast(bf16x2_t, kr.x), k1 = __builtin_bit_cast(bf16x2_t, kr.y);
+    const bf16x2_t k2 = __builtin_bit_cast(bf16x2_t, kr.z), k3 = __builtin_bit_cast(bf16x2_t, kr.w);
 #pragma unroll
     for (int gi = 0; gi < GC; ++gi) {
-      float d0 = qf[gi][0] * kf[0], d1 = qf[gi][1] * kf[1];
-#pragma unroll
-      for (int i = 2; i < 8; i += 2) {
-        d0 = __builtin_fmaf(qf[gi][i], kf[i], d0);
-        d1 = __builtin_fmaf(qf[gi][i + 1], kf[i + 1], d1);
-      }
+      // bf16 products are exact in fp32; two chains of two pairs each
+      float d0 = __builtin_amdgcn_fdot2_f32_bf16(qp[gi][0], k0, 0.f, false);
+      float d1 = __builtin_amdgcn_fdot2_f32_bf16(qp[gi][1], k1, 0.f, false);
+      d0 = __builtin_amdgcn_fdot2_f32_bf16(qp[gi][2], k2, d0, false);
+      d1 = __builtin_amdgcn_fdot2_f32_bf16(qp[gi][3], k3, d1, false);
       const float dot = group_sum<LPK>(d0 + d1);  // every lane, then the mask
       const float sc = ok ? dot * c : neg_inf;
       if (__any(sc > m[gi] + kRescale)) {
