@@ -187,6 +187,7 @@ std::atomic<int> g_dec_occ[kMaxDevices][3][4][2];
 // rest start on the decode rows' units).
 constexpr int kItemsFirstPercent = 50;
 constexpr int kFuseMaxHeads = 2;
+static_assert(kFuseMaxHeads <= 2, "the mixed kernel has decode units of one and two query heads only");
 constexpr bool kFusePaged = false;
 
 // Whether the decode rows run inside the split attention launch.  There they

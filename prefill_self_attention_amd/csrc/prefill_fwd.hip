@@ -1010,7 +1010,7 @@ void prefill_fwd_mixed_kernel(FwdParams p) {
     }
   };
   float* const red = reinterpret_cast<float*>(fwd_lds<D, true, true, kCacheBf16, kPaged, 1>());
-  static_assert(dec::red_floats<D, 8, kWaves>() * 4 <= Cfg<D>::kLdsBytes, "decode reduction exceeds LDS");
+  static_assert(dec::red_floats<D, 2, kWaves>() * 4 <= Cfg<D>::kLdsBytes, "decode reduction exceeds LDS");
   const bool items_first = wg < first;
   for (int phase = 0; phase < 2; ++phase) {
     if ((phase == 0) == items_first) {
@@ -1034,15 +1034,15 @@ void prefill_fwd_mixed_kernel(FwdParams p) {
         if ((open >> x) & 1u) drain(x, phase == 0 && i == 0);
       }
     } else if (units > 0) {
-      // each unit takes the next unit's number while it runs
+      // each unit takes the next unit's number while it runs; the host sends
+      // decode rows here only with one or two query heads per unit (units of
+      // 4 or 8 heads would also cost registers the items need)
       unsigned long long* const ctr = p.counters + 8;
       for (unsigned long long g = phase == 0 ? (uint32_t)(wg - first) : take(8, U, units); g < units; g = U + taken) {
-        switch (p.dec_heads) {
-          case 1: dec::decode_unit<D, 1, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
-          case 2: dec::decode_unit<D, 2, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
-          case 4: dec::decode_unit<D, 4, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
-          default: dec::decode_unit<D, 8, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken); break;
-        }
+        if (p.dec_heads == 1)
+          dec::decode_unit<D, 1, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken);
+        else
+          dec::decode_unit<D, 2, kPaged, kWaves>(p, (int64_t)g, red, ctr, &taken);
       }
       __syncthreads();  // every wave has read taken before take() rewrites it
     }
