@@ -84,11 +84,12 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 // in the workspace, work counters zeroed.  Then the persistent pass over the
 // items and the decode rows' units (both in one launch), then the merge of
 // blocks with more than one segment.
-// dec_seg_mult: a decode row's segments hold about dec_seg_mult * seg_tiles
-// tiles (longer ones when the rows run inside the attention launch).
+// A decode row's segments hold about dec_seg_mult * seg_tiles tiles, a
+// multi-row block's about item_seg_mult * seg_tiles (both longer when the
+// rows run inside the attention launch).
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
-                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult, void* ws,
-                               hipStream_t stream);
+                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult,
+                               int item_seg_mult, void* ws, hipStream_t stream);
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
                                 int head_dim, int grid, hipStream_t stream);

@@ -66,17 +66,19 @@ struct SeqPlan {
 };
 
 // Segments of a block whose keys span ntiles tiles: decode rows (one query,
-// HBM-bound) take segments of about dec_mult * seg_tiles tiles; blocks of
-// several rows (MFMA-bound, 128-row partial outputs) about 4 * seg_tiles --
-// longer segments measured faster there (fewer partials to write and merge).
-// Decode rows in a launch of their own measured faster with short segments
-// (dec_mult 1: more units in flight), inside the attention launch with long
-// ones (dec_mult 4: its one work-group per compute unit pays a fixed cost per
-// unit).  At most max_segs.  Segment s covers tiles
-// [s * ntiles / ns, (s + 1) * ntiles / ns).
+// HBM-bound) take segments of about dec_mult * seg_tiles tiles, blocks of
+// several rows (MFMA-bound, 128-row partial outputs) about item_mult *
+// seg_tiles.  With separate launches short decode segments measured faster
+// (dec_mult 1: more units in flight) and item_mult 4 beat 2 (fewer partials
+// to write and merge).  When the decode rows run beside the items in one
+// launch, long segments of both kinds measured faster (dec_mult 4: its one
+// work-group per compute unit pays a fixed cost per unit; item_mult 8: the
+// decode units keep the compute units busy while fewer, longer items run, and
+// most blocks then need no merge).  At most max_segs.  Segment s covers
+// tiles [s * ntiles / ns, (s + 1) * ntiles / ns).
 __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs,
-                                              int dec_mult) {
-  const int target = (decode_row ? dec_mult : 4) * seg_tiles;
+                                              int dec_mult, int item_mult) {
+  const int target = (decode_row ? dec_mult : item_mult) * seg_tiles;
   return min((ntiles + target - 1) / target, max_segs);
 }
 
@@ -84,12 +86,12 @@ __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int s
 // sequence's go to the decode list), and the merge entries of the blocks with
 // more than one segment.  Segment counts are capped at max_segs, so malformed
 // metadata cannot address outside the workspace.
-__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult) {
+__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult, int item_mult) {
   SeqPlan r{0, 0, 0};
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
+    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
     if (ns < 1) continue;
     if (len == 1)
       r.dec += ns;
@@ -105,7 +107,7 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int 
 // the thread writes them.  hdr[0], hdr[1] receive the totals.
 __global__ __launch_bounds__(kPlanThreads)
 void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
-                         int num_seqs, int num_tokens, int seg_tiles, int max_segs, int dec_mult,
+                         int num_seqs, int num_tokens, int seg_tiles, int max_segs, int dec_mult, int item_mult,
                          int64_t max_items, int64_t max_dec, int64_t max_merges,
                          int32_t* __restrict__ hdr, int4* __restrict__ items,
                          int4* __restrict__ dec, int4* __restrict__ merges,
@@ -125,7 +127,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       pre = prefix[b];
       // tokens outside [0, num_tokens) would index outside the partial buffers
       len = (start >= 0 && end <= num_tokens && end > start) ? end - start : 0;
-      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult);
+      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult, item_mult);
     }
     const int si = wave_incl_scan(c.items, lane);
     const int sd = wave_incl_scan(c.dec, lane);
@@ -156,12 +158,12 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       // run at the same time on one XCD and share its L2
       const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
       const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
-      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs, dec_mult);
+      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
       for (int s = 0; s < ns_max; ++s)
         for (int qb = 0; qb < nqb; ++qb) {
           const int qend = min(qb * kQueryBlock + kQueryBlock, len);
           const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
+          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
           if (s >= ns) continue;
           if (len == 1) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
@@ -175,7 +177,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult);
+        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
@@ -281,12 +283,12 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 }
 
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
-                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult, void* ws,
-                               hipStream_t stream) {
+                               int32_t num_tokens, const SplitLayout& L, int dec_seg_mult,
+                               int item_seg_mult, void* ws, hipStream_t stream) {
   char* base = static_cast<char*>(ws);
   const int64_t max_merges = (int64_t)(L.off_lse - L.off_merges) / 16;
   hipLaunchKernelGGL(splitkv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, prefix,
-                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, L.max_items, L.max_dec_items,
+                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, item_seg_mult, L.max_items, L.max_dec_items,
                      max_merges, reinterpret_cast<int32_t*>(base + L.off_hdr),
                      reinterpret_cast<int4*>(base + L.off_items),
                      reinterpret_cast<int4*>(base + L.off_dec),
