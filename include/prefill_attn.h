@@ -216,7 +216,7 @@ pa_status prefill_attn_varlen_fp8(const uint16_t *q, const uint16_t *k, const ui
  * partial results.  Enqueued on `stream`: a plan, one persistent attention
  * launch, a launch for the length-1 rows unless the attention launch runs
  * them beside the chunk's blocks (B > 1, max_seqlen > 1, at most two query
- * heads per K/V head, slab cache), and the merge.  Rows differ from
+ * heads per K/V head), and the merge.  Rows differ from
  * prefill_attn_chunked_gqa only by floating-point rounding order.
  *
  *   num_tokens        N, the rows of q, k, v and out (host); cu_seqlens[B]

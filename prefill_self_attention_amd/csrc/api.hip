@@ -188,13 +188,12 @@ std::atomic<int> g_dec_occ[kMaxDevices][3][4][2];
 constexpr int kItemsFirstPercent = 50;
 constexpr int kFuseMaxHeads = 2;
 static_assert(kFuseMaxHeads <= 2, "the mixed kernel has decode units of one and two query heads only");
-constexpr bool kFusePaged = false;
 
 // Whether the decode rows run inside the split attention launch.  There they
 // run beside the items, but with 8 waves per compute unit instead of 16; that
 // pays where a row's unit streams K/V (one query head per K/V head) and
 // costs where it computes (grouped heads: 4 or 8 query heads per load).
-bool fuse_decode(int heads_per_unit, bool paged) { return heads_per_unit <= kFuseMaxHeads && (kFusePaged || !paged); }
+bool fuse_decode(int heads_per_unit) { return heads_per_unit <= kFuseMaxHeads; }
 
 // Work-groups of the split-KV attention launch (resident ones only: it is
 // persistent), the share of them that starts on the attention items when the
@@ -314,7 +313,7 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // only a batch that may hold both multi-token blocks and length-1 rows
   // gains from running them together (one lone sequence, or rows of length
   // at most 1, leave one kind of work empty)
-  const bool fused = fuse_decode(gc, paged) && num_seqs > 1 && max_seqlen > 1;
+  const bool fused = fuse_decode(gc) && num_seqs > 1 && max_seqlen > 1;
   int fwd_grid = 0, items_first = 0, merge_grid = 0, dec_grid = 0;
   st = split_grid(head_dim, fused, &fwd_grid, &items_first, &merge_grid);
   if (st == PA_OK && !fused) st = decode_grid(head_dim, gc, paged, &dec_grid);
