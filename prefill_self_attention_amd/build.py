@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libprefill_attn.so")
-SOURCES = ["api.hip", "prefill_fwd.hip", "splitkv.hip"]
+SOURCES = ["api.hip", "prefill_fwd.hip", "splitkv.hip", "fwd64.hip"]
 ARCH = "gfx950"
 
 

@@ -31,6 +31,16 @@ bool check_mode() {
   return m == 1;
 }
 
+// The 64-row kernel serves varlen head_dim-128 calls unless PA_FWD64=0 (kept
+// for A/B measurements against the 32-row kernel).
+bool fwd64_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_FWD64");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 pa_status hip_fail(hipError_t e) {
   t_last_hip_error = (int)e;
   return PA_ERR_HIP;
@@ -170,6 +180,8 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
     p.vs = qc->vs;
     e = qc->fp8 ? pa::launch_prefill_fwd_fp8(p, num_seqs, head_dim, stream)
                 : pa::launch_prefill_fwd_int8(p, num_seqs, head_dim, stream);
+  } else if (pa::fwd64_supported(head_dim, prefix != nullptr, scale, max_seqlen, num_heads, num_kv_heads) && fwd64_enabled()) {
+    e = pa::launch_prefill_fwd64(p, num_seqs, stream);
   } else {
     e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
   }

@@ -1,0 +1,395 @@
+// fwd64.hip -- causal varlen prefill attention with a fused bf16 KV-cache
+// write, head_dim 128, for gfx950 (MI355X, CDNA4): 64 query rows per wave.
+//
+// Computes what prefill_fwd_kernel computes for varlen batches (see
+// prefill_fwd.hip and include/prefill_attn.h): for sequence b, head h and
+// token i, out = sum_{j <= i} softmax_j(scale * q_i . k_j) v_j over the keys
+// of sequence b ["Prefill不是热身：大模型推理的真正瓶颈与优化核心" §3 and
+// "大语言模型推理核心：Prefill与Decode原理及工程优化" §2.2: softmax(Q K^T /
+// sqrt(d_k)) V; untitled page www.zwxr.cn/news/300951 §1.1: a position sees
+// itself and the ones before it; "大模型 Prompt Prefill 阶段的高效 Batching 与算子排布"
+// §2: requests of a flattened batch never see each other], and copies every
+// token's K and V into the per-sequence [HK, len, D] cache
+// ["大模型推理优化：Prefill、Decode与KV Cache的工程实践" §1.3].
+//
+// Why a second kernel: with 32 query rows per wave every 32x32x16 MFMA needs
+// its own 1 KB operand fragment from LDS, and at the matrix cores' full rate
+// four SIMDs would read 128 B per clock, which is all the LDS delivers.  Here
+// a wave owns 64 query rows (two halves of 32), so each K or V fragment read
+// from LDS feeds two MFMAs, and one wave runs per SIMD with 512 registers:
+//
+//  * O^T (64 rows x 128 columns, fp32) stays in 128 AGPRs as the MFMA
+//    accumulators, and Q^T (64 rows x 128, bf16) in 64 more as the MFMA B
+//    operand of the scores; scores, weights and operand slots use fixed VGPRs.
+//  * The loop is software-pipelined inside the wave, in two phases per key
+//    tile (gen_fwd64.py writes both, fwd64_phases.h): the score MFMAs of tile
+//    j+1 run while the VALU does the softmax of tile j for rows 32..63, and
+//    the PV MFMAs of tile j run while the VALU does the softmax of tile j+1
+//    for rows 0..31.  The two streams are interleaved instruction by
+//    instruction, so the matrix cores and the vector ALU work at the same
+//    time in one wave; the next tiles' global-to-LDS loads are spread between
+//    the MFMAs as well.
+//  * The softmax is the one of prefill_fwd.hip (exp2 domain, lazy rescale by
+//    more than 2^8, causal masking on the diagonal tile only); the running
+//    sum adds the bf16-rounded weights that the PV product uses.
+//  * Work split as in prefill_fwd.hip: a work-group takes the block pair
+//    (z, n-1-z) of one (sequence, head); two waves (the upper group) walk the
+//    heavy block's first tiles, the other two the light block and then the
+//    heavy block's remaining tiles, and the heavy block's two partial states
+//    are merged through LDS at the end.  Each group keeps its K and V tiles
+//    in LDS rings of two (64 KB per group).
+//  * Tiles that hold a block's own tokens are copied from LDS to the cache
+//    with 16-byte streaming stores, every token once.
+//
+// Runs for varlen calls with head_dim 128, a bf16 cache and a non-negative
+// scale; api.hip sends every other case to prefill_fwd_kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "launch.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kRowBytes = 2 * kD;
+constexpr int kBM = kQueryBlock;   // 128 query rows per block
+constexpr int kBN = kKeyTile;      // 64 keys per tile
+constexpr int kThreads = 256;      // 4 waves, one per SIMD
+constexpr int kGroupBytes = 65536; // K ring (2 x 16 KB) + V ring (2 x 16 KB)
+constexpr int kLdsBytes = 2 * kGroupBytes;
+constexpr float kMInit = -1.0e30f;
+
+// The phases keep their state in registers the compiler never allocates
+// (the kernel caps its own allocation at v0-v63 and a0-a63): O^T in
+// a[64:191], Q^T in a[192:255], scores, weights, operand slots and
+// temporaries in v[64:255] (layout in gen_fwd64.py).  Only the generated
+// phases and helpers touch them.
+
+// Operands of the main loop (see gen_fwd64.py): wave-uniform values first.
+struct Fwd64Loop {
+  float c;            // |scale| * log2(e) > 0
+  int32_t gstart;     // first iteration to run (-1: the pre-loop iteration)
+  int32_t nit;        // iterations of the work-group (the upper group's tiles)
+  int32_t nmy;        // tiles of this wave's group
+  int32_t elo;        // tiles of the first run (lower group: the light block)
+  int32_t jump;       // tile index minus position in the second run
+  int32_t blk0, blk1; // query block of the first / second run
+  int32_t wsub;       // which 64 rows of the block the wave holds
+  int32_t len;        // sequence length
+  int32_t gt;         // lower group's last light position (-2: none)
+  uint32_t tileb;     // bytes of 64 K / V rows
+  uint32_t nrec;      // bytes from the sequence's first K / V row to the end of its last
+  uint32_t m0b;       // LDS address of the wave's first load block in its group
+  uint32_t kbl, kbh, vbl, vbh;  // first K / V row of the sequence (this K/V head)
+  uint32_t copy;      // 1: this query head writes the K/V head's cache rows
+  uint32_t kcl, kch, vcl, vch;  // the sequence's cache rows of this K/V head
+  const uint16_t* qb; // first Q row of the sequence (this head)
+  uint32_t kb0, kb1, kb2, kb3;  // LDS read bases of the score operand
+  uint32_t vb0, vb1;            // LDS read bases of the PV operand
+  uint32_t fk0, fk1, fk2, fk3, fk4, fk5, fk6, fk7;  // lane offsets of the eight loads
+  int32_t vd;         // lane%32 - 4*(lane/32): diagonal mask threshold
+  uint32_t cl;        // LDS lane base of the cache copy
+  uint32_t crow;      // first tile row of the lane in the cache copy
+  uint32_t coe, coo;  // cache byte offsets of the copy's even / odd rows
+  uint32_t qo0, qo1;  // Q byte offsets of the heavy block's rows (halves 0, 1)
+};
+
+// Wave-uniform values for the asm statements' SGPR operands.
+__device__ __forceinline__ uint32_t sgpr_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float sgpr_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+template <class T>
+__device__ __forceinline__ const T* sgpr_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(lo | hi << 32);
+}
+
+#include "fwd64_phases.h"
+
+// Naming v255 and a255 makes the kernel's register count cover the fixed
+// registers (the compiler allocates none of them itself).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void claim_registers() { asm volatile("" ::: "v255", "a255"); }
+#pragma clang diagnostic pop
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ int chunk_slot(int r, int c) {
+  return c ^ ((((r & 3) << 1) | ((r >> 2) & 1)) & 15);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t two = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+// MFMA results are read by VALU instructions after this (accumulators of
+// the last PV phase).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory"); }
+
+__device__ __forceinline__ void end_interval() {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tiles have landed
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_fwd64_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  claim_registers();
+  const int h = __builtin_amdgcn_workgroup_id_x();
+  const int b = __builtin_amdgcn_workgroup_id_y();
+  const int z = __builtin_amdgcn_workgroup_id_z();
+  const int64_t H = p.num_heads;
+  const int64_t HK = p.num_kv_heads;
+  const int seq_start = p.cu[b];
+  const int len = p.cu[b + 1] - seq_start;
+  const int nqb = (len + kBM - 1) / kBM;
+  const int qb_hi = nqb - 1 - z;
+  if (z > qb_hi) return;  // no block pair left for this work-group (every wave returns)
+  const bool has_lo = z < qb_hi;
+  auto ntiles_of = [=](int qb) { return (min((qb + 1) * kBM, len) + kBN - 1) / kBN; };
+  const int e_lo = has_lo ? ntiles_of(z) : 0;
+  const int e_hi = ntiles_of(qb_hi);
+  const int n_up = (e_lo + e_hi + 1) / 2;
+  const int n_lo = e_lo + e_hi - n_up;
+
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int ql = lane & 31;
+  const int hl = lane >> 5;
+  const bool upper = wave < 2;
+  const int wsub = wave & 1;
+  const int group = upper ? 0 : 1;
+  // the group's tile sequence: upper: heavy block tiles 0 .. n_up-1; lower:
+  // light block tiles 0 .. e_lo-1, then heavy block tiles n_up .. e_hi-1
+  const int n_my = upper ? n_up : n_lo;
+  const bool transition = !upper && has_lo && n_lo > e_lo;
+
+  const int hk = h / (int)(H / HK);
+  const bool writes_cache = h == hk * (int)(H / HK);
+  const int64_t row_stride = HK * kD;  // elements between consecutive tokens of k, v
+  const uint16_t* kin = p.k + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
+  const uint16_t* vin = p.v + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
+  const int64_t cache_base = (int64_t)seq_start * HK * kD + (int64_t)hk * len * kD;
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t gbase = lds0 + group * kGroupBytes;
+  const uint32_t rs = (uint32_t)(row_stride * 2);
+  const uint32_t rsq = (uint32_t)(H * kD * 2);
+
+  Fwd64Loop L;
+  L.c = p.scale_log2;
+  L.nit = n_up;
+  L.nmy = n_my;
+  L.elo = upper ? n_my : e_lo;
+  L.jump = upper ? 0 : n_up - e_lo;
+  L.blk0 = (upper || !has_lo) ? qb_hi : z;
+  L.blk1 = qb_hi;
+  L.wsub = wsub;
+  L.len = len;
+  L.gt = transition ? e_lo - 1 : -2;
+  L.tileb = (uint32_t)kBN * rs;
+  L.nrec = (uint32_t)(len - 1) * rs + kRowBytes;
+  L.m0b = gbase + 1024u * wsub;
+  L.kbl = (uint32_t)(uintptr_t)kin;
+  L.kbh = (uint32_t)((uintptr_t)kin >> 32);
+  L.vbl = (uint32_t)(uintptr_t)vin;
+  L.vbh = (uint32_t)((uintptr_t)vin >> 32);
+  L.copy = writes_cache ? 1u : 0u;
+  uint16_t* kc = p.kc + cache_base;
+  uint16_t* vc = p.vc + cache_base;
+  L.kcl = (uint32_t)(uintptr_t)kc;
+  L.kch = (uint32_t)((uintptr_t)kc >> 32);
+  L.vcl = (uint32_t)(uintptr_t)vc;
+  L.vch = (uint32_t)((uintptr_t)vc >> 32);
+  L.qb = p.q + ((int64_t)seq_start * H + h) * kD;
+  L.kb0 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 0 + hl);
+  L.kb1 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 2 + hl);
+  L.kb2 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 4 + hl);
+  L.kb3 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 6 + hl);
+  {
+    const int tg = lane >> 4, tl = lane & 15;
+    const int vrow0 = 4 * (tg >> 1) + (tl >> 2);
+    const int vd0 = 16 * (tg & 1) + 4 * (tl & 3);
+    L.vb0 = gbase + vrow0 * kRowBytes + 16 * chunk_slot(vrow0, (vd0 >> 3) & 15) + 2 * (vd0 & 7);
+    const int d1 = 32 + vd0;
+    L.vb1 = gbase + vrow0 * kRowBytes + 16 * chunk_slot(vrow0, (d1 >> 3) & 15) + 2 * (d1 & 7);
+  }
+  // Loads: instruction i of a tile fills LDS block 2 i + wsub, rows
+  // 8 i + r0 with r0 = 4 wsub + lane/16; lane slot lane%16 takes source
+  // chunk chunk_slot(r0, slot) (the swizzle depends on the row mod 8 only).
+  const int r0 = 4 * wsub + (lane >> 4);
+  const uint32_t lane_chunk = 16u * (uint32_t)chunk_slot(r0, lane & 15);
+  uint32_t fk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fk[i] = (uint32_t)(8 * i + r0) * rs + lane_chunk;
+  L.fk0 = fk[0]; L.fk1 = fk[1]; L.fk2 = fk[2]; L.fk3 = fk[3];
+  L.fk4 = fk[4]; L.fk5 = fk[5]; L.fk6 = fk[6]; L.fk7 = fk[7];
+  L.vd = ql - 4 * hl;
+  // cache copy: the wave's rows 32 wsub + 4 i + lane/16 of a tile
+  {
+    const int crow = 32 * wsub + (lane >> 4);
+    const int slot = lane & 15;
+    L.cl = gbase + crow * kRowBytes + 16 * slot;
+    L.crow = crow;
+    L.coe = crow * kRowBytes + 16 * chunk_slot(crow, slot);
+    L.coo = crow * kRowBytes + 16 * chunk_slot(crow + 4, slot);
+  }
+  {
+    const int first = qb_hi * kBM + 64 * wsub;
+    L.qo0 = (uint32_t)min(first + ql, len - 1) * rsq + 16u * hl;
+    L.qo1 = (uint32_t)min(first + 32 + ql, len - 1) * rsq + 16u * hl;
+  }
+
+  // ---------------------------------------------------------------- prologue
+  // Q of the first block's rows (rows past the sequence read its last row);
+  // K of the group's first tile into K slot 0
+  {
+    const int first = (upper ? qb_hi : (has_lo ? z : qb_hi)) * kBM + 64 * wsub;
+    fwd64_load_q(L.qb, (uint32_t)min(first + ql, len - 1) * rsq + 16u * hl,
+                 (uint32_t)min(first + 32 + ql, len - 1) * rsq + 16u * hl);
+  }
+  fwd64_o_zero();
+  if (n_my > 0) {
+    const int t0 = upper || e_lo > 0 ? 0 : n_up;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kin + (int64_t)t0 * kBN * row_stride), (short)0, (int)(L.nrec - (uint32_t)t0 * L.tileb), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+          (__attribute__((address_space(3))) void*)(lds + group * kGroupBytes + 1024 * (2 * i + wsub)), 16, fk[i], 0, 0, 0);
+  }
+  end_interval();
+
+  // ---------------------------------------------------------------- loop
+  float m0 = kMInit, l0 = 0.f, m1 = kMInit, l1 = 0.f;   // halves 0 and 1
+  float m0n = kMInit, l0n = 0.f;                         // the light block's half 0 at the transition
+
+  // store one block's finished rows (this wave's 64): block i of O^T from
+  // get(i), divided by the row sums (per-lane halves la0, la1)
+  auto store_rows = [&](int qb, float la0, float la1, auto&& get) __attribute__((always_inline)) {
+    const int first = qb * kBM + 64 * wsub;
+    static_for<0, 2>([&](auto qh_tag) __attribute__((always_inline)) {
+      constexpr int qh = decltype(qh_tag)::value;
+      const float lsum = qh == 0 ? la0 : la1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+      const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+      const int row = first + 32 * qh + ql;
+      uint16_t* dst = p.out + ((int64_t)(seq_start + min(row, len - 1)) * H + h) * kD;
+      static_for<0, 4>([&](auto db_tag) __attribute__((always_inline)) {
+        constexpr int db = decltype(db_tag)::value;
+        const f32x16_t o = get(std::integral_constant<int, 4 * qh + db>{});
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp) {
+          // lane (row, hl) holds d = 32 db + 8 cc + 4 hl + [0, 4); lanes l and
+          // l^32 trade pieces so that each writes 8 consecutive d
+          const int ca = 2 * cp, cb = 2 * cp + 1;
+          const uint32_t a0 = pack_bf16x2(o[4 * ca + 0] * inv, o[4 * ca + 1] * inv);
+          const uint32_t a1 = pack_bf16x2(o[4 * ca + 2] * inv, o[4 * ca + 3] * inv);
+          const uint32_t b0 = pack_bf16x2(o[4 * cb + 0] * inv, o[4 * cb + 1] * inv);
+          const uint32_t b1 = pack_bf16x2(o[4 * cb + 2] * inv, o[4 * cb + 3] * inv);
+          const uint32_t s0 = hl ? a0 : b0, s1 = hl ? a1 : b1;
+          const auto x0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+          const uint32_t o0 = hl ? x0[0] : x0[1], o1 = hl ? x1[0] : x1[1];
+          const u32x4_t w = hl ? u32x4_t{o0, o1, b0, b1} : u32x4_t{a0, a1, o0, o1};
+          if (row < len) *(u32x4_t*)(dst + 32 * db + 8 * (hl ? cb : ca)) = w;
+        }
+      });
+    });
+  };
+  auto o_get = [](auto i_tag) __attribute__((always_inline)) { return fwd64_o_read<decltype(i_tag)::value>(); };
+
+  int g = -1;
+  for (;;) {
+    L.gstart = g;
+    g = fwd64_loop(L, m0, l0, m1, l1, m0n, l0n);
+    if (g >= n_up) break;
+    // the lower group's light block is finished (its half-0 state was moved
+    // to m0n, l0n when the heavy block's first tile started): store it and
+    // start the heavy block's half 1
+    mfma_drain();
+    store_rows(z, l0n, l1, o_get);
+    fwd64_o_zero();
+    m1 = kMInit;
+    l1 = 0.f;
+  }
+
+  // ---------------------------------------------------------------- merge
+  // lower group holds the heavy block's remaining tiles (n_lo > e_lo) or
+  // only the light block; the upper group the heavy block's first tiles
+  const bool merge = n_lo > e_lo;
+  mfma_drain();
+  if (!merge) {
+    if (upper) store_rows(qb_hi, l0, l1, o_get);
+    else if (n_lo > 0) store_rows(z, l0, l1, o_get);
+    return;
+  }
+  float* mbuf = reinterpret_cast<float*>(lds) + wsub * (4 + 128) * 64;
+  if (upper) {
+    mbuf[lane] = m0;
+    mbuf[64 + lane] = l0;
+    mbuf[128 + lane] = m1;
+    mbuf[192 + lane] = l1;
+    static_for<0, 8>([&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_tag)::value;
+      const f32x16_t o = fwd64_o_read<i>();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mbuf[(4 + 16 * i + r) * 64 + lane] = o[r];
+    });
+  }
+  __syncthreads();
+  if (!upper) {
+    const float um0 = mbuf[lane], ul0 = mbuf[64 + lane], um1 = mbuf[128 + lane], ul1 = mbuf[192 + lane];
+    const float mx0 = fmaxf(m0, um0), mx1 = fmaxf(m1, um1);
+    const float fa0 = __builtin_amdgcn_exp2f(m0 - mx0), fb0 = __builtin_amdgcn_exp2f(um0 - mx0);
+    const float fa1 = __builtin_amdgcn_exp2f(m1 - mx1), fb1 = __builtin_amdgcn_exp2f(um1 - mx1);
+    auto merged = [&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_tag)::value;
+      const float fa = i < 4 ? fa0 : fa1, fb = i < 4 ? fb0 : fb1;
+      f32x16_t o = fwd64_o_read<i>();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = o[r] * fa + mbuf[(4 + 16 * i + r) * 64 + lane] * fb;
+      return o;
+    };
+    store_rows(qb_hi, l0 * fa0 + ul0 * fb0, l1 * fa1 + ul1 * fb1, merged);
+  }
+}
+
+}  // namespace
+
+bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, int num_heads, int num_kv_heads) {
+  // lane offsets within a sequence are 32-bit: rows of q and of k / v
+  const int64_t row_bytes = (int64_t)2 * kD * (num_heads > num_kv_heads ? num_heads : num_kv_heads);
+  return head_dim == 128 && !chunked && scale >= 0.f && (int64_t)max_seqlen * row_bytes < ((int64_t)1 << 31);
+}
+
+hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream) {
+  dim3 grid(p.num_heads, num_seqs, p.grid_z);
+  hipLaunchKernelGGL(prefill_fwd64_kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,706 @@
+#!/usr/bin/env python3
+"""Writes fwd64_phases.h: the main loop of the 64-row-per-wave prefill
+attention kernel (fwd64.hip) as one hand-scheduled inline-asm statement for
+gfx950, plus the small helpers that reach its fixed registers.
+
+Run from anywhere: ``python gen_fwd64.py`` rewrites fwd64_phases.h beside it
+(the header is committed; a CPU test checks it matches this script).
+
+Fixed registers (the compiler allocates none of them; every statement that
+touches them names them as clobbered, and a CPU test checks the compiled
+kernel never uses them outside these statements):
+
+  a[64:191]   O^T accumulators, O[qh][db] = a[64 + 16*(4*qh+db) .. +15]
+              (qh: query half of 32 rows, db: block of 32 head-dim columns)
+  a[192:255]  Q^T MFMA operands, Q[qh][ds] = a[192 + 4*(8*qh+ds) .. +3]
+              (ds: 16-column step of the head dimension)
+  v[128:159]  SA: scores of query half 0 (key blocks 0, 1: 16 registers each)
+  v[160:191]  SB: scores of query half 1 for even iterations
+  v[192:223]  SC: scores of query half 1 for odd iterations
+  v[224:239]  PA0, v[240:255] PA1: bf16 weights P of half 0 (even / odd)
+  v[112:127]  PB: bf16 weights P of half 1
+  v[96:111]   four K operand slots, v[80:95] four V operand slots
+  v[64:79]    temporaries
+  s[64:67]    buffer descriptor of the K tile being loaded, s[68:71] of V
+  s[72:91]    loop bookkeeping
+
+Iteration g of the loop (T[g]: the g-th key tile of the wave's group):
+score phase: S(T[g+1]) = K Q^T on 32 MFMAs (both query halves share each K
+fragment read from LDS) beside the softmax of T[g] for rows 32..63, plus the
+loads of K(T[g+2]) and V(T[g+1]); cache copies of the tiles' own rows; PV
+phase: O^T += V^T P^T for T[g] on 32 MFMAs (both halves share each V
+fragment) beside the softmax of T[g+1] for rows 0..31; then a barrier.  The
+VALU work is spread over the MFMA slots by an issue-cost model measured on
+this part (an MFMA every 32 cycles leaves about 19 cycles of issue for other
+instructions of the same wave).
+"""
+from __future__ import annotations
+
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "fwd64_phases.h")
+
+V_SA, V_SB, V_SC = 128, 160, 192
+V_PA = (224, 240)
+V_PB = 112
+V_KF = 96
+V_VF = 80
+V_T = 64
+A_O = 64
+A_Q = 192
+
+# temporaries (v[64:79])
+T_MX0, T_MX1 = V_T + 0, V_T + 1     # row-max chains / permlane pair
+T_THR = V_T + 2                     # m + 8
+T_MNEW = V_T + 3
+T_ALPHA = V_T + 4                   # rescale factor (kept to the end of the phase)
+T_NINF = V_T + 5                    # -inf
+T_ROW = V_T + 6                     # cache-copy row
+T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
+
+# scalar registers of the loop
+S_VK = 64          # s[64:67] K descriptor
+S_VV = 68          # s[68:71] V descriptor
+S_G = 72           # iteration
+S_T0, S_T1, S_T2 = 73, 74, 75   # tiles of g, g+1, g+2
+S_B0, S_B1 = 76, 77             # blocks of g, g+1
+S_KS, S_KP = 78, 79             # softmax kinds: score phase (g), PV phase (g+1)
+S_OLIVE = 80
+S_FLAG = 81
+S_M0SAVE = 82
+S_X, S_Y = 83, 84               # scratch
+S_CB = 86          # s[86:87], s[88:89] cache-store bases
+S_EXEC = 90        # s[90:91] saved exec
+NUM_SGPR_FIXED = list(range(64, 92))
+
+K_SLOT_BYTES = 16384                # one 64 x 128 bf16 tile
+V_OFF = 32768                       # V ring after the K ring (per group)
+LOOKAHEAD = 3                       # operand fragments in flight
+ROWSTEP_LOADS = 8                   # global-to-LDS loads per wave and tile
+MINIT = "0xf149f2ca"                # -1e30: running max before the first tile
+
+MFMA = "v_mfma_f32_32x32x16_bf16"
+
+
+def vr(a, n=1):
+    return "v%d" % a if n == 1 else "v[%d:%d]" % (a, a + n - 1)
+
+
+def ar(a, n=1):
+    return "a%d" % a if n == 1 else "a[%d:%d]" % (a, a + n - 1)
+
+
+def sr(a, n=1):
+    return "s%d" % a if n == 1 else "s[%d:%d]" % (a, a + n - 1)
+
+
+def s_bank(par):
+    """Score registers of half 1 for iteration parity par."""
+    return V_SB if par == 0 else V_SC
+
+
+# ------------------------------------------------------------------ softmax
+def softmax_ops(kind, qh, sbase, pbase, m, l, tag):
+    """Online-softmax update of one query half over one 64-key tile.
+
+    sbase: 32 score registers (key block 0: sbase..+15, block 1: +16..+31);
+    the lane holds query row 32*qh + lane%32 and, in register r of key
+    block kb, key 32*kb + 8*(r/4) + 4*(lane/32) + r%4.  pbase: 16 registers
+    of bf16 pairs, P[k] = (p[2k], p[2k+1]) over the 32 scores in order, which
+    is the B-operand order of the PV MFMAs.  m, l: the half's running max
+    (exp2 domain) and per-lane partial sum.
+
+    kind: 'n' every key visible, 'd' the wave's diagonal tile (key k > row q
+    masked, both relative to the tile / the wave's first row), 'm' every key
+    masked (P = 0, state unchanged).
+
+    Returns a list of groups; a group's instructions are emitted together.
+    When some lane's running max moves, S_FLAG is set and l rescaled; the O
+    accumulators are rescaled at the end of the phase.
+    """
+    groups = []
+    if kind == 'm':
+        for k in range(16):
+            groups.append(["v_mov_b32 %s, 0" % vr(pbase + k)])
+        return groups
+    if kind == 'n':
+        live = list(range(32))
+        diag_regs = []
+    elif qh == 0:   # diagonal: key block 0 on the diagonal, block 1 above it
+        live = list(range(16))
+        diag_regs = list(range(16))
+    else:           # half 1: key block 0 below the diagonal, block 1 on it
+        live = list(range(32))
+        diag_regs = list(range(16, 32))
+    # causal mask on the diagonal key block: key offset o_r > d masked, with
+    # o_r = 8*(r/4) + r%4 and d = lane%32 - 4*(lane/32) (the same d for both
+    # halves, because each half's diagonal block starts at its first row)
+    for i in diag_regs:
+        r = i % 16
+        o = 8 * (r // 4) + r % 4
+        groups.append(["v_cmp_gt_i32 vcc, %d, %%[vd]" % o,
+                       "v_cndmask_b32 %s, %s, %s, vcc" % (vr(sbase + i), vr(sbase + i), vr(T_NINF))])
+    # row max over the live scores: two chains of v_max3, then the partner lane
+    chains = [live[:len(live) // 2], live[len(live) // 2:]]
+    for ci, ch in enumerate(chains):
+        t = T_MX0 + ci
+        groups.append(["v_max3_f32 %s, %s, %s, %s" % (vr(t), vr(sbase + ch[0]), vr(sbase + ch[1]), vr(sbase + ch[2]))])
+        rest = ch[3:]
+        while len(rest) >= 2:
+            groups.append(["v_max3_f32 %s, %s, %s, %s" % (vr(t), vr(t), vr(sbase + rest[0]), vr(sbase + rest[1]))])
+            rest = rest[2:]
+        if rest:
+            groups.append(["v_max_f32 %s, %s, %s" % (vr(t), vr(t), vr(sbase + rest[0]))])
+    groups.append(["v_max_f32 %s, %s, %s" % (vr(T_MX0), vr(T_MX0), vr(T_MX1)),
+                   "v_mov_b32 %s, %s" % (vr(T_MX1), vr(T_MX0)),
+                   "s_nop 1",
+                   "v_permlane32_swap_b32 %s, %s" % (vr(T_MX0), vr(T_MX1)),
+                   "s_nop 1",
+                   "v_max_f32 %s, %s, %s" % (vr(T_MX0), vr(T_MX0), vr(T_MX1)),
+                   # row max in the exp2 domain (c > 0)
+                   "v_mul_f32 %s, %%[c], %s" % (vr(T_MX0), vr(T_MX0)),
+                   "v_add_f32 %s, 0x41000000, %s" % (vr(T_THR), m)])
+    # lazy rescale: the running max moves only when a lane's tile max exceeds
+    # it by more than 8 (so p stays below 2^8); then l *= alpha now and O at
+    # the end of the phase
+    lbl = ".Lnr%s_%%=" % tag
+    groups.append(["v_cmp_gt_f32 vcc, %s, %s" % (vr(T_MX0), vr(T_THR)),
+                   "s_cbranch_vccz %s" % lbl,
+                   "v_max_f32 %s, %s, %s" % (vr(T_MNEW), m, vr(T_MX0)),
+                   "v_sub_f32 %s, %s, %s" % (vr(T_ALPHA), m, vr(T_MNEW)),
+                   "v_mov_b32 %s, %s" % (m, vr(T_MNEW)),
+                   "v_exp_f32 %s, %s" % (vr(T_ALPHA), vr(T_ALPHA)),
+                   "s_mov_b32 %s, 1" % sr(S_FLAG),
+                   "s_nop 1",
+                   "v_mul_f32 %s, %s, %s" % (l, l, vr(T_ALPHA)),
+                   "%s:" % lbl])
+    # p = 2^(s c - m), in place; P packed to bf16; l += p in fp32 (v_add:
+    # the dot-product form of the sum stalls beside the MFMAs on this part).
+    # Pipelined so that every exp result is read at least two instructions
+    # after the exp (transcendental results need a wait state).
+    order = live
+
+    def pack(k):
+        return [["v_cvt_pk_bf16_f32 %s, %s, %s" % (vr(pbase + k), vr(sbase + 2 * k), vr(sbase + 2 * k + 1))],
+                ["v_add_f32 %s, %s, %s" % (l, l, vr(sbase + 2 * k))],
+                ["v_add_f32 %s, %s, %s" % (l, l, vr(sbase + 2 * k + 1))]]
+    for idx, i in enumerate(order):
+        groups.append(["v_fma_f32 %s, %s, %%[c], -%s" % (vr(sbase + i), vr(sbase + i), m)])
+        if idx >= 1:
+            j = order[idx - 1]
+            groups.append(["v_exp_f32 %s, %s" % (vr(sbase + j), vr(sbase + j))])
+        if idx >= 2 and order[idx - 2] % 2 == 1:
+            groups += pack(order[idx - 2] // 2)
+    groups.append(["v_exp_f32 %s, %s" % (vr(sbase + order[-1]), vr(sbase + order[-1]))])
+    if order[-2] % 2 == 1:
+        groups += pack(order[-2] // 2)
+    groups.append(["s_nop 1"])
+    if order[-1] % 2 == 1:
+        groups += pack(order[-1] // 2)
+    # P of keys that take no part (block 1 of half 0 on the diagonal)
+    for k in range(16):
+        if 2 * k not in live:
+            groups.append(["v_mov_b32 %s, 0" % vr(pbase + k)])
+    return groups
+
+
+def o_rescale(qh, after_mfma, tag):
+    """O[qh] *= alpha when S_FLAG is set and S_OLIVE (O holds data)."""
+    lbl = ".Lor%s_%%=" % tag
+    out = ["s_and_b32 %s, %s, %s" % (sr(S_FLAG), sr(S_FLAG), sr(S_OLIVE)),
+           "s_cmp_eq_u32 %s, 0" % sr(S_FLAG),
+           "s_cbranch_scc1 %s" % lbl]
+    if after_mfma:
+        # the phase's last MFMAs write these accumulators
+        out += ["s_nop 7", "s_nop 7", "s_nop 7", "s_nop 7"]
+    regs = list(range(A_O + 64 * qh, A_O + 64 * qh + 64))
+    n = len(T_RS)
+    for b in range(0, 64, n):
+        chunk = regs[b:b + n]
+        for t, a in zip(T_RS, chunk):
+            out.append("v_accvgpr_read_b32 %s, %s" % (vr(t), ar(a)))
+        for t, a in zip(T_RS, chunk):
+            out.append("v_mul_f32 %s, %s, %s" % (vr(t), vr(t), vr(T_ALPHA)))
+        for t, a in zip(T_RS, chunk):
+            out.append("v_accvgpr_write_b32 %s, %s" % (ar(a), vr(t)))
+    out += ["s_nop 2", "%s:" % lbl]
+    return out
+
+
+# ------------------------------------------------------------------ schedule
+# Issue cost (cycles of the wave's issue beside a running MFMA) used to
+# spread the softmax over the MFMA slots.
+SLOT_BUDGET = 18
+
+
+def cost(ins):
+    op = ins.split()[0]
+    if op.startswith("v_exp"):
+        return 7
+    if op.startswith("s_nop"):
+        return int(ins.split()[1]) + 1
+    if op.startswith("v_permlane"):
+        return 4
+    if op.startswith(("v_add_f32", "v_mul_f32", "v_mov_b32", "v_cndmask", "v_cmp", "v_max_f32", "v_sub_f32")):
+        return 3
+    if op.startswith("v_"):
+        return 4
+    if op.startswith(("ds_", "buffer_", "global_")):
+        return 3
+    if op.endswith(":"):
+        return 0
+    return 1
+
+
+def gcost(g):
+    return sum(cost(x) for x in g)
+
+
+def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
+    """Interleave: before the MFMA pair of fragment f wait for its reads and
+    issue fragment f+LOOKAHEAD's; load group i goes after MFMA i; the filler
+    groups (softmax) fill each MFMA slot up to SLOT_BUDGET issue cycles, in
+    order (raised when the rest would not fit; what is left follows the last
+    MFMA)."""
+    nfrag = len(frag_reads)
+    out = []
+    for f in range(min(LOOKAHEAD, nfrag)):
+        out += frag_reads[f]
+    issued = min(LOOKAHEAD, nfrag)
+    nslots = len(mfmas)
+    load_at = {i: g for i, g in enumerate(loadg)}
+    fi = 0
+    for s, (mf, f) in enumerate(mfmas):
+        used = 0
+        if s % 2 == 0:
+            pending = (issued - 1 - f) * reads_per_frag
+            out.append("s_waitcnt lgkmcnt(%d)" % pending)
+            used += 1
+            if issued < nfrag:
+                out += frag_reads[issued]
+                used += gcost(frag_reads[issued])
+                issued += 1
+        out.append(mf)
+        if s in load_at:
+            out += load_at[s]
+            used += gcost(load_at[s])
+        left = nslots - s
+        rest = sum(gcost(g) for g in fillers[fi:])
+        target = max(SLOT_BUDGET, used + rest / left)
+        placed = False
+        while fi < len(fillers):
+            c = gcost(fillers[fi])
+            if placed and used + c > target:
+                break
+            out += fillers[fi]
+            used += c
+            fi += 1
+            placed = True
+    while fi < len(fillers):
+        out += fillers[fi]
+        fi += 1
+    return out
+
+
+# ------------------------------------------------------------------ phases
+def loads(par, matrix):
+    """This wave's eight 1 KB global-to-LDS loads of the next K or V tile,
+    both issued in the score phase of iteration g: K(T[g+2]) into K slot
+    g % 2, V(T[g+1]) into V slot (g+1) % 2 (their previous tiles were last
+    read before the previous interval's barrier).  Instruction i fills LDS
+    block 2*i + wsub of the slot (M0 = %[m0b] + offset) from the tile's
+    buffer descriptor + %[fk<i>] (rows 8*i + 4*wsub + lane/16); rows past the
+    sequence are out of the descriptor's range and read as zero."""
+    groups = []
+    if matrix == 'k':
+        slot_off = par * K_SLOT_BYTES
+        desc = sr(S_VK, 4)
+    else:
+        slot_off = V_OFF + (1 - par) * K_SLOT_BYTES
+        desc = sr(S_VV, 4)
+    for i in range(ROWSTEP_LOADS):
+        groups.append(["s_add_u32 m0, %%[m0b], %d" % (slot_off + 2048 * i),
+                       "s_nop 0",
+                       "buffer_load_dwordx4 %%[fk%d], %s, 0 offen lds" % (i, desc)])
+    return groups
+
+
+def score_phase(par, kind, has_s, tag):
+    """Score phase of an iteration of parity par: S(T[g+1]) (if has_s) beside
+    softmax(T[g], half 1) of the given kind ('x': none), loads of K(T[g+2])
+    and V(T[g+1])."""
+    body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
+            "s_mov_b32 %s, 0" % sr(S_FLAG)]
+    fill = softmax_ops(kind, 1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1") if kind != 'x' else []
+    k_l, v_l = loads(par, 'k'), loads(par, 'v')
+    loadg = [x for pair in zip(k_l, v_l) for x in pair]
+    if has_s:
+        kslot = (1 - par) * K_SLOT_BYTES          # K(T[g+1]) in slot (g+1) % 2
+        nb = s_bank(1 - par)                      # half-1 scores of T[g+1]
+        frag_reads = []
+        mfmas = []
+        for ds in range(8):
+            for kb in range(2):
+                f = 2 * ds + kb
+                slot = V_KF + 4 * (f % 4)
+                off = kslot + 128 * (ds >> 2) + kb * 32 * 256
+                frag_reads.append(["ds_read_b128 %s, %%[kb%d] offset:%d" % (vr(slot, 4), ds & 3, off)])
+                for qh in range(2):
+                    dst = (V_SA if qh == 0 else nb) + 16 * kb
+                    src_c = "0" if ds == 0 else vr(dst, 16)
+                    mfmas.append(("%s %s, %s, %s, %s" % (MFMA, vr(dst, 16), vr(slot, 4),
+                                                         ar(A_Q + 4 * (8 * qh + ds), 4), src_c), f))
+        body += schedule(mfmas, frag_reads, 1, fill, loadg)
+    else:
+        for g in fill:
+            body += g
+        for g in loadg:
+            body += g
+    if kind in ('n', 'd'):
+        body += o_rescale(1, after_mfma=False, tag=tag)
+    return body
+
+
+def pv_phase(par, kind, has_pv, tag):
+    """PV phase of an iteration of parity par: O += P(T[g]) V(T[g]) (if
+    has_pv) beside softmax(T[g+1], half 0) of the given kind ('x': none)."""
+    body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
+            "s_mov_b32 %s, 0" % sr(S_FLAG)]
+    fill = softmax_ops(kind, 0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0") if kind != 'x' else []
+    if has_pv:
+        vslot = V_OFF + par * K_SLOT_BYTES          # V(T[g]) in slot g % 2
+        frag_reads = []
+        mfmas = []
+        for gg in range(4):
+            for db in range(4):
+                f = 4 * gg + db
+                slot = V_VF + 4 * (f % 4)
+                off = vslot + 128 * (db >> 1) + 4096 * gg
+                frag_reads.append(["ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot, 2), db & 1, off),
+                                   "ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot + 2, 2), db & 1, off + 2048)])
+                for qh in range(2):
+                    o = A_O + 16 * (4 * qh + db)
+                    pb = (V_PA[par] if qh == 0 else V_PB) + 4 * gg
+                    mfmas.append(("%s %s, %s, %s, %s" % (MFMA, ar(o, 16), vr(slot, 4), vr(pb, 4), ar(o, 16)), f))
+        body += ["s_nop 1"]   # the weights were written by VALU instructions
+        body += schedule(mfmas, frag_reads, 2, fill, [])
+    else:
+        for g in fill:
+            body += g
+    if kind in ('n', 'd'):
+        body += o_rescale(0, after_mfma=has_pv, tag=tag)
+    return body
+
+
+# ------------------------------------------------------------------ the loop
+def tile_of(x, t, b):
+    """t = T[x], b = block of T[x]: light run (x < elo) or heavy run."""
+    return ["s_cmp_lt_i32 %s, %%[elo]" % x,
+            "s_cselect_b32 %s, 0, %%[jump]" % sr(S_Y),
+            "s_cselect_b32 %s, %%[blk0], %%[blk1]" % sr(b),
+            "s_add_i32 %s, %s, %s" % (sr(t), x, sr(S_Y))]
+
+
+def kind_of(t, b, dst):
+    """dst = 0 if tile t is below the wave's diagonal tile of block b, 1 on
+    it, 2 above it (diagonal tile 2 b + wsub)."""
+    return ["s_lshl_b32 %s, %s, 1" % (sr(S_Y), sr(b)),
+            "s_add_i32 %s, %s, %%[wsub]" % (sr(S_Y), sr(S_Y)),
+            "s_cmp_lt_i32 %s, %s" % (sr(t), sr(S_Y)),
+            "s_cselect_b32 %s, 0, 1" % sr(dst),
+            "s_cmp_gt_i32 %s, %s" % (sr(t), sr(S_Y)),
+            "s_cselect_b32 %s, 2, %s" % (sr(dst), sr(dst))]
+
+
+def descriptor(t, d, lo, hi):
+    """Buffer descriptor of tile t's rows: base + t * tile bytes, range to
+    the end of the sequence's rows."""
+    return ["s_mul_i32 %s, %s, %%[tileb]" % (sr(S_Y), sr(t)),
+            "s_add_u32 %s, %%[%s], %s" % (sr(d), lo, sr(S_Y)),
+            "s_addc_u32 %s, %%[%s], 0" % (sr(d + 1), hi),
+            "s_sub_u32 %s, %%[nrec], %s" % (sr(d + 2), sr(S_Y))]
+
+
+def cache_copy(par, matrix, tag):
+    """Copy this wave's 32 rows (32 wsub + 4 i + lane/16, i < 8) of the K
+    tile T[g+1] (K slot (g+1) % 2) or the V tile T[g] (V slot g % 2) from LDS
+    to the cache, rows past the sequence masked.  The tile is in S_T1 (K) or
+    S_T0 (V)."""
+    if matrix == 'k':
+        slot_off, t, lo, hi = (1 - par) * K_SLOT_BYTES, S_T1, "kcl", "kch"
+    else:
+        slot_off, t, lo, hi = V_OFF + par * K_SLOT_BYTES, S_T0, "vcl", "vch"
+    out = []
+    regs = [V_VF + 4 * i for i in range(4)] + [V_KF + 4 * i for i in range(4)]
+    for i in range(8):
+        out.append("ds_read_b128 %s, %%[cl] offset:%d" % (vr(regs[i], 4), slot_off + 1024 * i))
+    # store bases: cache + 64 t rows (256 B each), and 4 KB past it
+    out += ["s_lshl_b32 %s, %s, 14" % (sr(S_Y), sr(t)),
+            "s_add_u32 %s, %%[%s], %s" % (sr(S_CB), lo, sr(S_Y)),
+            "s_addc_u32 %s, %%[%s], 0" % (sr(S_CB + 1), hi),
+            "s_add_u32 %s, %s, 4096" % (sr(S_CB + 2), sr(S_CB)),
+            "s_addc_u32 %s, %s, 0" % (sr(S_CB + 3), sr(S_CB + 1)),
+            # rows of the tile that exist: len - 64 t
+            "s_lshl_b32 %s, %s, 6" % (sr(S_Y), sr(t)),
+            "s_sub_i32 %s, %%[len], %s" % (sr(S_Y), sr(S_Y)),
+            "s_mov_b64 %s, exec" % sr(S_EXEC, 2),
+            "s_waitcnt lgkmcnt(0)"]
+    for i in range(8):
+        base = sr(S_CB, 2) if i < 4 else sr(S_CB + 2, 2)
+        off = 1024 * (i % 4)
+        coff = "%[coe]" if i % 2 == 0 else "%[coo]"
+        out += ["v_add_u32 %s, %d, %%[crow]" % (vr(T_ROW), 4 * i),
+                "v_cmp_gt_i32 vcc, %s, %s" % (sr(S_Y), vr(T_ROW)),
+                "s_and_b64 exec, %s, vcc" % sr(S_EXEC, 2),
+                "global_store_dwordx4 %s, %s, %s offset:%d nt" % (coff, vr(regs[i], 4), base, off)]
+    out += ["s_mov_b64 exec, %s" % sr(S_EXEC, 2)]
+    return out
+
+
+def q_reload():
+    """The heavy block's Q rows into the Q registers (lower group, after the
+    last light score tile); waited for by the interval's vmcnt(0)."""
+    out = []
+    for qh in range(2):
+        for ds in range(8):
+            out.append("global_load_dwordx4 %s, %%[qo%d], %%[qb] offset:%d" % (ar(A_Q + 4 * (8 * qh + ds), 4), qh, 32 * ds))
+    return out
+
+
+def body(par):
+    """One iteration (parity par) for g = S_G, ending after its barrier."""
+    P = "p%d" % par
+    out = []
+
+    def L(name):
+        return ".L%s_%s_%%=" % (name, P)
+    g = sr(S_G)
+    # a group past its tiles only meets the barrier
+    out += ["s_cmp_ge_i32 %s, %%[nmy]" % g,
+            "s_cbranch_scc1 %s" % L("bar")]
+    # T[g+1], its block, the PV-phase kind
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g)] + tile_of(sr(S_X), S_T1, S_B1)
+    out += ["s_mov_b32 %s, 3" % sr(S_KP),
+            "s_cmp_lt_i32 %s, %%[nmy]" % sr(S_X),
+            "s_cbranch_scc0 %s" % L("kp")] + kind_of(S_T1, S_B1, S_KP) + ["%s:" % L("kp")]
+    # T[g] (T[0] for the pre-loop iteration), its block, the score-phase kind
+    out += ["s_max_i32 %s, %s, 0" % (sr(S_X), g)] + tile_of(sr(S_X), S_T0, S_B0)
+    out += ["s_mov_b32 %s, 3" % sr(S_KS),
+            "s_cmp_lt_i32 %s, 0" % g,
+            "s_cbranch_scc1 %s" % L("ks")] + kind_of(S_T0, S_B0, S_KS) + ["%s:" % L("ks")]
+    # T[g+2] (or T[g] again: a load with no tile to fetch refills a free slot)
+    out += ["s_add_i32 %s, %s, 2" % (sr(S_X), g),
+            "s_cmp_lt_i32 %s, %%[nmy]" % sr(S_X),
+            "s_cbranch_scc1 %s" % L("t2"),
+            "s_mov_b32 %s, %s" % (sr(S_T2), sr(S_T0)),
+            "s_branch %s" % L("t2d"),
+            "%s:" % L("t2")] + tile_of(sr(S_X), S_T2, S_FLAG) + ["%s:" % L("t2d")]
+    # descriptors: K(T[g+2]), V(T[g+1]) (or V(T[g]) when there is no g+1)
+    out += descriptor(S_T2, S_VK, "kbl", "kbh")
+    out += ["s_cmp_eq_u32 %s, 3" % sr(S_KP),
+            "s_cselect_b32 %s, %s, %s" % (sr(S_X), sr(S_T0), sr(S_T1))]
+    out += descriptor(S_X, S_VV, "vbl", "vbh")
+    # olive of the score phase: T[g] is not the first tile of its run
+    out += ["s_cmp_eq_u32 %s, 0" % g,
+            "s_cselect_b32 %s, 0, 1" % sr(S_OLIVE),
+            "s_cmp_eq_u32 %s, %%[elo]" % g,
+            "s_cselect_b32 %s, 0, %s" % (sr(S_OLIVE), sr(S_OLIVE))]
+    # ---- score phase: dispatch on (has S = kind of g+1 != 3, kind of g)
+    kidx = {'n': 0, 'd': 1, 'm': 2, 'x': 3}
+    out += ["s_cmp_eq_u32 %s, 3" % sr(S_KP),
+            "s_cbranch_scc1 %s" % L("s_noS")]
+    for kind in ('n', 'd', 'm'):
+        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KS), kidx[kind]),
+                "s_cbranch_scc1 %s" % L("s_%s_S" % kind)]
+    out += ["s_branch %s" % L("s_x_S"), "%s:" % L("s_noS")]
+    for kind in ('n', 'd'):
+        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KS), kidx[kind]),
+                "s_cbranch_scc1 %s" % L("s_%s_noS" % kind)]
+    out += ["s_branch %s" % L("s_m_noS")]
+    for has_s in (True, False):
+        for kind in ('n', 'd', 'm', 'x'):
+            if kind == 'x' and not has_s:
+                continue
+            nm = "s_%s_%s" % (kind, "S" if has_s else "noS")
+            out += ["%s:" % L(nm)]
+            out += score_phase(par, kind, has_s, nm + P)
+            out += ["s_branch %s" % L("sdone")]
+    out += ["%s:" % L("sdone")]
+    # ---- the heavy block's Q after the last light score tile
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
+            "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
+            "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
+    # ---- cache copies of own rows: K(T[g+1]), V(T[g])
+    out += ["s_cmp_eq_u32 %[copy], 0",
+            "s_cbranch_scc1 %s" % L("nocv"),
+            "s_cmp_eq_u32 %s, 3" % sr(S_KP),
+            "s_cbranch_scc1 %s" % L("nock"),
+            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(S_T1)),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(S_B1)),
+            "s_cbranch_scc0 %s" % L("nock")] + cache_copy(par, 'k', P) + ["%s:" % L("nock")]
+    out += ["s_cmp_lt_i32 %s, 0" % g,
+            "s_cbranch_scc1 %s" % L("nocv"),
+            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(S_T0)),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(S_B0)),
+            "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv")]
+    # ---- at the last light tile the next tile's half-0 softmax starts the
+    # heavy block's state; the light block's is kept for its store
+    out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
+            "s_cbranch_scc0 %s" % L("notr"),
+            "v_mov_b32 %[m0n], %[m0v]",
+            "v_mov_b32 %[l0n], %[l0v]",
+            "v_mov_b32 %%[m0v], %s" % MINIT,
+            "v_mov_b32 %[l0v], 0",
+            "%s:" % L("notr")]
+    # olive of the PV phase: T[g+1] is not the first tile of its run
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
+            "s_cmp_eq_u32 %s, 0" % sr(S_X),
+            "s_cselect_b32 %s, 0, 1" % sr(S_OLIVE),
+            "s_cmp_eq_u32 %s, %%[elo]" % sr(S_X),
+            "s_cselect_b32 %s, 0, %s" % (sr(S_OLIVE), sr(S_OLIVE))]
+    # ---- PV phase: dispatch on (has PV = g >= 0, kind of g+1)
+    out += ["s_cmp_lt_i32 %s, 0" % g,
+            "s_cbranch_scc1 %s" % L("p_noPV")]
+    for kind in ('n', 'd', 'm'):
+        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KP), kidx[kind]),
+                "s_cbranch_scc1 %s" % L("p_%s_PV" % kind)]
+    out += ["s_branch %s" % L("p_x_PV"), "%s:" % L("p_noPV")]
+    for kind in ('n', 'd'):
+        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KP), kidx[kind]),
+                "s_cbranch_scc1 %s" % L("p_%s_noPV" % kind)]
+    out += ["s_branch %s" % L("p_m_noPV")]
+    for has_pv in (True, False):
+        for kind in ('n', 'd', 'm', 'x'):
+            if kind == 'x' and not has_pv:
+                continue
+            nm = "p_%s_%s" % (kind, "PV" if has_pv else "noPV")
+            out += ["%s:" % L(nm)]
+            out += pv_phase(par, kind, has_pv, nm + P)
+            out += ["s_branch %s" % L("pdone")]
+    out += ["%s:" % L("pdone")]
+    # ---- end of the interval: this wave's loads have landed; everyone's have
+    out += ["%s:" % L("bar"),
+            "s_waitcnt vmcnt(0) lgkmcnt(0)",
+            "s_barrier"]
+    return out
+
+
+LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt",
+                "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
+LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
+                "fk6", "fk7", "vd", "cl", "crow", "coe", "coo", "qo0", "qo1"]
+
+
+def loop_text():
+    """Iterations S_G = gstart .. nit-1 (gstart may be -1: the pre-loop
+    iteration), leaving after the transition iteration gt (returns gt + 1)
+    or after the last (returns nit)."""
+    out = ["s_mov_b32 %s, m0" % sr(S_M0SAVE),
+           "s_mov_b32 %s, 0x20000" % sr(S_VK + 3),
+           "s_mov_b32 %s, 0x20000" % sr(S_VV + 3),
+           "s_mov_b32 %s, %%[gstart]" % sr(S_G),
+           "s_bitcmp1_b32 %s, 0" % sr(S_G),
+           "s_cbranch_scc0 .Leven_%="]
+    out += [".Lodd_%=:"]
+    out += body(1)
+    out += ["s_cmp_eq_u32 %s, %%[gt]" % sr(S_G),
+            "s_cbranch_scc1 .Ltrans_%=",
+            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
+            "s_cmp_ge_i32 %s, %%[nit]" % sr(S_G),
+            "s_cbranch_scc1 .Lend_%="]
+    out += [".Leven_%=:"]
+    out += body(0)
+    out += ["s_cmp_eq_u32 %s, %%[gt]" % sr(S_G),
+            "s_cbranch_scc1 .Ltrans_%=",
+            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
+            "s_cmp_ge_i32 %s, %%[nit]" % sr(S_G),
+            "s_cbranch_scc0 .Lodd_%=",
+            "s_branch .Lend_%=",
+            ".Ltrans_%=:",
+            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
+            ".Lend_%=:",
+            "s_mov_b32 %%[gout], %s" % sr(S_G),
+            "s_mov_b32 m0, %s" % sr(S_M0SAVE)]
+    return out
+
+
+FIXED_CLOBBERS = ", ".join('"v%d"' % r for r in range(V_T, 256)) + ", " + ", ".join('"a%d"' % r for r in range(A_O, 256))
+SGPR_CLOBBERS = ", ".join('"s%d"' % r for r in NUM_SGPR_FIXED)
+
+
+def loop_function():
+    lines = ["// Main loop: iterations gstart .. nit-1 of this wave (see gen_fwd64.py);",
+             "// returns the next iteration (gt + 1 after the transition iteration gt).",
+             "__device__ __forceinline__ int fwd64_loop(const Fwd64Loop& L, float& m0v, float& l0v, float& m1v,",
+             "                                          float& l1v, float& m0n, float& l0n) {",
+             "  int gout;",
+             "  asm volatile("]
+    for ins in loop_text():
+        lines.append('      "%s\\n"' % ins.replace('"', '\\"'))
+    outs = ['[gout] "=s"(gout)', '[m0v] "+v"(m0v)', '[l0v] "+v"(l0v)', '[m1v] "+v"(m1v)', '[l1v] "+v"(l1v)',
+            '[m0n] "+v"(m0n)', '[l0n] "+v"(l0n)']
+    ins = ['[c] "s"(sgpr_f32(L.c))'] + ['[%s] "s"(sgpr_u32(L.%s))' % (n, n) for n in LOOP_SGPR_IN]
+    ins += ['[qb] "s"(sgpr_ptr(L.qb))']
+    ins += ['[%s] "v"(L.%s)' % (n, n) for n in LOOP_VGPR_IN]
+    lines.append("      : " + ", ".join(outs))
+    lines.append("      : " + ", ".join(ins))
+    lines.append('      : "vcc", "scc", "memory", ' + SGPR_CLOBBERS + ", " + FIXED_CLOBBERS + ");")
+    lines.append("  return gout;")
+    lines.append("}")
+    return "\n".join(lines)
+
+
+def helpers():
+    """Access to the fixed registers from the kernel's C++ code."""
+    out = []
+    lines = ["__device__ __forceinline__ void fwd64_o_zero() {", "  asm volatile("]
+    for r in range(A_O, A_O + 128):
+        lines.append('      "v_accvgpr_write_b32 %s, 0\\n"' % ar(r))
+    lines.append('      ::: "memory", ' + FIXED_CLOBBERS + ');')
+    lines.append("}")
+    out.append("\n".join(lines))
+    # block i of O^T (16 accumulators) into VGPRs of the compiler's choice
+    out.append("template <int I>\n__device__ __forceinline__ f32x16_t fwd64_o_read();")
+    for i in range(8):
+        lines = ["template <>", "__device__ __forceinline__ f32x16_t fwd64_o_read<%d>() {" % i,
+                 "  float r[16];", "  asm volatile("]
+        for k in range(16):
+            lines.append('      "v_accvgpr_read_b32 %%[r%d], %s\\n"' % (k, ar(A_O + 16 * i + k)))
+        lines.append("      : " + ", ".join('[r%d] "=v"(r[%d])' % (k, k) for k in range(16)))
+        lines.append("      :: " + FIXED_CLOBBERS + ");")
+        lines += ["  f32x16_t v;", "  for (int k = 0; k < 16; ++k) v[k] = r[k];", "  return v;", "}"]
+        out.append("\n".join(lines))
+    # Q^T of 64 rows straight into the Q registers: lane l holds row
+    # 32*qh + l%32, columns 16*ds + 8*(l/32) .. +8; base: the rows' first
+    # element, off0/off1: byte offsets of the lane's rows of half 0 / 1
+    # (8*(l/32) columns included).  Waited for by the caller's vmcnt(0).
+    lines = ["__device__ __forceinline__ void fwd64_load_q(const uint16_t* base, uint32_t off0, uint32_t off1) {",
+             "  asm volatile("]
+    for qh in range(2):
+        for ds in range(8):
+            lines.append('      "global_load_dwordx4 %s, %%[o%d], %%[b] offset:%d\\n"' % (ar(A_Q + 4 * (8 * qh + ds), 4), qh, 32 * ds))
+    lines.append('      :: [b] "s"(sgpr_ptr(base)), [o0] "v"(off0), [o1] "v"(off1) : "memory", ' + FIXED_CLOBBERS + ');')
+    lines.append("}")
+    out.append("\n".join(lines))
+    return out
+
+
+def main():
+    parts = ["// fwd64_phases.h -- generated by gen_fwd64.py; do not edit by hand.",
+             "// Main loop of the 64-row-per-wave attention kernel (fwd64.hip) and the",
+             "// helpers that reach its fixed registers.",
+             "#pragma once",
+             ""]
+    for h in helpers():
+        parts.append(h)
+        parts.append("")
+    parts.append(loop_function())
+    return "\n".join(parts) + "\n"
+
+
+if __name__ == "__main__":
+    t = main()
+    with open(OUT, "w") as f:
+        f.write(t)
+    print("wrote", OUT, len(t.splitlines()), "lines")

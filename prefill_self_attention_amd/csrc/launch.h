@@ -61,6 +61,10 @@ int fwd_grid_blocks(int max_seqlen);
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream);
+// Varlen, head_dim 128, bf16 cache, scale >= 0: the 64-row-per-wave kernel
+// (fwd64.hip), same grid and contract as launch_prefill_fwd.
+bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, int num_heads, int num_kv_heads);
+hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream);
 // Varlen with an INT8 or an FP8 (E4M3) cache (kq, vq, ks, vs instead of kc, vc).
 hipError_t launch_prefill_fwd_fp8(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,

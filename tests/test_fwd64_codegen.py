@@ -1,0 +1,90 @@
+"""CPU checks of the 64-row-per-wave kernel's generated code (fwd64.hip).
+
+The kernel keeps its state in registers the compiler never allocates: the
+asm statements of fwd64_phases.h name them directly.  These tests check that
+the committed header is what gen_fwd64.py writes, and that in the compiled
+kernel no instruction outside those asm statements touches the fixed
+registers (v112-v255: scores, weights; a64-a255: O and Q), with no register
+spills or private memory.
+"""
+import importlib.util
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "prefill_self_attention_amd", "csrc")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("gen_fwd64", os.path.join(CSRC, "gen_fwd64.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_generated_header_matches_generator():
+    text = _gen().main()
+    with open(os.path.join(CSRC, "fwd64_phases.h")) as f:
+        assert f.read() == text, "fwd64_phases.h is stale: run gen_fwd64.py"
+
+
+def test_schedule_keeps_every_instruction_once():
+    g = _gen()
+    # every softmax / load instruction of a phase appears in its schedule
+    for par in (0, 1):
+        for kind in ("n", "d", "m"):
+            body = g.score_phase(par, kind, True, "t")
+            fill = g.softmax_ops(kind, 1, g.s_bank(par), g.V_PB, "%[m1v]", "%[l1v]", "th1")
+            flat = [x for grp in fill for x in grp]
+            for ins in flat:
+                if not ins.startswith("s_nop"):
+                    assert body.count(ins) >= flat.count(ins), ins
+            assert sum(1 for x in body if x.startswith("v_mfma")) == 32
+            assert sum(1 for x in body if x.startswith("buffer_load")) == 16
+            pv = g.pv_phase(par, kind, True, "t")
+            assert sum(1 for x in pv if x.startswith("v_mfma")) == 32
+            assert sum(1 for x in pv if x.startswith("ds_read_b64_tr_b16")) == 32
+
+
+def _hipcc():
+    p = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return p if os.path.exists(p) else shutil.which("hipcc")
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_compiled_kernel_keeps_off_fixed_registers(tmp_path):
+    out = tmp_path / "fwd64.s"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fno-honor-nans", "-mno-amdgpu-ieee",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, "fwd64.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = out.read_text()
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", text)
+    assert re.search(r"\.vgpr_spill_count:\s+0\b", text)
+    assert re.search(r"\.sgpr_spill_count:\s+0\b", text)
+    assert re.search(r"\.vgpr_count:\s+512\b", text), "the kernel must claim all 512 registers"
+    inasm = False
+    bad = []
+    for line in text.splitlines():
+        if "ASMSTART" in line:
+            inasm = True
+            continue
+        if "ASMEND" in line:
+            inasm = False
+            continue
+        s = line.strip()
+        if inasm or not s or s.startswith((";", ".")):
+            continue
+        for m in re.finditer(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b", s):
+            kind, hi = (m.group(1), int(m.group(3))) if m.group(1) else (m.group(4), int(m.group(5)))
+            lo = int(m.group(2)) if m.group(1) else hi
+            if (kind == "v" and hi >= 112) or (kind == "a" and hi >= 64):
+                bad.append(s)
+                break
+            del lo
+    assert not bad, "compiler code touches the fixed registers:\n" + "\n".join(bad[:10])
