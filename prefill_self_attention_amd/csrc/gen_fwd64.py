@@ -59,20 +59,34 @@ T_NINF = V_T + 5                    # -inf
 T_ROW = V_T + 6                     # cache-copy row
 T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
 
-# scalar registers of the loop
+# scalar registers of the loop.  Pairs alternate with the iteration's
+# parity: iteration g of parity par = g % 2 reads T[g] from S_TT[par] and
+# T[g+1] from S_TT[1 - par], so T[g+1] is already in place for g + 1.
 S_VK = 64          # s[64:67] K descriptor
 S_VV = 68          # s[68:71] V descriptor
 S_G = 72           # iteration
-S_T0, S_T1, S_T2 = 73, 74, 75   # tiles of g, g+1, g+2
-S_B0, S_B1 = 76, 77             # blocks of g, g+1
-S_KS, S_KP = 78, 79             # softmax kinds: score phase (g), PV phase (g+1)
-S_OLIVE = 80
+S_TT = (73, 74)    # tiles T[g], T[g+1]
+S_T2 = 75          # tile whose K is loaded in the iteration (T[g+2])
+S_BB = (76, 77)    # blocks of T[g], T[g+1]
+S_KK = (78, 79)    # softmax kinds: of T[g] (score phase), of T[g+1] (PV phase)
+S_OO = (80, 92)    # olive flags (O holds data) of the score phase, of the PV phase
 S_FLAG = 81
 S_M0SAVE = 82
 S_X, S_Y = 83, 84               # scratch
 S_CB = 86          # s[86:87], s[88:89] cache-store bases
 S_EXEC = 90        # s[90:91] saved exec
-NUM_SGPR_FIXED = list(range(64, 92))
+S_SPEC = 93        # nonzero: the iteration takes the out-of-line middle part
+S_CS = 94          # score-phase variant: 0 the common one (all keys visible, a next tile)
+S_CP = 95          # PV-phase variant: 0 the common one
+S_NX, S_NY, S_NZ = 96, 97, 98   # scratch of the next iteration's bookkeeping
+NUM_SGPR_FIXED = list(range(64, 99))
+
+
+def roles(par):
+    """Registers of an iteration of parity par."""
+    return dict(T0=S_TT[par], T1=S_TT[1 - par], B0=S_BB[par], B1=S_BB[1 - par],
+                KS=S_KK[par], KP=S_KK[1 - par], OS=S_OO[par], OP=S_OO[1 - par])
+
 
 K_SLOT_BYTES = 16384                # one 64 x 128 bf16 tile
 V_OFF = 32768                       # V ring after the K ring (per group)
@@ -205,10 +219,11 @@ def softmax_ops(kind, qh, sbase, pbase, m, l, tag):
     return groups
 
 
-def o_rescale(qh, after_mfma, tag):
-    """O[qh] *= alpha when S_FLAG is set and S_OLIVE (O holds data)."""
+def o_rescale(qh, after_mfma, tag, olive):
+    """O[qh] *= alpha when S_FLAG is set and the olive register is (O holds
+    data)."""
     lbl = ".Lor%s_%%=" % tag
-    out = ["s_and_b32 %s, %s, %s" % (sr(S_FLAG), sr(S_FLAG), sr(S_OLIVE)),
+    out = ["s_and_b32 %s, %s, %s" % (sr(S_FLAG), sr(S_FLAG), sr(olive)),
            "s_cmp_eq_u32 %s, 0" % sr(S_FLAG),
            "s_cbranch_scc1 %s" % lbl]
     if after_mfma:
@@ -329,7 +344,7 @@ def loads(par, matrix):
 def score_phase(par, kind, has_s, tag):
     """Score phase of an iteration of parity par: S(T[g+1]) (if has_s) beside
     softmax(T[g], half 1) of the given kind ('x': none), loads of K(T[g+2])
-    and V(T[g+1])."""
+    and V(T[g+1]) (descriptors S_VK, S_VV)."""
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
     fill = softmax_ops(kind, 1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1") if kind != 'x' else []
@@ -358,16 +373,34 @@ def score_phase(par, kind, has_s, tag):
         for g in loadg:
             body += g
     if kind in ('n', 'd'):
-        body += o_rescale(1, after_mfma=False, tag=tag)
+        body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
     return body
+
+
+def interleave(main, extra):
+    """The groups of main with those of extra spread evenly among them."""
+    if not main:
+        return list(extra)
+    out, n, k = [], len(main), len(extra)
+    at = [((i + 1) * n) // (k + 1) for i in range(k)]
+    j = 0
+    for i, grp in enumerate(main):
+        while j < k and at[j] <= i:
+            out.append(extra[j])
+            j += 1
+        out.append(grp)
+    out += extra[j:]
+    return out
 
 
 def pv_phase(par, kind, has_pv, tag):
     """PV phase of an iteration of parity par: O += P(T[g]) V(T[g]) (if
-    has_pv) beside softmax(T[g+1], half 0) of the given kind ('x': none)."""
+    has_pv) beside softmax(T[g+1], half 0) of the given kind ('x': none) and
+    the scalar bookkeeping of iteration g + 1."""
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
     fill = softmax_ops(kind, 0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0") if kind != 'x' else []
+    fill = interleave(fill, book_next(par))
     if has_pv:
         vslot = V_OFF + par * K_SLOT_BYTES          # V(T[g]) in slot g % 2
         frag_reads = []
@@ -389,48 +422,116 @@ def pv_phase(par, kind, has_pv, tag):
         for g in fill:
             body += g
     if kind in ('n', 'd'):
-        body += o_rescale(0, after_mfma=has_pv, tag=tag)
+        body += o_rescale(0, after_mfma=has_pv, tag=tag, olive=roles(par)["OP"])
     return body
 
 
 # ------------------------------------------------------------------ the loop
-def tile_of(x, t, b):
+def tile_of(x, t, b, tmp=S_Y):
     """t = T[x], b = block of T[x]: light run (x < elo) or heavy run."""
     return ["s_cmp_lt_i32 %s, %%[elo]" % x,
-            "s_cselect_b32 %s, 0, %%[jump]" % sr(S_Y),
+            "s_cselect_b32 %s, 0, %%[jump]" % sr(tmp),
             "s_cselect_b32 %s, %%[blk0], %%[blk1]" % sr(b),
-            "s_add_i32 %s, %s, %s" % (sr(t), x, sr(S_Y))]
+            "s_add_i32 %s, %s, %s" % (sr(t), x, sr(tmp))]
 
 
-def kind_of(t, b, dst):
+def kind_of(t, b, dst, tmp=S_Y):
     """dst = 0 if tile t is below the wave's diagonal tile of block b, 1 on
     it, 2 above it (diagonal tile 2 b + wsub)."""
-    return ["s_lshl_b32 %s, %s, 1" % (sr(S_Y), sr(b)),
-            "s_add_i32 %s, %s, %%[wsub]" % (sr(S_Y), sr(S_Y)),
-            "s_cmp_lt_i32 %s, %s" % (sr(t), sr(S_Y)),
+    return ["s_lshl_b32 %s, %s, 1" % (sr(tmp), sr(b)),
+            "s_add_i32 %s, %s, %%[wsub]" % (sr(tmp), sr(tmp)),
+            "s_cmp_lt_i32 %s, %s" % (sr(t), sr(tmp)),
             "s_cselect_b32 %s, 0, 1" % sr(dst),
-            "s_cmp_gt_i32 %s, %s" % (sr(t), sr(S_Y)),
+            "s_cmp_gt_i32 %s, %s" % (sr(t), sr(tmp)),
             "s_cselect_b32 %s, 2, %s" % (sr(dst), sr(dst))]
 
 
-def descriptor(t, d, lo, hi):
+def descriptor(t, d, lo, hi, tmp=S_Y):
     """Buffer descriptor of tile t's rows: base + t * tile bytes, range to
     the end of the sequence's rows."""
-    return ["s_mul_i32 %s, %s, %%[tileb]" % (sr(S_Y), sr(t)),
-            "s_add_u32 %s, %%[%s], %s" % (sr(d), lo, sr(S_Y)),
+    return ["s_mul_i32 %s, %s, %%[tileb]" % (sr(tmp), sr(t)),
+            "s_add_u32 %s, %%[%s], %s" % (sr(d), lo, sr(tmp)),
             "s_addc_u32 %s, %%[%s], 0" % (sr(d + 1), hi),
-            "s_sub_u32 %s, %%[nrec], %s" % (sr(d + 2), sr(S_Y))]
+            "s_sub_u32 %s, %%[nrec], %s" % (sr(d + 2), sr(tmp))]
+
+
+def book_next(par):
+    """Scalar state of iteration h = g + 1 (parity 1 - par), computed in the
+    PV phase of iteration g as filler groups (each group keeps its own SCC
+    uses): T[h+1] and its block and kind, the olive flag of h's PV phase,
+    T[h+2] and the load descriptors, the flag of the out-of-line middle part
+    and the phase variant codes.  T[h], its block and kind and the olive flag
+    of h's score phase are g's T[g+1] values, already in h's registers."""
+    r = roles(1 - par)
+    g = sr(S_G)
+    NX, NY, NZ = sr(S_NX), sr(S_NY), sr(S_NZ)
+    T0, T1, B0, B1 = sr(r["T0"]), sr(r["T1"]), sr(r["B0"]), sr(r["B1"])
+    KS, KP, OP = sr(r["KS"]), sr(r["KP"]), sr(r["OP"])
+    return [
+        # T[h+1] = T[g+2], its block
+        ["s_add_i32 %s, %s, 2" % (NX, g)] + tile_of(NX, r["T1"], r["B1"], tmp=S_NY),
+        # its kind; 3 when it is past the wave's tiles
+        kind_of(r["T1"], r["B1"], r["KP"], tmp=S_NZ),
+        ["s_cmp_lt_i32 %s, %%[nmy]" % NX, "s_cselect_b32 %s, %s, 3" % (KP, KP)],
+        # olive of h's PV phase: T[h+1] does not start a run
+        ["s_cmp_eq_u32 %s, %%[elo]" % NX, "s_cselect_b32 %s, 0, 1" % OP,
+         "s_cmp_eq_u32 %s, 0" % NX, "s_cselect_b32 %s, 0, %s" % (OP, OP)],
+        # T[h+2], or T[h] again when there is none (the load refills a free slot)
+        ["s_add_i32 %s, %s, 3" % (NY, g), "s_cmp_lt_i32 %s, %%[elo]" % NY,
+         "s_cselect_b32 %s, 0, %%[jump]" % NZ, "s_add_i32 %s, %s, %s" % (sr(S_T2), NY, NZ),
+         "s_cmp_lt_i32 %s, %%[nmy]" % NY, "s_cselect_b32 %s, %s, %s" % (sr(S_T2), sr(S_T2), T0)],
+        descriptor(S_T2, S_VK, "kbl", "kbh", tmp=S_NY),
+        # V of T[h+1], or of T[h] when there is no T[h+1]
+        ["s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, %s, %s" % (NY, T0, T1)] +
+        descriptor(S_NY, S_VV, "vbl", "vbh", tmp=S_NY),
+        # out-of-line middle part: Q reload (h + 1 == gt), transition (h == gt)
+        ["s_add_i32 %s, %s, 2" % (NY, g), "s_cmp_eq_u32 %s, %%[gt]" % NY, "s_cselect_b32 %s, 1, 0" % sr(S_SPEC),
+         "s_add_i32 %s, %s, 1" % (NY, g), "s_cmp_eq_u32 %s, %%[gt]" % NY,
+         "s_cselect_b32 %s, 1, %s" % (sr(S_SPEC), sr(S_SPEC))],
+        # ... or a cache copy of K(T[h+1]) or V(T[h]) (tiles of the wave's own block)
+        ["s_lshr_b32 %s, %s, 1" % (NY, T1), "s_cmp_eq_u32 %s, %s" % (NY, B1), "s_cselect_b32 %s, 1, 0" % NY,
+         "s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, 0, %s" % (NY, NY)],
+        ["s_lshr_b32 %s, %s, 1" % (NZ, T0), "s_cmp_eq_u32 %s, %s" % (NZ, B0), "s_cselect_b32 %s, 1, 0" % NZ,
+         "s_or_b32 %s, %s, %s" % (NY, NY, NZ), "s_cmp_eq_u32 %[copy], 0",
+         "s_cselect_b32 %s, 0, %s" % (NY, NY), "s_or_b32 %s, %s, %s" % (sr(S_SPEC), sr(S_SPEC), NY)],
+        # variant codes
+        ["s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, 4, 0" % sr(S_CS),
+         "s_or_b32 %s, %s, %s" % (sr(S_CS), sr(S_CS), KS), "s_mov_b32 %s, %s" % (sr(S_CP), KP)],
+    ]
+
+
+def book_entry(par):
+    """Scalar state of iteration g = S_G (parity par) on entry to the loop:
+    T[g] (T[0] for the pre-loop iteration g = -1), its block, kind (3: no
+    softmax) and score-phase olive flag, then the rest as the previous
+    iteration's PV phase would have computed it."""
+    r = roles(par)
+    g = sr(S_G)
+    out = ["s_max_i32 %s, %s, 0" % (sr(S_X), g)] + tile_of(sr(S_X), r["T0"], r["B0"])
+    out += kind_of(r["T0"], r["B0"], r["KS"])
+    out += ["s_cmp_lt_i32 %s, 0" % g, "s_cselect_b32 %s, 3, %s" % (sr(r["KS"]), sr(r["KS"])),
+            "s_cmp_eq_u32 %s, %%[elo]" % g, "s_cselect_b32 %s, 0, 1" % sr(r["OS"]),
+            "s_cmp_eq_u32 %s, 0" % g, "s_cselect_b32 %s, 0, %s" % (sr(r["OS"]), sr(r["OS"]))]
+    out += ["s_add_i32 %s, %s, -1" % (g, g)]
+    for grp in book_next(1 - par):
+        out += grp
+    out += ["s_add_i32 %s, %s, 1" % (g, g),
+            # the pre-loop iteration has no PV phase (and may need no copy of V)
+            "s_cmp_lt_i32 %s, 0" % g, "s_cselect_b32 %s, 4, 0" % sr(S_NY),
+            "s_or_b32 %s, %s, %s" % (sr(S_CP), sr(S_CP), sr(S_NY)),
+            "s_or_b32 %s, %s, %s" % (sr(S_SPEC), sr(S_SPEC), sr(S_NY))]
+    return out
 
 
 def cache_copy(par, matrix, tag):
     """Copy this wave's 32 rows (32 wsub + 4 i + lane/16, i < 8) of the K
     tile T[g+1] (K slot (g+1) % 2) or the V tile T[g] (V slot g % 2) from LDS
-    to the cache, rows past the sequence masked.  The tile is in S_T1 (K) or
-    S_T0 (V)."""
+    to the cache, rows past the sequence masked."""
+    r = roles(par)
     if matrix == 'k':
-        slot_off, t, lo, hi = (1 - par) * K_SLOT_BYTES, S_T1, "kcl", "kch"
+        slot_off, t, lo, hi = (1 - par) * K_SLOT_BYTES, r["T1"], "kcl", "kch"
     else:
-        slot_off, t, lo, hi = V_OFF + par * K_SLOT_BYTES, S_T0, "vcl", "vch"
+        slot_off, t, lo, hi = V_OFF + par * K_SLOT_BYTES, r["T0"], "vcl", "vch"
     out = []
     regs = [V_VF + 4 * i for i in range(4)] + [V_KF + 4 * i for i in range(4)]
     for i in range(8):
@@ -468,121 +569,117 @@ def q_reload():
     return out
 
 
-def body(par):
-    """One iteration (parity par) for g = S_G, ending after its barrier."""
-    P = "p%d" % par
-    out = []
+def lbl(name, par):
+    return ".L%s_p%d_%%=" % (name, par)
 
-    def L(name):
-        return ".L%s_%s_%%=" % (name, P)
+
+def body(par):
+    """One iteration (parity par) for g = S_G, ending after its barrier: the
+    common case in line (branches not taken), every other case out of line
+    (slow_paths)."""
+    L = lambda name: lbl(name, par)
+    P = "p%d" % par
     g = sr(S_G)
-    # a group past its tiles only meets the barrier
-    out += ["s_cmp_ge_i32 %s, %%[nmy]" % g,
-            "s_cbranch_scc1 %s" % L("bar")]
-    # T[g+1], its block, the PV-phase kind
-    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g)] + tile_of(sr(S_X), S_T1, S_B1)
-    out += ["s_mov_b32 %s, 3" % sr(S_KP),
-            "s_cmp_lt_i32 %s, %%[nmy]" % sr(S_X),
-            "s_cbranch_scc0 %s" % L("kp")] + kind_of(S_T1, S_B1, S_KP) + ["%s:" % L("kp")]
-    # T[g] (T[0] for the pre-loop iteration), its block, the score-phase kind
-    out += ["s_max_i32 %s, %s, 0" % (sr(S_X), g)] + tile_of(sr(S_X), S_T0, S_B0)
-    out += ["s_mov_b32 %s, 3" % sr(S_KS),
-            "s_cmp_lt_i32 %s, 0" % g,
-            "s_cbranch_scc1 %s" % L("ks")] + kind_of(S_T0, S_B0, S_KS) + ["%s:" % L("ks")]
-    # T[g+2] (or T[g] again: a load with no tile to fetch refills a free slot)
-    out += ["s_add_i32 %s, %s, 2" % (sr(S_X), g),
-            "s_cmp_lt_i32 %s, %%[nmy]" % sr(S_X),
-            "s_cbranch_scc1 %s" % L("t2"),
-            "s_mov_b32 %s, %s" % (sr(S_T2), sr(S_T0)),
-            "s_branch %s" % L("t2d"),
-            "%s:" % L("t2")] + tile_of(sr(S_X), S_T2, S_FLAG) + ["%s:" % L("t2d")]
-    # descriptors: K(T[g+2]), V(T[g+1]) (or V(T[g]) when there is no g+1)
-    out += descriptor(S_T2, S_VK, "kbl", "kbh")
-    out += ["s_cmp_eq_u32 %s, 3" % sr(S_KP),
-            "s_cselect_b32 %s, %s, %s" % (sr(S_X), sr(S_T0), sr(S_T1))]
-    out += descriptor(S_X, S_VV, "vbl", "vbh")
-    # olive of the score phase: T[g] is not the first tile of its run
-    out += ["s_cmp_eq_u32 %s, 0" % g,
-            "s_cselect_b32 %s, 0, 1" % sr(S_OLIVE),
-            "s_cmp_eq_u32 %s, %%[elo]" % g,
-            "s_cselect_b32 %s, 0, %s" % (sr(S_OLIVE), sr(S_OLIVE))]
-    # ---- score phase: dispatch on (has S = kind of g+1 != 3, kind of g)
+    out = [# a group past its tiles only meets the barrier
+           "s_cmp_ge_i32 %s, %%[nmy]" % g,
+           "s_cbranch_scc1 %s" % L("bar"),
+           "s_cmp_eq_u32 %s, 0" % sr(S_CS),
+           "s_cbranch_scc0 %s" % L("ss")]
+    out += score_phase(par, 'n', True, "s_n_S" + P)
+    out += ["%s:" % L("sdone"),
+            "s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
+            "s_cbranch_scc0 %s" % L("ms"),
+            "%s:" % L("mdone"),
+            "s_cmp_eq_u32 %s, 0" % sr(S_CP),
+            "s_cbranch_scc0 %s" % L("ps")]
+    out += pv_phase(par, 'n', True, "p_n_PV" + P)
+    out += ["%s:" % L("pdone"),
+            # end of the interval: this wave's loads have landed; everyone's have
+            "%s:" % L("bar"),
+            "s_waitcnt vmcnt(0) lgkmcnt(0)",
+            "s_barrier"]
+    return out
+
+
+def slow_paths(par):
+    """Out-of-line parts of an iteration of parity par: the other score and
+    PV variants (diagonal, masked, no next tile, pre-loop), and the middle
+    part (Q reload, cache copies, transition)."""
+    L = lambda name: lbl(name, par)
+    P = "p%d" % par
+    r = roles(par)
+    g = sr(S_G)
+    KS, KP = sr(r["KS"]), sr(r["KP"])
     kidx = {'n': 0, 'd': 1, 'm': 2, 'x': 3}
-    out += ["s_cmp_eq_u32 %s, 3" % sr(S_KP),
-            "s_cbranch_scc1 %s" % L("s_noS")]
-    for kind in ('n', 'd', 'm'):
-        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KS), kidx[kind]),
+    # ---- score phase: has S = kind of g+1 != 3; kind of g
+    out = ["%s:" % L("ss"),
+           "s_cmp_eq_u32 %s, 3" % KP,
+           "s_cbranch_scc1 %s" % L("s_noS")]
+    for kind in ('d', 'm'):
+        out += ["s_cmp_eq_u32 %s, %d" % (KS, kidx[kind]),
                 "s_cbranch_scc1 %s" % L("s_%s_S" % kind)]
     out += ["s_branch %s" % L("s_x_S"), "%s:" % L("s_noS")]
     for kind in ('n', 'd'):
-        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KS), kidx[kind]),
+        out += ["s_cmp_eq_u32 %s, %d" % (KS, kidx[kind]),
                 "s_cbranch_scc1 %s" % L("s_%s_noS" % kind)]
     out += ["s_branch %s" % L("s_m_noS")]
     for has_s in (True, False):
         for kind in ('n', 'd', 'm', 'x'):
-            if kind == 'x' and not has_s:
+            if (kind == 'x' and not has_s) or (kind == 'n' and has_s):
                 continue
             nm = "s_%s_%s" % (kind, "S" if has_s else "noS")
             out += ["%s:" % L(nm)]
             out += score_phase(par, kind, has_s, nm + P)
             out += ["s_branch %s" % L("sdone")]
-    out += ["%s:" % L("sdone")]
-    # ---- the heavy block's Q after the last light score tile
+    # ---- middle part
+    out += ["%s:" % L("ms")]
+    # the heavy block's Q after the last light score tile
     out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
             "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
             "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
-    # ---- cache copies of own rows: K(T[g+1]), V(T[g])
+    # cache copies of own rows: K(T[g+1]), V(T[g])
     out += ["s_cmp_eq_u32 %[copy], 0",
             "s_cbranch_scc1 %s" % L("nocv"),
-            "s_cmp_eq_u32 %s, 3" % sr(S_KP),
+            "s_cmp_eq_u32 %s, 3" % KP,
             "s_cbranch_scc1 %s" % L("nock"),
-            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(S_T1)),
-            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(S_B1)),
+            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T1"])),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B1"])),
             "s_cbranch_scc0 %s" % L("nock")] + cache_copy(par, 'k', P) + ["%s:" % L("nock")]
     out += ["s_cmp_lt_i32 %s, 0" % g,
             "s_cbranch_scc1 %s" % L("nocv"),
-            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(S_T0)),
-            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(S_B0)),
+            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T0"])),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B0"])),
             "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv")]
-    # ---- at the last light tile the next tile's half-0 softmax starts the
-    # heavy block's state; the light block's is kept for its store
+    # at the last light tile the next tile's half-0 softmax starts the heavy
+    # block's state; the light block's is kept for its store
     out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
             "s_cbranch_scc0 %s" % L("notr"),
             "v_mov_b32 %[m0n], %[m0v]",
             "v_mov_b32 %[l0n], %[l0v]",
             "v_mov_b32 %%[m0v], %s" % MINIT,
             "v_mov_b32 %[l0v], 0",
-            "%s:" % L("notr")]
-    # olive of the PV phase: T[g+1] is not the first tile of its run
-    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
-            "s_cmp_eq_u32 %s, 0" % sr(S_X),
-            "s_cselect_b32 %s, 0, 1" % sr(S_OLIVE),
-            "s_cmp_eq_u32 %s, %%[elo]" % sr(S_X),
-            "s_cselect_b32 %s, 0, %s" % (sr(S_OLIVE), sr(S_OLIVE))]
-    # ---- PV phase: dispatch on (has PV = g >= 0, kind of g+1)
-    out += ["s_cmp_lt_i32 %s, 0" % g,
+            "%s:" % L("notr"),
+            "s_branch %s" % L("mdone")]
+    # ---- PV phase: has PV = g >= 0; kind of g+1
+    out += ["%s:" % L("ps"),
+            "s_cmp_lt_i32 %s, 0" % g,
             "s_cbranch_scc1 %s" % L("p_noPV")]
-    for kind in ('n', 'd', 'm'):
-        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KP), kidx[kind]),
+    for kind in ('d', 'm'):
+        out += ["s_cmp_eq_u32 %s, %d" % (KP, kidx[kind]),
                 "s_cbranch_scc1 %s" % L("p_%s_PV" % kind)]
     out += ["s_branch %s" % L("p_x_PV"), "%s:" % L("p_noPV")]
     for kind in ('n', 'd'):
-        out += ["s_cmp_eq_u32 %s, %d" % (sr(S_KP), kidx[kind]),
+        out += ["s_cmp_eq_u32 %s, %d" % (KP, kidx[kind]),
                 "s_cbranch_scc1 %s" % L("p_%s_noPV" % kind)]
     out += ["s_branch %s" % L("p_m_noPV")]
     for has_pv in (True, False):
         for kind in ('n', 'd', 'm', 'x'):
-            if kind == 'x' and not has_pv:
+            if (kind == 'x' and not has_pv) or (kind == 'n' and has_pv):
                 continue
             nm = "p_%s_%s" % (kind, "PV" if has_pv else "noPV")
             out += ["%s:" % L(nm)]
             out += pv_phase(par, kind, has_pv, nm + P)
             out += ["s_branch %s" % L("pdone")]
-    out += ["%s:" % L("pdone")]
-    # ---- end of the interval: this wave's loads have landed; everyone's have
-    out += ["%s:" % L("bar"),
-            "s_waitcnt vmcnt(0) lgkmcnt(0)",
-            "s_barrier"]
     return out
 
 
@@ -601,7 +698,9 @@ def loop_text():
            "s_mov_b32 %s, 0x20000" % sr(S_VV + 3),
            "s_mov_b32 %s, %%[gstart]" % sr(S_G),
            "s_bitcmp1_b32 %s, 0" % sr(S_G),
-           "s_cbranch_scc0 .Leven_%="]
+           "s_cbranch_scc0 .Lentry0_%="]
+    out += book_entry(1) + ["s_branch .Lodd_%="]
+    out += [".Lentry0_%=:"] + book_entry(0) + ["s_branch .Leven_%="]
     out += [".Lodd_%=:"]
     out += body(1)
     out += ["s_cmp_eq_u32 %s, %%[gt]" % sr(S_G),
@@ -616,8 +715,9 @@ def loop_text():
             "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
             "s_cmp_ge_i32 %s, %%[nit]" % sr(S_G),
             "s_cbranch_scc0 .Lodd_%=",
-            "s_branch .Lend_%=",
-            ".Ltrans_%=:",
+            "s_branch .Lend_%="]
+    out += slow_paths(1) + slow_paths(0)
+    out += [".Ltrans_%=:",
             "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
             ".Lend_%=:",
             "s_mov_b32 %%[gout], %s" % sr(S_G),
