@@ -245,8 +245,10 @@ void prefill_fwd64_kernel(FwdParams p) {
   uint32_t fk[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) fk[i] = (uint32_t)(8 * i + r0) * rs + lane_chunk;
-  L.fk0 = fk[0]; L.fk1 = fk[1]; L.fk2 = fk[2]; L.fk3 = fk[3];
-  L.fk4 = fk[4]; L.fk5 = fk[5]; L.fk6 = fk[6]; L.fk7 = fk[7];
+  // the loop's odd loads carry an instruction offset of 2048 bytes (which
+  // moves the LDS address too); 8 rows of at least 256 bytes precede them
+  L.fk0 = fk[0]; L.fk1 = fk[1] - 2048u; L.fk2 = fk[2]; L.fk3 = fk[3] - 2048u;
+  L.fk4 = fk[4]; L.fk5 = fk[5] - 2048u; L.fk6 = fk[6]; L.fk7 = fk[7] - 2048u;
   L.vd = ql - 4 * hl;
   // cache copy: the wave's rows 32 wsub + 4 i + lane/16 of a tile
   {

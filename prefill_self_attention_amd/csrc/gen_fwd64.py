@@ -231,7 +231,7 @@ def o_rescale(qh, after_mfma, tag, olive):
         out += ["s_nop 7", "s_nop 7", "s_nop 7", "s_nop 7"]
     regs = list(range(A_O + 64 * qh, A_O + 64 * qh + 64))
     n = len(T_RS)
-    for b in range(0, 64, n):
+    for b in range(0, len(regs), n):
         chunk = regs[b:b + n]
         for t, a in zip(T_RS, chunk):
             out.append("v_accvgpr_read_b32 %s, %s" % (vr(t), ar(a)))
@@ -274,7 +274,8 @@ def gcost(g):
 
 def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
     """Interleave: before the MFMA pair of fragment f wait for its reads and
-    issue fragment f+LOOKAHEAD's; load group i goes after MFMA i; the filler
+    issue fragment f+LOOKAHEAD's; load pair i = (before, after) goes around
+    MFMA i; the filler
     groups (softmax) fill each MFMA slot up to SLOT_BUDGET issue cycles, in
     order (raised when the rest would not fit; what is left follows the last
     MFMA)."""
@@ -296,10 +297,13 @@ def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
                 out += frag_reads[issued]
                 used += gcost(frag_reads[issued])
                 issued += 1
+        if s in load_at:
+            out += load_at[s][0]
+            used += gcost(load_at[s][0])
         out.append(mf)
         if s in load_at:
-            out += load_at[s]
-            used += gcost(load_at[s])
+            out += load_at[s][1]
+            used += gcost(load_at[s][1])
         left = nslots - s
         rest = sum(gcost(g) for g in fillers[fi:])
         target = max(SLOT_BUDGET, used + rest / left)
@@ -324,9 +328,14 @@ def loads(par, matrix):
     both issued in the score phase of iteration g: K(T[g+2]) into K slot
     g % 2, V(T[g+1]) into V slot (g+1) % 2 (their previous tiles were last
     read before the previous interval's barrier).  Instruction i fills LDS
-    block 2*i + wsub of the slot (M0 = %[m0b] + offset) from the tile's
-    buffer descriptor + %[fk<i>] (rows 8*i + 4*wsub + lane/16); rows past the
-    sequence are out of the descriptor's range and read as zero."""
+    block 2*i + wsub of the slot from the tile's buffer descriptor +
+    %[fk<i>] (rows 8*i + 4*wsub + lane/16); rows past the sequence are out
+    of the descriptor's range and read as zero.  Loads 2j and 2j+1 share one
+    M0 (= %[m0b] + offset of block 4j): the instruction offset 2048 of the
+    odd one moves both its LDS and its memory address, so %[fk<odd>] holds
+    the row offset less 2048.  Returns (before, after) pairs: the M0 write
+    goes before an MFMA, the load after it (an LDS DMA needs one wait state
+    after M0 is written)."""
     groups = []
     if matrix == 'k':
         slot_off = par * K_SLOT_BYTES
@@ -335,9 +344,11 @@ def loads(par, matrix):
         slot_off = V_OFF + (1 - par) * K_SLOT_BYTES
         desc = sr(S_VV, 4)
     for i in range(ROWSTEP_LOADS):
-        groups.append(["s_add_u32 m0, %%[m0b], %d" % (slot_off + 2048 * i),
-                       "s_nop 0",
-                       "buffer_load_dwordx4 %%[fk%d], %s, 0 offen lds" % (i, desc)])
+        if i % 2 == 0:
+            groups.append((["s_add_u32 m0, %%[m0b], %d" % (slot_off + 2048 * i)],
+                           ["buffer_load_dwordx4 %%[fk%d], %s, 0 offen lds" % (i, desc)]))
+        else:
+            groups.append(([], ["buffer_load_dwordx4 %%[fk%d], %s, 0 offen offset:2048 lds" % (i, desc)]))
     return groups
 
 
@@ -349,7 +360,8 @@ def score_phase(par, kind, has_s, tag):
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
     fill = softmax_ops(kind, 1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1") if kind != 'x' else []
     k_l, v_l = loads(par, 'k'), loads(par, 'v')
-    loadg = [x for pair in zip(k_l, v_l) for x in pair]
+    # pairs sharing an M0 stay together: K0 K1 V0 V1 K2 K3 ...
+    loadg = [x for j in range(0, ROWSTEP_LOADS, 2) for x in (k_l[j], k_l[j + 1], v_l[j], v_l[j + 1])]
     if has_s:
         kslot = (1 - par) * K_SLOT_BYTES          # K(T[g+1]) in slot (g+1) % 2
         nb = s_bank(1 - par)                      # half-1 scores of T[g+1]
@@ -370,8 +382,8 @@ def score_phase(par, kind, has_s, tag):
     else:
         for g in fill:
             body += g
-        for g in loadg:
-            body += g
+        for before, after in loadg:
+            body += before + (["s_nop 0"] if before else []) + after
     if kind in ('n', 'd'):
         body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
     return body
