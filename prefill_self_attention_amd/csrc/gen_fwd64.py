@@ -56,7 +56,6 @@ T_THR = V_T + 2                     # m + 8
 T_MNEW = V_T + 3
 T_ALPHA = V_T + 4                   # rescale factor (kept to the end of the phase)
 T_NINF = V_T + 5                    # -inf
-T_ROW = V_T + 6                     # cache-copy row
 T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
 
 # scalar registers of the loop.  Pairs alternate with the iteration's
@@ -73,10 +72,9 @@ S_OO = (80, 92)    # olive flags (O holds data) of the score phase, of the PV ph
 S_FLAG = 81
 S_M0SAVE = 82
 S_X, S_Y = 83, 84               # scratch
-S_CB = 86          # s[86:87], s[88:89] cache-store bases
-S_EXEC = 90        # s[90:91] saved exec
+S_CB = 88          # s[88:91] cache-store descriptor
 S_SPEC = 93        # nonzero: the iteration takes the out-of-line middle part
-S_CS = 94          # score-phase variant: 0 the common one (all keys visible, a next tile)
+S_CS = 94          # score-phase variant: 0 the common one (all keys of T[g] visible)
 S_CP = 95          # PV-phase variant: 0 the common one
 S_NX, S_NY, S_NZ = 96, 97, 98   # scratch of the next iteration's bookkeeping
 NUM_SGPR_FIXED = list(range(64, 99))
@@ -115,46 +113,23 @@ def s_bank(par):
 
 
 # ------------------------------------------------------------------ softmax
-def softmax_ops(kind, qh, sbase, pbase, m, l, tag):
+def softmax_ops(qh, sbase, pbase, m, l, tag):
     """Online-softmax update of one query half over one 64-key tile.
 
     sbase: 32 score registers (key block 0: sbase..+15, block 1: +16..+31);
     the lane holds query row 32*qh + lane%32 and, in register r of key
-    block kb, key 32*kb + 8*(r/4) + 4*(lane/32) + r%4.  pbase: 16 registers
-    of bf16 pairs, P[k] = (p[2k], p[2k+1]) over the 32 scores in order, which
-    is the B-operand order of the PV MFMAs.  m, l: the half's running max
-    (exp2 domain) and per-lane partial sum.
-
-    kind: 'n' every key visible, 'd' the wave's diagonal tile (key k > row q
-    masked, both relative to the tile / the wave's first row), 'm' every key
-    masked (P = 0, state unchanged).
+    block kb, key 32*kb + 8*(r/4) + 4*(lane/32) + r%4.  Scores the causal
+    mask hides are -inf already (mask_ops).  pbase: 16 registers of bf16
+    pairs, P[k] = (p[2k], p[2k+1]) over the 32 scores in order, which is the
+    B-operand order of the PV MFMAs.  m, l: the half's running max (exp2
+    domain) and per-lane partial sum.
 
     Returns a list of groups; a group's instructions are emitted together.
     When some lane's running max moves, S_FLAG is set and l rescaled; the O
     accumulators are rescaled at the end of the phase.
     """
     groups = []
-    if kind == 'm':
-        for k in range(16):
-            groups.append(["v_mov_b32 %s, 0" % vr(pbase + k)])
-        return groups
-    if kind == 'n':
-        live = list(range(32))
-        diag_regs = []
-    elif qh == 0:   # diagonal: key block 0 on the diagonal, block 1 above it
-        live = list(range(16))
-        diag_regs = list(range(16))
-    else:           # half 1: key block 0 below the diagonal, block 1 on it
-        live = list(range(32))
-        diag_regs = list(range(16, 32))
-    # causal mask on the diagonal key block: key offset o_r > d masked, with
-    # o_r = 8*(r/4) + r%4 and d = lane%32 - 4*(lane/32) (the same d for both
-    # halves, because each half's diagonal block starts at its first row)
-    for i in diag_regs:
-        r = i % 16
-        o = 8 * (r // 4) + r % 4
-        groups.append(["v_cmp_gt_i32 vcc, %d, %%[vd]" % o,
-                       "v_cndmask_b32 %s, %s, %s, vcc" % (vr(sbase + i), vr(sbase + i), vr(T_NINF))])
+    live = list(range(32))
     # row max over the live scores: two chains of v_max3, then the partner lane
     chains = [live[:len(live) // 2], live[len(live) // 2:]]
     for ci, ch in enumerate(chains):
@@ -212,11 +187,28 @@ def softmax_ops(kind, qh, sbase, pbase, m, l, tag):
     groups.append(["s_nop 1"])
     if order[-1] % 2 == 1:
         groups += pack(order[-1] // 2)
-    # P of keys that take no part (block 1 of half 0 on the diagonal)
-    for k in range(16):
-        if 2 * k not in live:
-            groups.append(["v_mov_b32 %s, 0" % vr(pbase + k)])
     return groups
+
+
+def mask_ops(kind, qh, sbase):
+    """Scores of one query half over one tile that the causal mask hides, set
+    to -inf before the phase's softmax (which then gives them weight 0 and
+    leaves the running max alone): 'd' the wave's diagonal tile (key k >
+    row q hidden, both relative to the tile / the half's first row; for half
+    0 key block 1 lies wholly above the diagonal), 'm' every key.  Register
+    layout as in softmax_ops."""
+    out = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF)]
+    if kind == 'm':
+        return out + ["v_mov_b32 %s, %s" % (vr(sbase + i), vr(T_NINF)) for i in range(32)]
+    diag = range(16) if qh == 0 else range(16, 32)
+    for i in diag:
+        r = i % 16
+        o = 8 * (r // 4) + r % 4
+        out += ["v_cmp_gt_i32 vcc, %d, %%[vd]" % o,
+                "v_cndmask_b32 %s, %s, %s, vcc" % (vr(sbase + i), vr(sbase + i), vr(T_NINF))]
+    if qh == 0:
+        out += ["v_mov_b32 %s, %s" % (vr(sbase + i), vr(T_NINF)) for i in range(16, 32)]
+    return out
 
 
 def o_rescale(qh, after_mfma, tag, olive):
@@ -352,40 +344,34 @@ def loads(par, matrix):
     return groups
 
 
-def score_phase(par, kind, has_s, tag):
-    """Score phase of an iteration of parity par: S(T[g+1]) (if has_s) beside
-    softmax(T[g], half 1) of the given kind ('x': none), loads of K(T[g+2])
-    and V(T[g+1]) (descriptors S_VK, S_VV)."""
+def score_phase(par, tag):
+    """Score phase of an iteration of parity par: S(T[g+1]) beside
+    softmax(T[g], half 1), loads of K(T[g+2]) and V(T[g+1]) (descriptors
+    S_VK, S_VV).  In the last iteration T[g+1] does not exist: its K slot
+    holds a refilled tile and the scores go unused."""
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
-    fill = softmax_ops(kind, 1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1") if kind != 'x' else []
+    fill = softmax_ops(1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1")
     k_l, v_l = loads(par, 'k'), loads(par, 'v')
     # pairs sharing an M0 stay together: K0 K1 V0 V1 K2 K3 ...
     loadg = [x for j in range(0, ROWSTEP_LOADS, 2) for x in (k_l[j], k_l[j + 1], v_l[j], v_l[j + 1])]
-    if has_s:
-        kslot = (1 - par) * K_SLOT_BYTES          # K(T[g+1]) in slot (g+1) % 2
-        nb = s_bank(1 - par)                      # half-1 scores of T[g+1]
-        frag_reads = []
-        mfmas = []
-        for ds in range(8):
-            for kb in range(2):
-                f = 2 * ds + kb
-                slot = V_KF + 4 * (f % 4)
-                off = kslot + 128 * (ds >> 2) + kb * 32 * 256
-                frag_reads.append(["ds_read_b128 %s, %%[kb%d] offset:%d" % (vr(slot, 4), ds & 3, off)])
-                for qh in range(2):
-                    dst = (V_SA if qh == 0 else nb) + 16 * kb
-                    src_c = "0" if ds == 0 else vr(dst, 16)
-                    mfmas.append(("%s %s, %s, %s, %s" % (MFMA, vr(dst, 16), vr(slot, 4),
-                                                         ar(A_Q + 4 * (8 * qh + ds), 4), src_c), f))
-        body += schedule(mfmas, frag_reads, 1, fill, loadg)
-    else:
-        for g in fill:
-            body += g
-        for before, after in loadg:
-            body += before + (["s_nop 0"] if before else []) + after
-    if kind in ('n', 'd'):
-        body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
+    kslot = (1 - par) * K_SLOT_BYTES          # K(T[g+1]) in slot (g+1) % 2
+    nb = s_bank(1 - par)                      # half-1 scores of T[g+1]
+    frag_reads = []
+    mfmas = []
+    for ds in range(8):
+        for kb in range(2):
+            f = 2 * ds + kb
+            slot = V_KF + 4 * (f % 4)
+            off = kslot + 128 * (ds >> 2) + kb * 32 * 256
+            frag_reads.append(["ds_read_b128 %s, %%[kb%d] offset:%d" % (vr(slot, 4), ds & 3, off)])
+            for qh in range(2):
+                dst = (V_SA if qh == 0 else nb) + 16 * kb
+                src_c = "0" if ds == 0 else vr(dst, 16)
+                mfmas.append(("%s %s, %s, %s, %s" % (MFMA, vr(dst, 16), vr(slot, 4),
+                                                     ar(A_Q + 4 * (8 * qh + ds), 4), src_c), f))
+    body += schedule(mfmas, frag_reads, 1, fill, loadg)
+    body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
     return body
 
 
@@ -405,13 +391,13 @@ def interleave(main, extra):
     return out
 
 
-def pv_phase(par, kind, has_pv, tag):
+def pv_phase(par, has_pv, tag):
     """PV phase of an iteration of parity par: O += P(T[g]) V(T[g]) (if
-    has_pv) beside softmax(T[g+1], half 0) of the given kind ('x': none) and
+    has_pv) beside softmax(T[g+1], half 0) and
     the scalar bookkeeping of iteration g + 1."""
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
-    fill = softmax_ops(kind, 0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0") if kind != 'x' else []
+    fill = softmax_ops(0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0")
     fill = interleave(fill, book_next(par))
     if has_pv:
         vslot = V_OFF + par * K_SLOT_BYTES          # V(T[g]) in slot g % 2
@@ -433,8 +419,7 @@ def pv_phase(par, kind, has_pv, tag):
     else:
         for g in fill:
             body += g
-    if kind in ('n', 'd'):
-        body += o_rescale(0, after_mfma=has_pv, tag=tag, olive=roles(par)["OP"])
+    body += o_rescale(0, after_mfma=has_pv, tag=tag, olive=roles(par)["OP"])
     return body
 
 
@@ -506,9 +491,8 @@ def book_next(par):
         ["s_lshr_b32 %s, %s, 1" % (NZ, T0), "s_cmp_eq_u32 %s, %s" % (NZ, B0), "s_cselect_b32 %s, 1, 0" % NZ,
          "s_or_b32 %s, %s, %s" % (NY, NY, NZ), "s_cmp_eq_u32 %[copy], 0",
          "s_cselect_b32 %s, 0, %s" % (NY, NY), "s_or_b32 %s, %s, %s" % (sr(S_SPEC), sr(S_SPEC), NY)],
-        # variant codes
-        ["s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, 4, 0" % sr(S_CS),
-         "s_or_b32 %s, %s, %s" % (sr(S_CS), sr(S_CS), KS), "s_mov_b32 %s, %s" % (sr(S_CP), KP)],
+        # variant codes: masks needed (and for the PV phase, its products)
+        ["s_mov_b32 %s, %s" % (sr(S_CS), KS), "s_mov_b32 %s, %s" % (sr(S_CP), KP)],
     ]
 
 
@@ -538,7 +522,8 @@ def book_entry(par):
 def cache_copy(par, matrix, tag):
     """Copy this wave's 32 rows (32 wsub + 4 i + lane/16, i < 8) of the K
     tile T[g+1] (K slot (g+1) % 2) or the V tile T[g] (V slot g % 2) from LDS
-    to the cache, rows past the sequence masked."""
+    to the cache.  Buffer stores through a descriptor whose range ends at the
+    sequence's last row drop the rows past it."""
     r = roles(par)
     if matrix == 'k':
         slot_off, t, lo, hi = (1 - par) * K_SLOT_BYTES, r["T1"], "kcl", "kch"
@@ -548,26 +533,20 @@ def cache_copy(par, matrix, tag):
     regs = [V_VF + 4 * i for i in range(4)] + [V_KF + 4 * i for i in range(4)]
     for i in range(8):
         out.append("ds_read_b128 %s, %%[cl] offset:%d" % (vr(regs[i], 4), slot_off + 1024 * i))
-    # store bases: cache + 64 t rows (256 B each), and 4 KB past it
-    out += ["s_lshl_b32 %s, %s, 14" % (sr(S_Y), sr(t)),
-            "s_add_u32 %s, %%[%s], %s" % (sr(S_CB), lo, sr(S_Y)),
-            "s_addc_u32 %s, %%[%s], 0" % (sr(S_CB + 1), hi),
-            "s_add_u32 %s, %s, 4096" % (sr(S_CB + 2), sr(S_CB)),
-            "s_addc_u32 %s, %s, 0" % (sr(S_CB + 3), sr(S_CB + 1)),
-            # rows of the tile that exist: len - 64 t
-            "s_lshl_b32 %s, %s, 6" % (sr(S_Y), sr(t)),
-            "s_sub_i32 %s, %%[len], %s" % (sr(S_Y), sr(S_Y)),
-            "s_mov_b64 %s, exec" % sr(S_EXEC, 2),
+    # descriptor of the sequence's cache rows of this K/V head (256 B each);
+    # the tile's first row (64 t) and its 17th (+4 KB) as store offsets
+    out += ["s_mov_b32 %s, %%[%s]" % (sr(S_CB), lo),
+            "s_mov_b32 %s, %%[%s]" % (sr(S_CB + 1), hi),
+            "s_lshl_b32 %s, %%[len], 8" % sr(S_CB + 2),
+            "s_mov_b32 %s, 0x20000" % sr(S_CB + 3),
+            "s_lshl_b32 %s, %s, 14" % (sr(S_X), sr(t)),
+            "s_add_u32 %s, %s, 4096" % (sr(S_Y), sr(S_X)),
             "s_waitcnt lgkmcnt(0)"]
     for i in range(8):
-        base = sr(S_CB, 2) if i < 4 else sr(S_CB + 2, 2)
-        off = 1024 * (i % 4)
+        soff = sr(S_X) if i < 4 else sr(S_Y)
         coff = "%[coe]" if i % 2 == 0 else "%[coo]"
-        out += ["v_add_u32 %s, %d, %%[crow]" % (vr(T_ROW), 4 * i),
-                "v_cmp_gt_i32 vcc, %s, %s" % (sr(S_Y), vr(T_ROW)),
-                "s_and_b64 exec, %s, vcc" % sr(S_EXEC, 2),
-                "global_store_dwordx4 %s, %s, %s offset:%d nt" % (coff, vr(regs[i], 4), base, off)]
-    out += ["s_mov_b64 exec, %s" % sr(S_EXEC, 2)]
+        out.append("buffer_store_dwordx4 %s, %s, %s, %s offen offset:%d nt"
+                   % (vr(regs[i], 4), coff, sr(S_CB, 4), soff, 1024 * (i % 4)))
     return out
 
 
@@ -586,25 +565,33 @@ def lbl(name, par):
 
 
 def body(par):
-    """One iteration (parity par) for g = S_G, ending after its barrier: the
-    common case in line (branches not taken), every other case out of line
-    (slow_paths)."""
+    """One iteration (parity par) for g = S_G, ending after its barrier.  The
+    two phases exist once each; what differs between iterations (masked
+    scores, cache copies, Q reload, transition, the pre-loop iteration's PV
+    phase) is out of line (slow_paths), reached by branches that the common
+    iteration does not take."""
     L = lambda name: lbl(name, par)
     P = "p%d" % par
     g = sr(S_G)
     out = [# a group past its tiles only meets the barrier
            "s_cmp_ge_i32 %s, %%[nmy]" % g,
            "s_cbranch_scc1 %s" % L("bar"),
+           # cache copies first, so their stores drain during the iteration
+           "s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
+           "s_cbranch_scc0 %s" % L("cs"),
+           "%s:" % L("cdone"),
            "s_cmp_eq_u32 %s, 0" % sr(S_CS),
-           "s_cbranch_scc0 %s" % L("ss")]
-    out += score_phase(par, 'n', True, "s_n_S" + P)
+           "s_cbranch_scc0 %s" % L("ss"),
+           "%s:" % L("sgo")]
+    out += score_phase(par, "s" + P)
     out += ["%s:" % L("sdone"),
             "s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
             "s_cbranch_scc0 %s" % L("ms"),
             "%s:" % L("mdone"),
             "s_cmp_eq_u32 %s, 0" % sr(S_CP),
-            "s_cbranch_scc0 %s" % L("ps")]
-    out += pv_phase(par, 'n', True, "p_n_PV" + P)
+            "s_cbranch_scc0 %s" % L("ps"),
+            "%s:" % L("pgo")]
+    out += pv_phase(par, True, "p" + P)
     out += ["%s:" % L("pdone"),
             # end of the interval: this wave's loads have landed; everyone's have
             "%s:" % L("bar"),
@@ -614,43 +601,27 @@ def body(par):
 
 
 def slow_paths(par):
-    """Out-of-line parts of an iteration of parity par: the other score and
-    PV variants (diagonal, masked, no next tile, pre-loop), and the middle
-    part (Q reload, cache copies, transition)."""
+    """Out-of-line parts of an iteration of parity par: masking of scores
+    before a phase, cache copies, Q reload, transition, and the pre-loop
+    iteration's PV phase."""
     L = lambda name: lbl(name, par)
     P = "p%d" % par
     r = roles(par)
     g = sr(S_G)
     KS, KP = sr(r["KS"]), sr(r["KP"])
-    kidx = {'n': 0, 'd': 1, 'm': 2, 'x': 3}
-    # ---- score phase: has S = kind of g+1 != 3; kind of g
+    # ---- score phase of a tile T[g] that is not wholly visible (or of no
+    # tile: the pre-loop iteration): its half-1 scores are masked first
     out = ["%s:" % L("ss"),
-           "s_cmp_eq_u32 %s, 3" % KP,
-           "s_cbranch_scc1 %s" % L("s_noS")]
-    for kind in ('d', 'm'):
-        out += ["s_cmp_eq_u32 %s, %d" % (KS, kidx[kind]),
-                "s_cbranch_scc1 %s" % L("s_%s_S" % kind)]
-    out += ["s_branch %s" % L("s_x_S"), "%s:" % L("s_noS")]
-    for kind in ('n', 'd'):
-        out += ["s_cmp_eq_u32 %s, %d" % (KS, kidx[kind]),
-                "s_cbranch_scc1 %s" % L("s_%s_noS" % kind)]
-    out += ["s_branch %s" % L("s_m_noS")]
-    for has_s in (True, False):
-        for kind in ('n', 'd', 'm', 'x'):
-            if (kind == 'x' and not has_s) or (kind == 'n' and has_s):
-                continue
-            nm = "s_%s_%s" % (kind, "S" if has_s else "noS")
-            out += ["%s:" % L(nm)]
-            out += score_phase(par, kind, has_s, nm + P)
-            out += ["s_branch %s" % L("sdone")]
-    # ---- middle part
-    out += ["%s:" % L("ms")]
-    # the heavy block's Q after the last light score tile
-    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
-            "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
-            "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
-    # cache copies of own rows: K(T[g+1]), V(T[g])
-    out += ["s_cmp_eq_u32 %[copy], 0",
+            "s_cmp_eq_u32 %s, 1" % KS,
+            "s_cbranch_scc1 %s" % L("ssd"),
+            "s_cmp_eq_u32 %s, 0" % KS,
+            "s_cbranch_scc1 %s" % L("sgo")]
+    out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("sgo"), "%s:" % L("ssd")]
+    out += mask_ops('d', 1, s_bank(par)) + ["s_branch %s" % L("sgo")]
+    # ---- cache copies of own rows: K(T[g+1]), V(T[g]), both in LDS since
+    # the previous barrier
+    out += ["%s:" % L("cs"),
+            "s_cmp_eq_u32 %[copy], 0",
             "s_cbranch_scc1 %s" % L("nocv"),
             "s_cmp_eq_u32 %s, 3" % KP,
             "s_cbranch_scc1 %s" % L("nock"),
@@ -661,7 +632,14 @@ def slow_paths(par):
             "s_cbranch_scc1 %s" % L("nocv"),
             "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T0"])),
             "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B0"])),
-            "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv")]
+            "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv"),
+            "s_branch %s" % L("cdone")]
+    # ---- middle part
+    out += ["%s:" % L("ms")]
+    # the heavy block's Q after the last light score tile
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
+            "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
+            "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
     # at the last light tile the next tile's half-0 softmax starts the heavy
     # block's state; the light block's is kept for its store
     out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
@@ -672,33 +650,29 @@ def slow_paths(par):
             "v_mov_b32 %[l0v], 0",
             "%s:" % L("notr"),
             "s_branch %s" % L("mdone")]
-    # ---- PV phase: has PV = g >= 0; kind of g+1
+    # ---- PV phase when T[g+1] is not wholly visible (or missing): its
+    # half-0 scores are masked first (the score phase's MFMAs wrote them:
+    # wait them out); the pre-loop iteration (g < 0) has no PV products
     out += ["%s:" % L("ps"),
+            "s_nop 7", "s_nop 7", "s_nop 7",
+            "s_cmp_eq_u32 %s, 1" % KP,
+            "s_cbranch_scc1 %s" % L("psd"),
+            "s_cmp_eq_u32 %s, 0" % KP,
+            "s_cbranch_scc1 %s" % L("psv")]
+    out += mask_ops('m', 0, V_SA) + ["s_branch %s" % L("psv"), "%s:" % L("psd")]
+    out += mask_ops('d', 0, V_SA)
+    out += ["%s:" % L("psv"),
             "s_cmp_lt_i32 %s, 0" % g,
-            "s_cbranch_scc1 %s" % L("p_noPV")]
-    for kind in ('d', 'm'):
-        out += ["s_cmp_eq_u32 %s, %d" % (KP, kidx[kind]),
-                "s_cbranch_scc1 %s" % L("p_%s_PV" % kind)]
-    out += ["s_branch %s" % L("p_x_PV"), "%s:" % L("p_noPV")]
-    for kind in ('n', 'd'):
-        out += ["s_cmp_eq_u32 %s, %d" % (KP, kidx[kind]),
-                "s_cbranch_scc1 %s" % L("p_%s_noPV" % kind)]
-    out += ["s_branch %s" % L("p_m_noPV")]
-    for has_pv in (True, False):
-        for kind in ('n', 'd', 'm', 'x'):
-            if (kind == 'x' and not has_pv) or (kind == 'n' and has_pv):
-                continue
-            nm = "p_%s_%s" % (kind, "PV" if has_pv else "noPV")
-            out += ["%s:" % L(nm)]
-            out += pv_phase(par, kind, has_pv, nm + P)
-            out += ["s_branch %s" % L("pdone")]
+            "s_cbranch_scc0 %s" % L("pgo")]
+    out += pv_phase(par, False, "q" + P)
+    out += ["s_branch %s" % L("pdone")]
     return out
 
 
 LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt",
                 "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
 LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
-                "fk6", "fk7", "vd", "cl", "crow", "coe", "coo", "qo0", "qo1"]
+                "fk6", "fk7", "vd", "cl", "coe", "coo", "qo0", "qo1"]
 
 
 def loop_text():

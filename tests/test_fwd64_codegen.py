@@ -32,20 +32,37 @@ def test_generated_header_matches_generator():
         assert f.read() == text, "fwd64_phases.h is stale: run gen_fwd64.py"
 
 
+def test_mask_blocks_hide_the_causal_upper_triangle():
+    g = _gen()
+    # diagonal tile: key offset o of register r (8*(r/4) + r%4 within its key
+    # block) is hidden when o > vd; half 0's key block 1 is wholly hidden
+    for qh in (0, 1):
+        text = g.mask_ops('d', qh, 0)
+        masked = [int(x.split()[1].strip(",")[1:]) for x in text if x.startswith("v_cndmask_b32")]
+        wiped = [int(x.split()[1].strip(",")[1:]) for x in text if x.startswith("v_mov_b32") and "0xff800000" not in x]
+        assert masked == (list(range(16)) if qh == 0 else list(range(16, 32)))
+        assert wiped == (list(range(16, 32)) if qh == 0 else [])
+        for r in range(16):
+            want = "v_cmp_gt_i32 vcc, %d, %%[vd]" % (8 * (r // 4) + r % 4)
+            assert want in text
+    # masked tile: all 32 scores
+    assert sum(1 for x in g.mask_ops('m', 1, 0) if x.startswith("v_mov_b32 v")) == 33
+
+
 def test_schedule_keeps_every_instruction_once():
     g = _gen()
     # every softmax / load instruction of a phase appears in its schedule
     for par in (0, 1):
-        for kind in ("n", "d", "m"):
-            body = g.score_phase(par, kind, True, "t")
-            fill = g.softmax_ops(kind, 1, g.s_bank(par), g.V_PB, "%[m1v]", "%[l1v]", "th1")
+        for kind in ("n",):
+            body = g.score_phase(par, "t")
+            fill = g.softmax_ops(1, g.s_bank(par), g.V_PB, "%[m1v]", "%[l1v]", "th1")
             flat = [x for grp in fill for x in grp]
             for ins in flat:
                 if not ins.startswith("s_nop"):
                     assert body.count(ins) >= flat.count(ins), ins
             assert sum(1 for x in body if x.startswith("v_mfma")) == 32
             assert sum(1 for x in body if x.startswith("buffer_load")) == 16
-            pv = g.pv_phase(par, kind, True, "t")
+            pv = g.pv_phase(par, True, "t")
             assert sum(1 for x in pv if x.startswith("v_mfma")) == 32
             assert sum(1 for x in pv if x.startswith("ds_read_b64_tr_b16")) == 32
 
