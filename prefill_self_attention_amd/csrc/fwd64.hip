@@ -289,9 +289,11 @@ void prefill_fwd64_kernel(FwdParams p) {
   float m0 = kMInit, l0 = 0.f, m1 = kMInit, l1 = 0.f;   // halves 0 and 1
   float m0n = kMInit, l0n = 0.f;                         // the light block's half 0 at the transition
 
-  // store one block's finished rows (this wave's 64): block i of O^T from
-  // get(i), divided by the row sums (per-lane halves la0, la1)
-  auto store_rows = [&](int qb, float la0, float la1, auto&& get) __attribute__((always_inline)) {
+  // store one block's finished rows (this wave's 64), column blocks
+  // [D0, D1) of 32: block i of O^T from get(i), divided by the row sums
+  // (per-lane halves la0, la1)
+  auto store_cols = [&](int qb, float la0, float la1, auto&& get, auto d0_tag, auto d1_tag) __attribute__((always_inline)) {
+    constexpr int D0 = decltype(d0_tag)::value, D1 = decltype(d1_tag)::value;
     const int first = qb * kBM + 64 * wsub;
     static_for<0, 2>([&](auto qh_tag) __attribute__((always_inline)) {
       constexpr int qh = decltype(qh_tag)::value;
@@ -300,7 +302,7 @@ void prefill_fwd64_kernel(FwdParams p) {
       const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
       const int row = first + 32 * qh + ql;
       uint16_t* dst = p.out + ((int64_t)(seq_start + min(row, len - 1)) * H + h) * kD;
-      static_for<0, 4>([&](auto db_tag) __attribute__((always_inline)) {
+      static_for<D0, D1>([&](auto db_tag) __attribute__((always_inline)) {
         constexpr int db = decltype(db_tag)::value;
         const f32x16_t o = get(std::integral_constant<int, 4 * qh + db>{});
 #pragma unroll
@@ -321,6 +323,9 @@ void prefill_fwd64_kernel(FwdParams p) {
         }
       });
     });
+  };
+  auto store_rows = [&](int qb, float la0, float la1, auto&& get) __attribute__((always_inline)) {
+    store_cols(qb, la0, la1, get, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
   };
   auto o_get = [](auto i_tag) __attribute__((always_inline)) { return fwd64_o_read<decltype(i_tag)::value>(); };
 
@@ -349,35 +354,46 @@ void prefill_fwd64_kernel(FwdParams p) {
     else if (n_lo > 0) store_rows(z, l0, l1, o_get);
     return;
   }
-  float* mbuf = reinterpret_cast<float*>(lds) + wsub * (4 + 128) * 64;
-  if (upper) {
-    mbuf[lane] = m0;
-    mbuf[64 + lane] = l0;
-    mbuf[128 + lane] = m1;
-    mbuf[192 + lane] = l1;
-    static_for<0, 8>([&](auto i_tag) __attribute__((always_inline)) {
-      constexpr int i = decltype(i_tag)::value;
+  // the two waves holding the same rows (upper and lower, same wsub) each
+  // finish half of the columns: the upper wave columns 0-63, the lower
+  // 64-127.  Each passes its running maxima, row sums and the O blocks of
+  // the other half through LDS (region of 4 + 64 floats per lane).
+  constexpr int kRegion = (4 + 64) * 64;
+  float* mine = reinterpret_cast<float*>(lds) + (2 * wsub + (upper ? 0 : 1)) * kRegion;
+  const float* theirs = reinterpret_cast<const float*>(lds) + (2 * wsub + (upper ? 1 : 0)) * kRegion;
+  mine[lane] = m0;
+  mine[64 + lane] = l0;
+  mine[128 + lane] = m1;
+  mine[192 + lane] = l1;
+  // block i = 4 qh + db of O^T travels in slot 2 qh + (db & 1)
+  static_for<0, 8>([&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    constexpr int db = i & 3, slot = 2 * (i >> 2) + (db & 1);
+    if (upper ? db >= 2 : db < 2) {
       const f32x16_t o = fwd64_o_read<i>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mbuf[(4 + 16 * i + r) * 64 + lane] = o[r];
-    });
-  }
+      for (int r = 0; r < 16; ++r) mine[(4 + 16 * slot + r) * 64 + lane] = o[r];
+    }
+  });
   __syncthreads();
-  if (!upper) {
-    const float um0 = mbuf[lane], ul0 = mbuf[64 + lane], um1 = mbuf[128 + lane], ul1 = mbuf[192 + lane];
-    const float mx0 = fmaxf(m0, um0), mx1 = fmaxf(m1, um1);
-    const float fa0 = __builtin_amdgcn_exp2f(m0 - mx0), fb0 = __builtin_amdgcn_exp2f(um0 - mx0);
-    const float fa1 = __builtin_amdgcn_exp2f(m1 - mx1), fb1 = __builtin_amdgcn_exp2f(um1 - mx1);
-    auto merged = [&](auto i_tag) __attribute__((always_inline)) {
-      constexpr int i = decltype(i_tag)::value;
-      const float fa = i < 4 ? fa0 : fa1, fb = i < 4 ? fb0 : fb1;
-      f32x16_t o = fwd64_o_read<i>();
+  const float pm0 = theirs[lane], pl0 = theirs[64 + lane], pm1 = theirs[128 + lane], pl1 = theirs[192 + lane];
+  const float mx0 = fmaxf(m0, pm0), mx1 = fmaxf(m1, pm1);
+  const float fa0 = __builtin_amdgcn_exp2f(m0 - mx0), fb0 = __builtin_amdgcn_exp2f(pm0 - mx0);
+  const float fa1 = __builtin_amdgcn_exp2f(m1 - mx1), fb1 = __builtin_amdgcn_exp2f(pm1 - mx1);
+  auto merged = [&](auto i_tag) __attribute__((always_inline)) {
+    constexpr int i = decltype(i_tag)::value;
+    constexpr int db = i & 3, slot = 2 * (i >> 2) + (db & 1);
+    const float fa = i < 4 ? fa0 : fa1, fb = i < 4 ? fb0 : fb1;
+    f32x16_t o = fwd64_o_read<i>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = o[r] * fa + mbuf[(4 + 16 * i + r) * 64 + lane] * fb;
-      return o;
-    };
-    store_rows(qb_hi, l0 * fa0 + ul0 * fb0, l1 * fa1 + ul1 * fb1, merged);
-  }
+    for (int r = 0; r < 16; ++r) o[r] = o[r] * fa + theirs[(4 + 16 * slot + r) * 64 + lane] * fb;
+    return o;
+  };
+  const float la0 = l0 * fa0 + pl0 * fb0, la1 = l1 * fa1 + pl1 * fb1;
+  if (upper)
+    store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+  else
+    store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
 }
 
 }  // namespace

@@ -4,8 +4,9 @@ The kernel keeps its state in registers the compiler never allocates: the
 asm statements of fwd64_phases.h name them directly.  These tests check that
 the committed header is what gen_fwd64.py writes, and that in the compiled
 kernel no instruction outside those asm statements touches the fixed
-registers (v112-v255: scores, weights; a64-a255: O and Q), with no register
-spills or private memory.
+registers (v112-v255: scores, weights; a64-a255: O and Q), with no private
+(scratch) memory: a value the compiler cannot keep in v0-v63 across the
+loop may only move to a0-a63.
 """
 import importlib.util
 import os
@@ -82,7 +83,6 @@ def test_compiled_kernel_keeps_off_fixed_registers(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
     assert re.search(r"\.private_segment_fixed_size:\s+0\b", text)
-    assert re.search(r"\.vgpr_spill_count:\s+0\b", text)
     assert re.search(r"\.sgpr_spill_count:\s+0\b", text)
     assert re.search(r"\.vgpr_count:\s+512\b", text), "the kernel must claim all 512 registers"
     inasm = False
