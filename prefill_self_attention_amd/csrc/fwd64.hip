@@ -158,9 +158,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void prefill_fwd64_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   claim_registers();
-  const int h = __builtin_amdgcn_workgroup_id_x();
-  const int b = __builtin_amdgcn_workgroup_id_y();
-  const int z = __builtin_amdgcn_workgroup_id_z();
+  // Work-group order.  Units (sequence, head) are spread over the 8 XCDs
+  // (the dispatcher places work-group i of a 1-D grid on XCD i % 8), and a
+  // unit's block pairs z follow one another in its XCD's dispatch stream, so
+  // the pairs that read the same head's K/V run at the same time and share
+  // that XCD's L2.  With H a multiple of 8, XCD x holds heads
+  // [x H/8, (x+1) H/8) of every sequence (grouped K/V heads stay together).
+  int h, b, z;
+  {
+    const int wg = __builtin_amdgcn_workgroup_id_x();
+    const int xcd = wg & 7, s = wg >> 3;
+    const int u = s / p.grid_z;
+    z = s - u * p.grid_z;
+    if (p.num_heads % 8 == 0) {
+      const int hx = p.num_heads / 8;
+      b = u / hx;
+      h = xcd * hx + (u - b * hx);
+    } else {
+      const int unit = u * 8 + xcd;
+      b = unit / p.num_heads;
+      h = unit - b * p.num_heads;
+    }
+    if (b >= p.num_seqs) return;  // padding of the last units (every wave returns)
+  }
   const int64_t H = p.num_heads;
   const int64_t HK = p.num_kv_heads;
   const int seq_start = p.cu[b];
@@ -405,8 +425,13 @@ bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, in
 }
 
 hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream) {
-  dim3 grid(p.num_heads, num_seqs, p.grid_z);
-  hipLaunchKernelGGL(prefill_fwd64_kernel, grid, dim3(kThreads), 0, stream, p);
+  FwdParams q = p;
+  q.num_seqs = num_seqs;
+  // units per XCD (8 XCDs), each with grid_z block pairs
+  const int64_t per_xcd = ((int64_t)p.num_heads * num_seqs + 7) / 8;
+  const int64_t grid = 8 * per_xcd * p.grid_z;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prefill_fwd64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct FwdParams {
   // block_table[b * bt_stride + j / 16]
   const int32_t* block_table;
   int32_t bt_stride;
+  int32_t num_seqs;         // B (set by the launch of the 64-row kernel)
 };
 
 constexpr int kPageRows = 16;  // tokens per cache block
