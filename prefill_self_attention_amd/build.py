@@ -1,6 +1,9 @@
-"""Build libprefill_attn.so (HIP, gfx950) in-tree with hipcc.
+"""Build libprefill_attn.so (HIP, gfx950) in-tree with hipcc, and the small
+libpa_mfma_peak.so (a matrix-core rate probe the benchmark reports beside
+the attention rate).
 
 Run as ``python -m prefill_self_attention_amd.build`` or call ``build()``.
+Prints a warning for every kernel that uses scratch (private) memory.
 Flags: -O3 for gfx950 only; IEEE mode off with relaxed NaN handling (no
 canonicalising moves before max/min); packed-fp32 VALU ops disabled in device code
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``; the host pass prints a
@@ -18,6 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libprefill_attn.so")
 SOURCES = ["api.hip", "prefill_fwd.hip", "splitkv.hip", "fwd64.hip"]
+PEAK_LIB = os.path.join(HERE, "libpa_mfma_peak.so")
+PEAK_SOURCES = ["mfma_peak.hip"]
 ARCH = "gfx950"
 
 
@@ -26,15 +31,30 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+def scratch_kernels(remarks: str):
+    """(kernel, bytes per lane) for every kernel whose resource-usage remark
+    reports scratch memory."""
+    found, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].split(" [-R")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name is not None:
+            n = int(line.split("ScratchSize [bytes/lane]:", 1)[1].split()[0])
+            if n > 0:
+                found.append((name, n))
+    return found
+
+
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            # no NaN canonicalisation around max/min (inputs are finite by contract)
            "-fno-honor-nans", "-mno-amdgpu-ieee",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument",
+           "-Rpass-analysis=kernel-resource-usage",
            "-I", INCLUDE, "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -45,8 +65,13 @@ def build(verbose: bool = False) -> str:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out, flush=True)
+    for name, n in scratch_kernels(out):
+        print("build.py: warning: kernel %s uses %d bytes/lane of scratch memory" % (name, n),
+              file=sys.stderr, flush=True)
+    if verbose:
+        msgs = [l for l in out.splitlines() if "remark:" not in l and l.strip()]
+        if msgs:
+            print("\n".join(msgs), flush=True)
     # a kernel whose host-side launch stub was not emitted leaves an undefined
     # symbol that only shows when the library is loaded: fail here instead
     nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], stdout=subprocess.PIPE,
@@ -55,8 +80,13 @@ def build(verbose: bool = False) -> str:
     if missing:
         os.remove(tmp)
         raise RuntimeError("hipcc emitted no launch stub for:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _compile(PEAK_SOURCES, PEAK_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
