@@ -67,7 +67,8 @@ typedef enum {
     PA_ERR_SEQLENS = 7,   /* check mode: cu_seqlens[0] != 0, decreasing, or a length > max_seqlen */
     PA_ERR_CAPACITY = 8,  /* check mode: a prefix length < 0, prefix + length > cache_capacity, or a block id outside the pool */
     PA_ERR_HIP = 9,       /* a HIP runtime call failed; see pa_last_hip_error() */
-    PA_ERR_WORKSPACE = 10 /* split-KV: workspace_bytes below prefill_attn_splitkv_workspace_size() */
+    PA_ERR_WORKSPACE = 10, /* split-KV: workspace_bytes below prefill_attn_splitkv_workspace_size() */
+    PA_ERR_NOALLOC_LIMIT = 11 /* no-allocation split-KV: the workspace the problem needs exceeds prefill_attn_splitkv_noalloc_limit() */
 } pa_status;
 
 /*
@@ -243,6 +244,39 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t *q, const uint16_t *k, con
                                        int32_t cache_capacity, uint16_t *out, float scale,
                                        hipStream_t stream, const int32_t *prefix_lens,
                                        void *workspace, size_t workspace_bytes);
+
+/*
+ * prefill_attn_chunked_splitkv without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing: the plan,
+ * partial results and counters live in a fixed array of
+ * prefill_attn_splitkv_noalloc_limit() bytes (128 MiB) that the library holds
+ * on each GPU it runs on until the process ends.  The array of the current
+ * device is used (its address is looked up on the first call on a device).
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: each call's plan writes
+ * what the call reads).  Calls that overlap in time on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ * Check mode's host-side metadata checks are not run (they copy metadata to
+ * host memory).
+ *
+ * Arguments, results and errors as prefill_attn_chunked_splitkv, without
+ * workspace and workspace_bytes; PA_ERR_NOALLOC_LIMIT when
+ * prefill_attn_splitkv_workspace_size(num_seqs, num_tokens, num_heads,
+ * head_dim, cache_capacity) exceeds the array (nothing is enqueued).
+ */
+pa_status prefill_attn_chunked_splitkv_noalloc(const uint16_t *q, const uint16_t *k,
+                                               const uint16_t *v, const int32_t *cu_seqlens,
+                                               int32_t num_seqs, int32_t max_seqlen,
+                                               int32_t num_tokens, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               uint16_t *k_cache, uint16_t *v_cache,
+                                               int32_t cache_capacity, uint16_t *out, float scale,
+                                               hipStream_t stream, const int32_t *prefix_lens);
+
+/* Bytes of the per-GPU array prefill_attn_chunked_splitkv_noalloc uses. */
+size_t prefill_attn_splitkv_noalloc_limit(void);
 
 /*
  * Split-KV chunked prefill over a paged KV cache [P2 §4.2 and P5 §3.4: the

@@ -57,6 +57,11 @@ def load() -> ctypes.CDLL:
     lib.prefill_attn_chunked_splitkv_paged.restype = ctypes.c_int
     lib.prefill_attn_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.prefill_attn_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.prefill_attn_chunked_splitkv_noalloc.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                                         p, p, i32, p, ctypes.c_float, p, p]
+    lib.prefill_attn_chunked_splitkv_noalloc.restype = ctypes.c_int
+    lib.prefill_attn_splitkv_noalloc_limit.argtypes = []
+    lib.prefill_attn_splitkv_noalloc_limit.restype = ctypes.c_size_t
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_set_check_mode.argtypes = [ctypes.c_int]
@@ -229,6 +234,42 @@ def prefill_attn_chunked_splitkv(q, k, v, cu_seqlens, k_cache, v_cache, out, pre
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), N, H, HK, D,
         _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
         _stream(stream), _ptr(prefix_lens), _ptr(workspace), workspace.numel())
+    if st != PA_OK:
+        raise PrefillAttnError(st)
+    return out
+
+
+def splitkv_noalloc_limit() -> int:
+    """Bytes of the per-GPU array prefill_attn_chunked_splitkv_noalloc uses."""
+    return int(load().prefill_attn_splitkv_noalloc_limit())
+
+
+def prefill_attn_chunked_splitkv_noalloc(q, k, v, cu_seqlens, k_cache, v_cache, out, prefix_lens,
+                                         scale=None, max_seqlen=None, stream=None):
+    """prefill_attn_chunked_splitkv with the library's fixed per-GPU scratch
+    array in place of a workspace: allocates nothing.  Calls that overlap in
+    time on one GPU race on the array.  Returns out."""
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("out", out)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    _check_tensor("prefix_lens", prefix_lens, torch.int32)
+    H, HK, D = _heads(q, k, v)
+    N = q.shape[0]
+    B = cu_seqlens.shape[0] - 1
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[1] != HK or \
+            k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [B, HK, cap, D]")
+    cap = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen is None:
+        max_seqlen = _max_seqlen(cu_seqlens)
+    st = load().prefill_attn_chunked_splitkv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, int(max_seqlen), N, H, HK, D,
+        _ptr(k_cache), _ptr(v_cache), int(cap), _ptr(out), ctypes.c_float(scale),
+        _stream(stream), _ptr(prefix_lens))
     if st != PA_OK:
         raise PrefillAttnError(st)
     return out

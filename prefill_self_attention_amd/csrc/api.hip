@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -280,7 +281,7 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       int32_t cache_capacity, uint16_t* out, float scale, hipStream_t stream,
                       const int32_t* prefix_lens, void* workspace, size_t workspace_bytes,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
-                      int32_t num_blocks) {
+                      int32_t num_blocks, bool host_checks = true) {
   pa_status st = check_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_heads, head_dim,
                               k_cache, v_cache, out, scale);
   if (st != PA_OK) return st;
@@ -305,7 +306,7 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       pa::split_layout(num_seqs, num_tokens, num_heads, head_dim, cache_capacity);
   if (workspace_bytes < L.bytes) return PA_ERR_WORKSPACE;
   if (num_seqs == 0 || max_seqlen == 0 || num_tokens == 0) return PA_OK;
-  if (check_mode()) {
+  if (host_checks && check_mode()) {
     st = check_metadata(cu_seqlens, num_seqs, max_seqlen, prefix_lens, cache_capacity, stream);
     if (st != PA_OK) return st;
     if (block_table) {
@@ -386,6 +387,68 @@ pa_status prefill_attn_chunked_splitkv(const uint16_t* q, const uint16_t* k, con
   return splitkv_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_tokens, num_heads,
                      num_kv_heads, head_dim, k_cache, v_cache, cache_capacity, out, scale, stream,
                      prefix_lens, workspace, workspace_bytes, nullptr, 0, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of prefill_attn_chunked_splitkv_noalloc: one array per GPU, in
+// place of the caller's workspace, held until the process ends.  In host
+// code `scratch` only stands for the symbol: its device address on each
+// device comes from hipGetSymbolAddress (noalloc_scratch) and only that
+// address is passed on.
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's scratch address, looked up on the first call on that
+// device (with it current, as every call here launches on the current
+// device).
+pa_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prefill_attn_splitkv_noalloc_limit(void) { return kNoAllocScratchBytes; }
+
+pa_status prefill_attn_chunked_splitkv_noalloc(const uint16_t* q, const uint16_t* k,
+                                               const uint16_t* v, const int32_t* cu_seqlens,
+                                               int32_t num_seqs, int32_t max_seqlen,
+                                               int32_t num_tokens, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               uint16_t* k_cache, uint16_t* v_cache,
+                                               int32_t cache_capacity, uint16_t* out, float scale,
+                                               hipStream_t stream, const int32_t* prefix_lens) {
+  // the problem's workspace must fit the array (0: invalid sizes, which the
+  // common checks below report)
+  const size_t need = prefill_attn_splitkv_workspace_size(num_seqs, num_tokens, num_heads,
+                                                          head_dim, cache_capacity);
+  if (need > kNoAllocScratchBytes) return PA_ERR_NOALLOC_LIMIT;
+  void* ws = nullptr;
+  pa_status st = noalloc_scratch(&ws);
+  if (st != PA_OK) return st;
+  return splitkv_run(q, k, v, cu_seqlens, num_seqs, max_seqlen, num_tokens, num_heads,
+                     num_kv_heads, head_dim, k_cache, v_cache, cache_capacity, out, scale, stream,
+                     prefix_lens, ws, kNoAllocScratchBytes, nullptr, 0, 0, /*host_checks=*/false);
 }
 
 pa_status prefill_attn_chunked_splitkv_paged(
@@ -519,6 +582,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_CAPACITY: return "PA_ERR_CAPACITY: prefix_lens must be >= 0 with prefix + length <= cache_capacity";
     case PA_ERR_HIP: return "PA_ERR_HIP: a HIP runtime call failed (see pa_last_hip_error)";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace smaller than prefill_attn_splitkv_workspace_size()";
+    case PA_ERR_NOALLOC_LIMIT: return "PA_ERR_NOALLOC_LIMIT: the problem needs more scratch than prefill_attn_splitkv_noalloc_limit() bytes";
     default: return "unknown pa_status";
   }
 }

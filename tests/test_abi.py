@@ -36,7 +36,8 @@ def test_header_declares_expected_entry_points():
         "prefill_attn_varlen_fp8",
         "prefill_attn_chunked_splitkv_paged",
         "prefill_attn_splitkv_workspace_size", "pa_status_string", "pa_set_check_mode",
-        "pa_last_hip_error"])
+        "pa_last_hip_error", "prefill_attn_chunked_splitkv_noalloc",
+        "prefill_attn_splitkv_noalloc_limit"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         s = P.pa_status_string(code)
         assert s.startswith("PA_")
     assert P.pa_status_string(42) == "unknown pa_status"
@@ -203,3 +204,17 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libprefill_attn.so")
     with pytest.raises(RuntimeError, match="not built"):
         binding.load()
+
+
+def test_noalloc_limit_and_rejection(lib):
+    # the fixed array's size, and a problem whose workspace exceeds it is
+    # refused before any HIP call (dummy 16-byte aligned pointers)
+    assert P.splitkv_noalloc_limit() == 128 << 20
+    need = P.splitkv_workspace_size(1, 1 << 20, 64, 128, 1 << 20)
+    assert need > P.splitkv_noalloc_limit()
+    d = ctypes.c_void_p(0x10000)
+    st = lib.prefill_attn_chunked_splitkv_noalloc(d, d, d, d, 1, 1 << 20, 1 << 20, 64, 64, 128,
+                                                  ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000),
+                                                  1 << 20, ctypes.c_void_p(0x40000), ctypes.c_float(0.1),
+                                                  None, ctypes.c_void_p(0x50000))
+    assert st == 11 and P.pa_status_string(st).startswith("PA_ERR_NOALLOC_LIMIT")
