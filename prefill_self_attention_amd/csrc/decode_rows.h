@@ -68,15 +68,16 @@ __device__ __forceinline__ float lane_read(float x, int src) {
 template <int D, int GC, int W>
 constexpr int red_floats() { return W * GC * (2 + D); }
 
-// Unit g of the decode list (item g / (H / GC), query heads GC * (g % (H / GC))
-// onward), run by the first W waves of the work-group; red is LDS of
+// Unit g of the decode list (item it = {sequence, segment, segments}, query
+// heads GC * (g % (H / GC)) onward), run by the first W waves of the
+// work-group; red is LDS of
 // red_floats<D, GC, W>() floats.  Unless `next` is null, thread 0 also
 // takes the next value of counter *next (issued first, so its latency hides
 // behind the unit) and leaves it in *taken (LDS) before the final
 // work-group barrier, after which every wave may read it and red may be
 // reused.
 template <int D, int GC, bool kPaged, int W>
-__device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float* red,
+__device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, int4 it, float* red,
                                             unsigned long long* next, unsigned long long* taken) {
   constexpr int LPK = D / 8, KPI = 64 / LPK;
   // key steps whose loads are issued together (two such groups in flight):
@@ -94,7 +95,6 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float
 
   unsigned long long nxt = 0;
   if (next && tid == 0) nxt = atomicAdd(next, 1ull);
-  const int4 it = p.dec_items[g / units];
   const int h0 = (int)(g % units) * GC;
   const int hk = h0 / G;
   const int b = it.x, s = it.y, ns = it.z;
@@ -293,6 +293,13 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float
   // every wave read the previous *taken before the barrier above
   if (next && tid == 0) *taken = nxt;
   __syncthreads();  // red is rewritten by the next unit
+}
+
+// Unit g of the plan's decode list p.dec_items.
+template <int D, int GC, bool kPaged, int W>
+__device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, float* red,
+                                            unsigned long long* next, unsigned long long* taken) {
+  decode_unit<D, GC, kPaged, W>(p, g, p.dec_items[g / (p.num_heads / GC)], red, next, taken);
 }
 
 }  // namespace dec

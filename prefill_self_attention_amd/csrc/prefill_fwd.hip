@@ -933,8 +933,29 @@ __global__ __launch_bounds__(kThreads)
 void prefill_fwd_kernel(FwdParams p) {
   // raw id builtins: the device library's id helpers are built with IEEE mode
   // on and would not inline into this IEEE-off kernel
-  fwd_item<D, kChunked, false, kCache>(p, __builtin_amdgcn_workgroup_id_x(), __builtin_amdgcn_workgroup_id_y(),
-                                      __builtin_amdgcn_workgroup_id_z(), 0, 1);
+  const int h = __builtin_amdgcn_workgroup_id_x(), b = __builtin_amdgcn_workgroup_id_y();
+  int z = __builtin_amdgcn_workgroup_id_z();
+  if constexpr (kChunked && kCache == kCacheBf16) {
+    // Chunked: a length-1 row (a decode row) reads its whole cached context
+    // for one query, a GEMV: it runs as one VALU decode unit (decode_rows.h)
+    // over all its keys, written straight to out and to the cache, instead
+    // of as a 128-row MFMA block holding one row ["大模型 Prompt Prefill 阶段的高效
+    // Batching 与算子排布" §3; untitled page www.zwxr.cn/news/300951 §1.2].
+    const int len = p.cu[b + 1] - p.cu[b];
+    if (len == 1) {
+      if (z == 0) {
+        float* const red = reinterpret_cast<float*>(fwd_lds<D, kChunked, false, kCache, false, 0>());
+        static_assert(dec::red_floats<D, 1, kWaves>() * 4 <= Cfg<D>::kLdsBytes, "decode reduction exceeds LDS");
+        dec::decode_unit<D, 1, false, kWaves>(p, (int64_t)h, make_int4(b, 0, 1, 0), red, nullptr, nullptr);
+      }
+      return;
+    }
+    // pairs in reverse order: the last z-layer holds only the longest
+    // sequences' pairs, so the chunk's long blocks are dispatched first and
+    // the decode rows fill the compute units behind them
+    z = p.grid_z - 1 - z;
+  }
+  fwd_item<D, kChunked, false, kCache>(p, h, b, z, 0, 1);
 }
 
 // Split-KV chunked prefill: a persistent grid walks the planned items, item i
