@@ -311,7 +311,11 @@ void prefill_fwd64_kernel(FwdParams p) {
 
   // store one block's finished rows (this wave's 64), column blocks
   // [D0, D1) of 32: block i of O^T from get(i), divided by the row sums
-  // (per-lane halves la0, la1)
+  // (per-lane halves la0, la1).  Buffer stores through a descriptor that
+  // ends at the sequence's last row drop the rows past it.
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.out + ((int64_t)seq_start * H + h) * kD), (short)0, (int)((uint32_t)(len - 1) * rsq + kRowBytes),
+      0x00020000);
   auto store_cols = [&](int qb, float la0, float la1, auto&& get, auto d0_tag, auto d1_tag) __attribute__((always_inline)) {
     constexpr int D0 = decltype(d0_tag)::value, D1 = decltype(d1_tag)::value;
     const int first = qb * kBM + 64 * wsub;
@@ -319,9 +323,8 @@ void prefill_fwd64_kernel(FwdParams p) {
       constexpr int qh = decltype(qh_tag)::value;
       const float lsum = qh == 0 ? la0 : la1;
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
-      const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
-      const int row = first + 32 * qh + ql;
-      uint16_t* dst = p.out + ((int64_t)(seq_start + min(row, len - 1)) * H + h) * kD;
+      const float inv = __builtin_amdgcn_rcpf(__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+      const uint32_t rowoff = (uint32_t)(first + 32 * qh + ql) * rsq;
       static_for<D0, D1>([&](auto db_tag) __attribute__((always_inline)) {
         constexpr int db = decltype(db_tag)::value;
         const f32x16_t o = get(std::integral_constant<int, 4 * qh + db>{});
@@ -339,7 +342,7 @@ void prefill_fwd64_kernel(FwdParams p) {
           const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
           const uint32_t o0 = hl ? x0[0] : x0[1], o1 = hl ? x1[0] : x1[1];
           const u32x4_t w = hl ? u32x4_t{o0, o1, b0, b1} : u32x4_t{a0, a1, o0, o1};
-          if (row < len) *(u32x4_t*)(dst + 32 * db + 8 * (hl ? cb : ca)) = w;
+          __builtin_amdgcn_raw_buffer_store_b128(w, orsrc, rowoff + 2 * (32 * db + 8 * (hl ? cb : ca)), 0, 0);
         }
       });
     });
@@ -378,13 +381,11 @@ void prefill_fwd64_kernel(FwdParams p) {
   // finish half of the columns: the upper wave columns 0-63, the lower
   // 64-127.  Each passes its running maxima, row sums and the O blocks of
   // the other half through LDS (region of 4 + 64 floats per lane).
-  constexpr int kRegion = (4 + 64) * 64;
-  float* mine = reinterpret_cast<float*>(lds) + (2 * wsub + (upper ? 0 : 1)) * kRegion;
-  const float* theirs = reinterpret_cast<const float*>(lds) + (2 * wsub + (upper ? 1 : 0)) * kRegion;
-  mine[lane] = m0;
-  mine[64 + lane] = l0;
-  mine[128 + lane] = m1;
-  mine[192 + lane] = l1;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kRegion = 17 * 64;  // float4 per lane: (m0, l0, m1, l1), then 16 of O
+  f32x4_t* mine = reinterpret_cast<f32x4_t*>(lds) + (2 * wsub + (upper ? 0 : 1)) * kRegion;
+  const f32x4_t* theirs = reinterpret_cast<const f32x4_t*>(lds) + (2 * wsub + (upper ? 1 : 0)) * kRegion;
+  mine[lane] = f32x4_t{m0, l0, m1, l1};
   // block i = 4 qh + db of O^T travels in slot 2 qh + (db & 1)
   static_for<0, 8>([&](auto i_tag) __attribute__((always_inline)) {
     constexpr int i = decltype(i_tag)::value;
@@ -392,11 +393,13 @@ void prefill_fwd64_kernel(FwdParams p) {
     if (upper ? db >= 2 : db < 2) {
       const f32x16_t o = fwd64_o_read<i>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(4 + 16 * slot + r) * 64 + lane] = o[r];
+      for (int r = 0; r < 4; ++r)
+        mine[(1 + 4 * slot + r) * 64 + lane] = f32x4_t{o[4 * r], o[4 * r + 1], o[4 * r + 2], o[4 * r + 3]};
     }
   });
   __syncthreads();
-  const float pm0 = theirs[lane], pl0 = theirs[64 + lane], pm1 = theirs[128 + lane], pl1 = theirs[192 + lane];
+  const f32x4_t ml = theirs[lane];
+  const float pm0 = ml[0], pl0 = ml[1], pm1 = ml[2], pl1 = ml[3];
   const float mx0 = fmaxf(m0, pm0), mx1 = fmaxf(m1, pm1);
   const float fa0 = __builtin_amdgcn_exp2f(m0 - mx0), fb0 = __builtin_amdgcn_exp2f(pm0 - mx0);
   const float fa1 = __builtin_amdgcn_exp2f(m1 - mx1), fb1 = __builtin_amdgcn_exp2f(pm1 - mx1);
@@ -406,7 +409,11 @@ void prefill_fwd64_kernel(FwdParams p) {
     const float fa = i < 4 ? fa0 : fa1, fb = i < 4 ? fb0 : fb1;
     f32x16_t o = fwd64_o_read<i>();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] = o[r] * fa + theirs[(4 + 16 * slot + r) * 64 + lane] * fb;
+    for (int r = 0; r < 4; ++r) {
+      const f32x4_t x = theirs[(1 + 4 * slot + r) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * r + e] = o[4 * r + e] * fa + x[e] * fb;
+    }
     return o;
   };
   const float la0 = l0 * fa0 + pl0 * fb0, la1 = l1 * fa1 + pl1 * fb1;

@@ -564,12 +564,98 @@ def lbl(name, par):
     return ".L%s_p%d_%%=" % (name, par)
 
 
+def copy_part(par):
+    """Cache copies of own rows: K(T[g+1]) and V(T[g]), both in LDS since the
+    previous barrier (run when S_SPEC is set)."""
+    L = lambda name: lbl(name, par)
+    P = "p%d" % par
+    r = roles(par)
+    g = sr(S_G)
+    return (["s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
+             "s_cbranch_scc1 %s" % L("nocv"),
+             "s_cmp_eq_u32 %[copy], 0",
+             "s_cbranch_scc1 %s" % L("nocv"),
+             "s_cmp_eq_u32 %s, 3" % sr(r["KP"]),
+             "s_cbranch_scc1 %s" % L("nock"),
+             "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T1"])),
+             "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B1"])),
+             "s_cbranch_scc0 %s" % L("nock")] + cache_copy(par, 'k', P) + ["%s:" % L("nock"),
+            "s_cmp_lt_i32 %s, 0" % g,
+            "s_cbranch_scc1 %s" % L("nocv"),
+            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T0"])),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B0"])),
+            "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv")])
+
+
+def score_mask_part(par):
+    """Score phase of a tile T[g] that is not wholly visible (or of no tile:
+    the pre-loop iteration): its half-1 scores are masked first."""
+    L = lambda name: lbl(name, par)
+    KS = sr(roles(par)["KS"])
+    out = ["s_cmp_eq_u32 %s, 0" % sr(S_CS),
+           "s_cbranch_scc1 %s" % L("sgo"),
+           "s_cmp_eq_u32 %s, 1" % KS,
+           "s_cbranch_scc1 %s" % L("ssd"),
+           "s_cmp_eq_u32 %s, 0" % KS,
+           "s_cbranch_scc1 %s" % L("sgo")]
+    out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("sgo"), "%s:" % L("ssd")]
+    out += mask_ops('d', 1, s_bank(par))
+    return out
+
+
+def middle_part(par):
+    """Between the phases (run when S_SPEC is set): the heavy block's Q after
+    the last light score tile; at the last light tile the next tile's half-0
+    softmax starts the heavy block's state (the light block's is kept for
+    its store)."""
+    L = lambda name: lbl(name, par)
+    g = sr(S_G)
+    out = ["s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
+           "s_cbranch_scc1 %s" % L("notr"),
+           "s_add_i32 %s, %s, 1" % (sr(S_X), g),
+           "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
+           "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
+    out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
+            "s_cbranch_scc0 %s" % L("notr"),
+            "v_mov_b32 %[m0n], %[m0v]",
+            "v_mov_b32 %[l0n], %[l0v]",
+            "v_mov_b32 %%[m0v], %s" % MINIT,
+            "v_mov_b32 %[l0v], 0",
+            "%s:" % L("notr")]
+    return out
+
+
+def pv_mask_part(par):
+    """PV phase when T[g+1] is not wholly visible (or missing): its half-0
+    scores are masked first (the score phase's MFMAs wrote them: wait them
+    out); the pre-loop iteration (g < 0) leaves for its phase without PV
+    products."""
+    L = lambda name: lbl(name, par)
+    KP = sr(roles(par)["KP"])
+    out = ["s_cmp_eq_u32 %s, 0" % sr(S_CP),
+           "s_cbranch_scc1 %s" % L("pgo"),
+           "s_nop 7", "s_nop 7", "s_nop 7",
+           "s_cmp_eq_u32 %s, 1" % KP,
+           "s_cbranch_scc1 %s" % L("psd"),
+           "s_cmp_eq_u32 %s, 0" % KP,
+           "s_cbranch_scc1 %s" % L("psv")]
+    out += mask_ops('m', 0, V_SA) + ["s_branch %s" % L("psv"), "%s:" % L("psd")]
+    out += mask_ops('d', 0, V_SA)
+    out += ["%s:" % L("psv"),
+            "s_cmp_lt_i32 %s, 0" % sr(S_G),
+            "s_cbranch_scc1 %s" % L("pre")]
+    return out
+
+
 def body(par):
     """One iteration (parity par) for g = S_G, ending after its barrier.  The
-    two phases exist once each; what differs between iterations (masked
-    scores, cache copies, Q reload, transition, the pre-loop iteration's PV
-    phase) is out of line (slow_paths), reached by branches that the common
-    iteration does not take."""
+    two phases exist once each; what differs between iterations (cache
+    copies, masked scores, Q reload, transition) sits in line in two blocks,
+    one before each phase, that the common iteration jumps over with one
+    branch each: code met only on a few iterations then lies on the
+    instruction fetch's sequential path instead of at distant targets that
+    each cost a cold instruction-cache miss.  The pre-loop iteration's PV
+    phase (no products) is out of line (slow_paths)."""
     L = lambda name: lbl(name, par)
     P = "p%d" % par
     g = sr(S_G)
@@ -577,20 +663,15 @@ def body(par):
            "s_cmp_ge_i32 %s, %%[nmy]" % g,
            "s_cbranch_scc1 %s" % L("bar"),
            # cache copies first, so their stores drain during the iteration
-           "s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
-           "s_cbranch_scc0 %s" % L("cs"),
-           "%s:" % L("cdone"),
-           "s_cmp_eq_u32 %s, 0" % sr(S_CS),
-           "s_cbranch_scc0 %s" % L("ss"),
-           "%s:" % L("sgo")]
+           "s_or_b32 %s, %s, %s" % (sr(S_X), sr(S_SPEC), sr(S_CS)),
+           "s_cbranch_scc0 %s" % L("sgo")]
+    out += copy_part(par) + score_mask_part(par)
+    out += ["%s:" % L("sgo")]
     out += score_phase(par, "s" + P)
-    out += ["%s:" % L("sdone"),
-            "s_cmp_eq_u32 %s, 0" % sr(S_SPEC),
-            "s_cbranch_scc0 %s" % L("ms"),
-            "%s:" % L("mdone"),
-            "s_cmp_eq_u32 %s, 0" % sr(S_CP),
-            "s_cbranch_scc0 %s" % L("ps"),
-            "%s:" % L("pgo")]
+    out += ["s_or_b32 %s, %s, %s" % (sr(S_X), sr(S_SPEC), sr(S_CP)),
+            "s_cbranch_scc0 %s" % L("pgo")]
+    out += middle_part(par) + pv_mask_part(par)
+    out += ["%s:" % L("pgo")]
     out += pv_phase(par, True, "p" + P)
     out += ["%s:" % L("pdone"),
             # end of the interval: this wave's loads have landed; everyone's have
@@ -601,72 +682,10 @@ def body(par):
 
 
 def slow_paths(par):
-    """Out-of-line parts of an iteration of parity par: masking of scores
-    before a phase, cache copies, Q reload, transition, and the pre-loop
-    iteration's PV phase."""
+    """Out-of-line part of an iteration of parity par: the pre-loop
+    iteration's PV phase (softmax of T[0]'s half 0, no products)."""
     L = lambda name: lbl(name, par)
-    P = "p%d" % par
-    r = roles(par)
-    g = sr(S_G)
-    KS, KP = sr(r["KS"]), sr(r["KP"])
-    # ---- score phase of a tile T[g] that is not wholly visible (or of no
-    # tile: the pre-loop iteration): its half-1 scores are masked first
-    out = ["%s:" % L("ss"),
-            "s_cmp_eq_u32 %s, 1" % KS,
-            "s_cbranch_scc1 %s" % L("ssd"),
-            "s_cmp_eq_u32 %s, 0" % KS,
-            "s_cbranch_scc1 %s" % L("sgo")]
-    out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("sgo"), "%s:" % L("ssd")]
-    out += mask_ops('d', 1, s_bank(par)) + ["s_branch %s" % L("sgo")]
-    # ---- cache copies of own rows: K(T[g+1]), V(T[g]), both in LDS since
-    # the previous barrier
-    out += ["%s:" % L("cs"),
-            "s_cmp_eq_u32 %[copy], 0",
-            "s_cbranch_scc1 %s" % L("nocv"),
-            "s_cmp_eq_u32 %s, 3" % KP,
-            "s_cbranch_scc1 %s" % L("nock"),
-            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T1"])),
-            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B1"])),
-            "s_cbranch_scc0 %s" % L("nock")] + cache_copy(par, 'k', P) + ["%s:" % L("nock")]
-    out += ["s_cmp_lt_i32 %s, 0" % g,
-            "s_cbranch_scc1 %s" % L("nocv"),
-            "s_lshr_b32 %s, %s, 1" % (sr(S_X), sr(r["T0"])),
-            "s_cmp_eq_u32 %s, %s" % (sr(S_X), sr(r["B0"])),
-            "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv"),
-            "s_branch %s" % L("cdone")]
-    # ---- middle part
-    out += ["%s:" % L("ms")]
-    # the heavy block's Q after the last light score tile
-    out += ["s_add_i32 %s, %s, 1" % (sr(S_X), g),
-            "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
-            "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
-    # at the last light tile the next tile's half-0 softmax starts the heavy
-    # block's state; the light block's is kept for its store
-    out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
-            "s_cbranch_scc0 %s" % L("notr"),
-            "v_mov_b32 %[m0n], %[m0v]",
-            "v_mov_b32 %[l0n], %[l0v]",
-            "v_mov_b32 %%[m0v], %s" % MINIT,
-            "v_mov_b32 %[l0v], 0",
-            "%s:" % L("notr"),
-            "s_branch %s" % L("mdone")]
-    # ---- PV phase when T[g+1] is not wholly visible (or missing): its
-    # half-0 scores are masked first (the score phase's MFMAs wrote them:
-    # wait them out); the pre-loop iteration (g < 0) has no PV products
-    out += ["%s:" % L("ps"),
-            "s_nop 7", "s_nop 7", "s_nop 7",
-            "s_cmp_eq_u32 %s, 1" % KP,
-            "s_cbranch_scc1 %s" % L("psd"),
-            "s_cmp_eq_u32 %s, 0" % KP,
-            "s_cbranch_scc1 %s" % L("psv")]
-    out += mask_ops('m', 0, V_SA) + ["s_branch %s" % L("psv"), "%s:" % L("psd")]
-    out += mask_ops('d', 0, V_SA)
-    out += ["%s:" % L("psv"),
-            "s_cmp_lt_i32 %s, 0" % g,
-            "s_cbranch_scc0 %s" % L("pgo")]
-    out += pv_phase(par, False, "q" + P)
-    out += ["s_branch %s" % L("pdone")]
-    return out
+    return ["%s:" % L("pre")] + pv_phase(par, False, "q" + "p%d" % par) + ["s_branch %s" % L("pdone")]
 
 
 LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt",
@@ -740,9 +759,14 @@ def loop_function():
 def helpers():
     """Access to the fixed registers from the kernel's C++ code."""
     out = []
+    # O = 0 by eight MFMAs with zero operands (C = 0): 8 issue slots
+    # instead of 128 accumulator writes; the MFMAs that accumulate into O
+    # next come long after these have finished
     lines = ["__device__ __forceinline__ void fwd64_o_zero() {", "  asm volatile("]
-    for r in range(A_O, A_O + 128):
-        lines.append('      "v_accvgpr_write_b32 %s, 0\\n"' % ar(r))
+    zl = ["s_nop 1"] + ["v_mov_b32 %s, 0" % vr(V_T + i) for i in range(4)] + ["s_nop 4"]
+    zl += ["%s %s, %s, %s, 0" % (MFMA, ar(A_O + 16 * i, 16), vr(V_T, 4), vr(V_T, 4)) for i in range(8)]
+    for x in zl:
+        lines.append('      "%s\\n"' % x)
     lines.append('      ::: "memory", ' + FIXED_CLOBBERS + ');')
     lines.append("}")
     out.append("\n".join(lines))
