@@ -85,6 +85,7 @@ struct Fwd64Loop {
   int32_t wsub;       // which 64 rows of the block the wave holds
   int32_t len;        // sequence length
   int32_t gt;         // lower group's last light position (-2: none)
+  int32_t wlom1, wwid; // window of the loop entry's common iterations: (wlom1, wlom1 + 1 + wwid]
   uint32_t tileb;     // bytes of 64 K / V rows
   uint32_t nrec;      // bytes from the sequence's first K / V row to the end of its last
   uint32_t m0b;       // LDS address of the wave's first load block in its group
@@ -352,9 +353,21 @@ void prefill_fwd64_kernel(FwdParams p) {
   };
   auto o_get = [](auto i_tag) __attribute__((always_inline)) { return fwd64_o_read<decltype(i_tag)::value>(); };
 
+  // Iterations h whose bookkeeping is the common case (see book_fast in
+  // gen_fwd64.py) for a run of positions [x0, x1) holding tiles x + off of
+  // block blk: h - 1 in the run, h + 2 before its end, T[h + 1] before the
+  // block's own tiles (which hold its diagonal).
+  auto set_window = [&](int x0, int x1, int off, int blk) {
+    const int lo = x0 + 1, hi = min(x1 - 3, 2 * blk - off - 2);
+    L.wlom1 = hi < lo ? INT32_MIN : lo - 1;
+    L.wwid = hi < lo ? 0 : hi - lo;
+  };
   int g = -1;
   for (;;) {
     L.gstart = g;
+    if (upper) set_window(0, n_my, 0, qb_hi);
+    else if (g < 0 && has_lo) set_window(0, e_lo, 0, z);
+    else set_window(g < 0 ? 0 : e_lo, n_my, L.jump, qb_hi);
     g = fwd64_loop(L, m0, l0, m1, l1, m0n, l0n);
     if (g >= n_up) break;
     // the lower group's light block is finished (its half-0 state was moved

@@ -398,7 +398,7 @@ def pv_phase(par, has_pv, tag):
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
     fill = softmax_ops(0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0")
-    fill = interleave(fill, book_next(par))
+    fill = interleave(fill, book_fast(par))
     if has_pv:
         vslot = V_OFF + par * K_SLOT_BYTES          # V(T[g]) in slot g % 2
         frag_reads = []
@@ -420,6 +420,7 @@ def pv_phase(par, has_pv, tag):
         for g in fill:
             body += g
     body += o_rescale(0, after_mfma=has_pv, tag=tag, olive=roles(par)["OP"])
+    body += book_check(tag)
     return body
 
 
@@ -494,6 +495,44 @@ def book_next(par):
         # variant codes: masks needed (and for the PV phase, its products)
         ["s_mov_b32 %s, %s" % (sr(S_CS), KS), "s_mov_b32 %s, %s" % (sr(S_CP), KP)],
     ]
+
+
+def book_fast(par):
+    """The common case of book_next: iteration h = g + 1 lies inside the
+    loop entry's window of iterations (%[wlom1] < h <= %[wlom1] + 1 +
+    %[wwid]) where T[h], T[h+1], T[h+2] are consecutive tiles of one run,
+    all below the wave's diagonal and the block's own tiles, and h + 1
+    does not start a run: then T[h+1] = T[h] + 1 in the same block, kind 0,
+    olive, the load descriptors move on by one tile, and no part of the
+    iteration is out of line.  Always run; book_check redoes the whole of
+    book_next when h is outside the window."""
+    r = roles(1 - par)
+    T0, T1, B0, B1 = sr(r["T0"]), sr(r["T1"]), sr(r["B0"]), sr(r["B1"])
+    KP, OP = sr(r["KP"]), sr(r["OP"])
+    out = [["s_add_i32 %s, %s, 1" % (T1, T0), "s_mov_b32 %s, %s" % (B1, B0)],
+           ["s_mov_b32 %s, 0" % KP, "s_mov_b32 %s, 1" % OP]]
+    for d in (S_VK, S_VV):
+        out.append(["s_add_u32 %s, %s, %%[tileb]" % (sr(d), sr(d)),
+                    "s_addc_u32 %s, %s, 0" % (sr(d + 1), sr(d + 1)),
+                    "s_sub_u32 %s, %s, %%[tileb]" % (sr(d + 2), sr(d + 2))])
+    out.append(["s_mov_b32 %s, 0" % sr(S_SPEC), "s_mov_b32 %s, 0" % sr(S_CS), "s_mov_b32 %s, 0" % sr(S_CP)])
+    return out
+
+
+def book_check(tag):
+    """After the PV phase: h = g + 1 outside the window takes the whole
+    book_next (out of line, book_slow)."""
+    return ["s_sub_u32 %s, %s, %%[wlom1]" % (sr(S_NX), sr(S_G)),
+            "s_cmp_gt_u32 %s, %%[wwid]" % sr(S_NX),
+            "s_cbranch_scc1 .Lbk%s_%%=" % tag,
+            ".Lbd%s_%%=:" % tag]
+
+
+def book_slow(par, tag):
+    out = [".Lbk%s_%%=:" % tag]
+    for grp in book_next(par):
+        out += grp
+    return out + ["s_branch .Lbd%s_%%=" % tag]
 
 
 def book_entry(par):
@@ -682,13 +721,16 @@ def body(par):
 
 
 def slow_paths(par):
-    """Out-of-line part of an iteration of parity par: the pre-loop
-    iteration's PV phase (softmax of T[0]'s half 0, no products)."""
+    """Out-of-line parts of an iteration of parity par: the pre-loop
+    iteration's PV phase (softmax of T[0]'s half 0, no products) and the
+    whole bookkeeping of the next iteration outside the common window."""
     L = lambda name: lbl(name, par)
-    return ["%s:" % L("pre")] + pv_phase(par, False, "q" + "p%d" % par) + ["s_branch %s" % L("pdone")]
+    P = "p%d" % par
+    out = ["%s:" % L("pre")] + pv_phase(par, False, "q" + P) + ["s_branch %s" % L("pdone")]
+    return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
-LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt",
+LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt", "wlom1", "wwid",
                 "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
 LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
                 "fk6", "fk7", "vd", "cl", "coe", "coo", "qo0", "qo1"]
