@@ -25,6 +25,7 @@ namespace dec {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kRescale = 8.0f;  // lazy rescale headroom, log2 units
 constexpr float kMInit = -1.0e30f;
@@ -81,8 +82,9 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, int4 
                                             unsigned long long* next, unsigned long long* taken) {
   constexpr int LPK = D / 8, KPI = 64 / LPK;
   // key steps whose loads are issued together (two such groups in flight):
-  // as many as the registers left beside GC heads' q and O allow
-  constexpr int kUnroll = W <= 4 ? 4 : GC <= 2 ? 8 : GC == 4 ? 4 : 2;
+  // as many as the registers left beside GC heads' q and O allow.  Every
+  // cached K/V row is read once: streaming (non-temporal) loads.
+  constexpr int kUnroll = W <= 4 ? 8 : GC <= 2 ? 8 : GC == 4 ? 4 : 2;
   float (*const rd)[GC][2 + D] = reinterpret_cast<float (*)[GC][2 + D]>(red);
   const int tid = __builtin_amdgcn_workitem_id_x();
   // wave-uniform in a scalar register: the key loop below is then a scalar loop
@@ -156,12 +158,12 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, int4 
         const int kq = min(sb + kslot, wc - 1);
         const int64_t base = (((int64_t)ids[u] * HK + hk) * kPageRows) * D;
         const uint32_t off = (uint32_t)(kq % kPageRows) * D + 8 * dch;
-        kr[u] = *(const uint4*)(p.kc + base + off);
-        vr[u] = *(const uint4*)(p.vc + base + off);
+        kr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(p.kc + base + off)));
+        vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(p.vc + base + off)));
       } else {
         const uint32_t off = (uint32_t)min(kb + u * KPI + kslot, wc - 1) * D + 8 * dch;
-        kr[u] = *(const uint4*)(kc + off);
-        vr[u] = *(const uint4*)(vc + off);
+        kr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(kc + off)));
+        vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)(vc + off)));
       }
     }
   };
