@@ -365,7 +365,9 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   p.bt_stride = max_blocks_per_seq;
   hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L,
                                          fused ? 4 : 1, fused ? 8 : 4, ws, stream);
-  if (e == hipSuccess) e = pa::launch_prefill_fwd_split(p, head_dim, paged, stream);
+  // with every row of length 1 the plan makes no attention items: only the
+  // decode launch has work
+  if (e == hipSuccess && (fused || max_seqlen > 1)) e = pa::launch_prefill_fwd_split(p, head_dim, paged, stream);
   if (e == hipSuccess && !fused) e = pa::launch_splitkv_decode(p, head_dim, paged, stream);
   if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
   if (e != hipSuccess) return hip_fail(e);

@@ -84,7 +84,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams& p, int64_t g, int4 
   // key steps whose loads are issued together (two such groups in flight):
   // as many as the registers left beside GC heads' q and O allow.  Every
   // cached K/V row is read once: streaming (non-temporal) loads.
-  constexpr int kUnroll = W <= 4 ? 8 : GC <= 2 ? 8 : GC == 4 ? 4 : 2;
+  constexpr int kUnroll = W <= 4 || GC <= 2 ? 8 : GC == 4 ? 4 : 2;
   float (*const rd)[GC][2 + D] = reinterpret_cast<float (*)[GC][2 + D]>(red);
   const int tid = __builtin_amdgcn_workitem_id_x();
   // wave-uniform in a scalar register: the key loop below is then a scalar loop
