@@ -322,6 +322,45 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (last > num_tokens) return PA_ERR_SEQLENS;
   }
   const bool paged = block_table != nullptr;
+  // One sequence with several rows (a prompt chunk over its cached prefix):
+  // its new K/V rows go to the cache first, then split-KV items on the
+  // 64-row kernel read every key from there, and the merge combines the
+  // segments.
+  if (!paged && num_seqs == 1 && max_seqlen > 1 &&
+      pa::fwd64_split_supported(head_dim, scale, max_seqlen, num_heads, cache_capacity)) {
+    char* ws = static_cast<char*>(workspace);
+    pa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.cu = cu_seqlens;
+    p.prefix = prefix_lens;
+    p.kc = k_cache;
+    p.vc = v_cache;
+    p.out = out;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.cap = cache_capacity;
+    p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634, 0x1p-100);
+    p.hdr = reinterpret_cast<const int32_t*>(ws + L.off_hdr);
+    p.items = reinterpret_cast<const int4*>(ws + L.off_items);
+    p.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
+    p.part_o = reinterpret_cast<float*>(ws + L.off_o);
+    p.seg_tiles = L.seg_tiles;
+    p.max_segs = L.max_segs;
+    int fwd_grid = 0, items_first = 0, merge_grid = 0;
+    st = split_grid(head_dim, false, &fwd_grid, &items_first, &merge_grid);
+    if (st != PA_OK) return st;
+    // items of about 2 x seg_tiles tiles: a 512-row chunk over an 8K-token
+    // prefix then fills the compute units with two units each
+    hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, 1, 2, ws,
+                                           stream, /*rows_as_items=*/true);
+    if (e == hipSuccess) e = pa::launch_cache_append(p, num_seqs, num_tokens, stream);
+    if (e == hipSuccess) e = pa::launch_prefill_fwd64_split(p, L.max_items, stream);
+    if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return PA_OK;
+  }
   const int gc = pa::splitkv_heads_per_unit(num_heads, num_kv_heads);
   // only a batch that may hold both multi-token blocks and length-1 rows
   // gains from running them together (one lone sequence, or rows of length

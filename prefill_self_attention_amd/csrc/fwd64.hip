@@ -57,6 +57,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kRowBytes = 2 * kD;
@@ -82,7 +83,7 @@ struct Fwd64Loop {
   int32_t elo;        // tiles of the first run (lower group: the light block)
   int32_t jump;       // tile index minus position in the second run
   int32_t blk0, blk1; // query block of the first / second run
-  int32_t wsub;       // which 64 rows of the block the wave holds
+  int32_t r0p, r0p1, r0p63;  // key position of the wave's first row less 128 x block (+1, +63)
   int32_t len;        // sequence length
   int32_t gt;         // lower group's last light position (-2: none)
   int32_t wlom1, wwid; // window of the loop entry's common iterations: (wlom1, wlom1 + 1 + wwid]
@@ -155,18 +156,74 @@ __device__ __forceinline__ void end_interval() {
   __builtin_amdgcn_s_barrier();
 }
 
+// kSplit = false: varlen (keys from k, v; block pairs).  kSplit = true:
+// split-KV items of a chunked call (keys from the cache, which already holds
+// the call's new rows; each group of two waves takes its own unit (item,
+// head) and writes a partial result when the item's block has several
+// segments).
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_fwd64_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   claim_registers();
-  // Work-group order.  Units (sequence, head) are spread over the 8 XCDs
-  // (the dispatcher places work-group i of a 1-D grid on XCD i % 8), and a
-  // unit's block pairs z follow one another in its XCD's dispatch stream, so
-  // the pairs that read the same head's K/V run at the same time and share
-  // that XCD's L2.  With H a multiple of 8, XCD x holds heads
-  // [x H/8, (x+1) H/8) of every sequence (grouped K/V heads stay together).
-  int h, b, z;
-  {
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int ql = lane & 31;
+  const int hl = lane >> 5;
+  const bool upper = wave < 2;
+  const int wsub = wave & 1;
+  const int group = upper ? 0 : 1;
+  const int64_t H = p.num_heads;
+  const int64_t HK = p.num_kv_heads;
+  int h, b, z, seq_start, len;
+  int qb_hi, e_lo, n_up, n_lo, n_my, pfx = 0, seg = 0, nseg = 1, seg_t0 = 0;
+  bool has_lo, transition;
+  if constexpr (kSplit) {
+    // units u = item * H + head; work-group w takes units 2 w (waves 0, 1)
+    // and 2 w + 1 (waves 2, 3): with H even, one item of two heads, which
+    // cover the same key tiles
+    const int64_t units = (int64_t)p.hdr[0] * H;
+    const int64_t u0 = 2 * (int64_t)__builtin_amdgcn_workgroup_id_x();
+    if (u0 >= units) return;  // every wave returns
+    const int64_t um = u0 + group, uo = u0 + 1 - group;
+    const bool mine_ok = um < units;
+    auto seg_tiles = [&](int64_t u, int& bb, int& qb, int& s, int& ns, int& t0) {
+      const int4 it = p.items[u / H];
+      bb = it.x;
+      qb = it.y;
+      s = it.z;
+      ns = it.w;
+      const int st = p.cu[bb], ln = p.cu[bb + 1] - st, pre = p.prefix[bb];
+      const int nt = (min(pre + min((qb + 1) * kBM, ln), p.cap) + kBN - 1) / kBN;  // within the capacity
+      t0 = s * nt / ns;
+      return (s + 1) * nt / ns - t0;
+    };
+    int bo, qbo, so, nso, t0o;
+    const int n_other = uo < units ? seg_tiles(uo, bo, qbo, so, nso, t0o) : 0;
+    // an idle group (no second unit) takes the first unit's addresses and no tiles
+    const int64_t ua = mine_ok ? um : uo;
+    int qb;
+    n_my = seg_tiles(ua, b, qb, seg, nseg, seg_t0);
+    if (!mine_ok) n_my = 0;
+    h = (int)(ua % H);
+    seq_start = p.cu[b];
+    len = p.cu[b + 1] - seq_start;
+    pfx = p.prefix[b];
+    z = qb;
+    qb_hi = qb;
+    has_lo = false;
+    e_lo = 0;
+    n_up = max(n_my, n_other);  // iterations of the work-group
+    n_lo = 0;
+    transition = false;
+  } else {
+    // Work-group order.  Units (sequence, head) are spread over the 8 XCDs
+    // (the dispatcher places work-group i of a 1-D grid on XCD i % 8), and a
+    // unit's block pairs z follow one another in its XCD's dispatch stream,
+    // so the pairs that read the same head's K/V run at the same time and
+    // share that XCD's L2.  With H a multiple of 8, XCD x holds heads
+    // [x H/8, (x+1) H/8) of every sequence (grouped K/V heads stay together).
     const int wg = __builtin_amdgcn_workgroup_id_x();
     const int xcd = wg & 7, s = wg >> 3;
     const int u = s / p.grid_z;
@@ -181,39 +238,32 @@ void prefill_fwd64_kernel(FwdParams p) {
       h = unit - b * p.num_heads;
     }
     if (b >= p.num_seqs) return;  // padding of the last units (every wave returns)
+    seq_start = p.cu[b];
+    len = p.cu[b + 1] - seq_start;
+    const int nqb = (len + kBM - 1) / kBM;
+    qb_hi = nqb - 1 - z;
+    if (z > qb_hi) return;  // no block pair left for this work-group (every wave returns)
+    has_lo = z < qb_hi;
+    auto ntiles_of = [=](int qb) { return (min((qb + 1) * kBM, len) + kBN - 1) / kBN; };
+    e_lo = has_lo ? ntiles_of(z) : 0;
+    const int e_hi = ntiles_of(qb_hi);
+    n_up = (e_lo + e_hi + 1) / 2;
+    n_lo = e_lo + e_hi - n_up;
+    // the group's tile sequence: upper: heavy block tiles 0 .. n_up-1; lower:
+    // light block tiles 0 .. e_lo-1, then heavy block tiles n_up .. e_hi-1
+    n_my = upper ? n_up : n_lo;
+    transition = !upper && has_lo && n_lo > e_lo;
   }
-  const int64_t H = p.num_heads;
-  const int64_t HK = p.num_kv_heads;
-  const int seq_start = p.cu[b];
-  const int len = p.cu[b + 1] - seq_start;
-  const int nqb = (len + kBM - 1) / kBM;
-  const int qb_hi = nqb - 1 - z;
-  if (z > qb_hi) return;  // no block pair left for this work-group (every wave returns)
-  const bool has_lo = z < qb_hi;
-  auto ntiles_of = [=](int qb) { return (min((qb + 1) * kBM, len) + kBN - 1) / kBN; };
-  const int e_lo = has_lo ? ntiles_of(z) : 0;
-  const int e_hi = ntiles_of(qb_hi);
-  const int n_up = (e_lo + e_hi + 1) / 2;
-  const int n_lo = e_lo + e_hi - n_up;
-
-  const int tid = __builtin_amdgcn_workitem_id_x();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int lane = tid & 63;
-  const int ql = lane & 31;
-  const int hl = lane >> 5;
-  const bool upper = wave < 2;
-  const int wsub = wave & 1;
-  const int group = upper ? 0 : 1;
-  // the group's tile sequence: upper: heavy block tiles 0 .. n_up-1; lower:
-  // light block tiles 0 .. e_lo-1, then heavy block tiles n_up .. e_hi-1
-  const int n_my = upper ? n_up : n_lo;
-  const bool transition = !upper && has_lo && n_lo > e_lo;
 
   const int hk = h / (int)(H / HK);
-  const bool writes_cache = h == hk * (int)(H / HK);
-  const int64_t row_stride = HK * kD;  // elements between consecutive tokens of k, v
-  const uint16_t* kin = p.k + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
-  const uint16_t* vin = p.v + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
+  const bool writes_cache = !kSplit && h == hk * (int)(H / HK);
+  // elements between consecutive keys: tokens of k, v (varlen) or rows of
+  // the cache (split: [B, HK, cap, D])
+  const int64_t row_stride = kSplit ? (int64_t)kD : HK * kD;
+  const uint16_t* kin = kSplit ? p.kc + ((int64_t)b * HK + hk) * p.cap * kD
+                               : p.k + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
+  const uint16_t* vin = kSplit ? p.vc + ((int64_t)b * HK + hk) * p.cap * kD
+                               : p.v + (int64_t)seq_start * row_stride + (int64_t)hk * kD;
   const int64_t cache_base = (int64_t)seq_start * HK * kD + (int64_t)hk * len * kD;
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t gbase = lds0 + group * kGroupBytes;
@@ -224,23 +274,26 @@ void prefill_fwd64_kernel(FwdParams p) {
   L.c = p.scale_log2;
   L.nit = n_up;
   L.nmy = n_my;
-  L.elo = upper ? n_my : e_lo;
-  L.jump = upper ? 0 : n_up - e_lo;
+  L.elo = kSplit ? 0 : upper ? n_my : e_lo;
+  L.jump = kSplit ? seg_t0 : upper ? 0 : n_up - e_lo;
   L.blk0 = (upper || !has_lo) ? qb_hi : z;
   L.blk1 = qb_hi;
-  L.wsub = wsub;
+  L.r0p = pfx + 64 * wsub;
+  L.r0p1 = L.r0p + 1;
+  L.r0p63 = L.r0p + 63;
   L.len = len;
   L.gt = transition ? e_lo - 1 : -2;
   L.tileb = (uint32_t)kBN * rs;
-  L.nrec = (uint32_t)(len - 1) * rs + kRowBytes;
+  // keys [0, prefix + len), within the cache row's capacity (split)
+  L.nrec = (uint32_t)((kSplit ? min(pfx + len, p.cap) : len) - 1) * rs + kRowBytes;
   L.m0b = gbase + 1024u * wsub;
   L.kbl = (uint32_t)(uintptr_t)kin;
   L.kbh = (uint32_t)((uintptr_t)kin >> 32);
   L.vbl = (uint32_t)(uintptr_t)vin;
   L.vbh = (uint32_t)((uintptr_t)vin >> 32);
   L.copy = writes_cache ? 1u : 0u;
-  uint16_t* kc = p.kc + cache_base;
-  uint16_t* vc = p.vc + cache_base;
+  uint16_t* kc = kSplit ? p.kc : p.kc + cache_base;  // the copy (varlen only) writes these
+  uint16_t* vc = kSplit ? p.vc : p.vc + cache_base;
   L.kcl = (uint32_t)(uintptr_t)kc;
   L.kch = (uint32_t)((uintptr_t)kc >> 32);
   L.vcl = (uint32_t)(uintptr_t)vc;
@@ -296,7 +349,7 @@ void prefill_fwd64_kernel(FwdParams p) {
   }
   fwd64_o_zero();
   if (n_my > 0) {
-    const int t0 = upper || e_lo > 0 ? 0 : n_up;
+    const int t0 = kSplit ? seg_t0 : upper || e_lo > 0 ? 0 : n_up;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kin + (int64_t)t0 * kBN * row_stride), (short)0, (int)(L.nrec - (uint32_t)t0 * L.tileb), 0x00020000);
 #pragma unroll
@@ -355,17 +408,21 @@ void prefill_fwd64_kernel(FwdParams p) {
 
   // Iterations h whose bookkeeping is the common case (see book_fast in
   // gen_fwd64.py) for a run of positions [x0, x1) holding tiles x + off of
-  // block blk: h - 1 in the run, h + 2 before its end, T[h + 1] before the
-  // block's own tiles (which hold its diagonal).
+  // block blk: h - 1 in the run, h + 2 before its end, T[h + 1] wholly
+  // visible to the wave (below (R0 + 1) / 64, see kind_of) and, when the
+  // wave copies to the cache, before the block's own tiles.
   auto set_window = [&](int x0, int x1, int off, int blk) {
-    const int lo = x0 + 1, hi = min(x1 - 3, 2 * blk - off - 2);
+    int hi = min(x1 - 3, ((kBM * blk + L.r0p1) >> 6) - off - 2);
+    if (L.copy) hi = min(hi, 2 * blk - off - 2);
+    const int lo = x0 + 1;
     L.wlom1 = hi < lo ? INT32_MIN : lo - 1;
     L.wwid = hi < lo ? 0 : hi - lo;
   };
   int g = -1;
   for (;;) {
     L.gstart = g;
-    if (upper) set_window(0, n_my, 0, qb_hi);
+    if (kSplit) set_window(0, n_my, seg_t0, qb_hi);
+    else if (upper) set_window(0, n_my, 0, qb_hi);
     else if (g < 0 && has_lo) set_window(0, e_lo, 0, z);
     else set_window(g < 0 ? 0 : e_lo, n_my, L.jump, qb_hi);
     g = fwd64_loop(L, m0, l0, m1, l1, m0n, l0n);
@@ -378,6 +435,43 @@ void prefill_fwd64_kernel(FwdParams p) {
     fwd64_o_zero();
     m1 = kMInit;
     l1 = 0.f;
+  }
+
+  if constexpr (kSplit) {
+    mfma_drain();
+    if (n_my == 0) return;
+    if (nseg == 1) {
+      store_rows(qb_hi, l0, l1, o_get);
+      return;
+    }
+    // the rows' partial result over this segment's keys: O / l in fp32 and
+    // m + log2(l) (log2 of the sum of 2^(s c) over those keys; -inf when a
+    // row sees none of them), at slot (token, head, segment)
+    static_for<0, 2>([&](auto qh_tag) __attribute__((always_inline)) {
+      constexpr int qh = decltype(qh_tag)::value;
+      const float lp = qh == 0 ? l0 : l1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp), false, false);
+      const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const bool any = l > 0.f;
+      const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
+      const int row = qb_hi * kBM + 64 * wsub + 32 * qh + ql;
+      const int64_t slot = ((int64_t)(seq_start + row) * H + h) * p.max_segs + seg;
+      float* dst = p.part_o + slot * kD + 4 * hl;
+      static_for<0, 4>([&](auto db_tag) __attribute__((always_inline)) {
+        constexpr int db = decltype(db_tag)::value;
+        const f32x16_t o = fwd64_o_read<4 * qh + db>();
+        if (row < len) {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const f32x4_t w = {o[4 * cc] * inv, o[4 * cc + 1] * inv, o[4 * cc + 2] * inv, o[4 * cc + 3] * inv};
+            *reinterpret_cast<f32x4_t*>(dst + 32 * db + 8 * cc) = w;
+          }
+        }
+      });
+      if (row < len && hl == 0)
+        p.part_lse[slot] = any ? (qh == 0 ? m0 : m1) + __builtin_amdgcn_logf(l) : -__builtin_huge_valf();
+    });
+    return;
   }
 
   // ---------------------------------------------------------------- merge
@@ -394,7 +488,6 @@ void prefill_fwd64_kernel(FwdParams p) {
   // finish half of the columns: the upper wave columns 0-63, the lower
   // 64-127.  Each passes its running maxima, row sums and the O blocks of
   // the other half through LDS (region of 4 + 64 floats per lane).
-  typedef float f32x4_t __attribute__((ext_vector_type(4)));
   constexpr int kRegion = 17 * 64;  // float4 per lane: (m0, l0, m1, l1), then 16 of O
   f32x4_t* mine = reinterpret_cast<f32x4_t*>(lds) + (2 * wsub + (upper ? 0 : 1)) * kRegion;
   const f32x4_t* theirs = reinterpret_cast<const f32x4_t*>(lds) + (2 * wsub + (upper ? 1 : 0)) * kRegion;
@@ -451,7 +544,66 @@ hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t st
   const int64_t per_xcd = ((int64_t)p.num_heads * num_seqs + 7) / 8;
   const int64_t grid = 8 * per_xcd * p.grid_z;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_fwd64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL(prefill_fwd64_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  return hipGetLastError();
+}
+
+bool fwd64_split_supported(int head_dim, float scale, int max_seqlen, int num_heads, int cap) {
+  // 32-bit offsets: rows of q and out (up to 127 past the last one), rows of
+  // one (sequence, K/V head) of the cache
+  const int64_t q_row = (int64_t)2 * kD * num_heads;
+  return head_dim == 128 && scale >= 0.f && ((int64_t)max_seqlen + kBM) * q_row < ((int64_t)1 << 31) &&
+         (int64_t)cap * kRowBytes < ((int64_t)1 << 31);
+}
+
+hipError_t launch_prefill_fwd64_split(const FwdParams& p, int64_t max_items, hipStream_t stream) {
+  const int64_t grid = (max_items * p.num_heads + 1) / 2;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_fwd64_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+namespace {
+// Every new token's K and V row into the cache slab [B, HK, cap, D] at
+// position prefix + i, 16 bytes a thread (K then V); tokens past
+// cu[num_seqs] are left alone.
+__global__ __launch_bounds__(256) void cache_append_kernel(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ prefix, int num_seqs,
+                                                           int num_kv_heads, int cap, int64_t rows,
+                                                           uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+  const int64_t i = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
+  const int64_t chunks = rows * 16;  // 16-byte chunks of one matrix
+  if (i >= 2 * chunks) return;
+  const bool is_v = i >= chunks;
+  const int64_t j = is_v ? i - chunks : i;
+  const int64_t row = j >> 4;        // token * HK + hk
+  const int c = (int)(j & 15);
+  const int hk = (int)(row % num_kv_heads);
+  const int tok = (int)(row / num_kv_heads);
+  if (tok >= cu[num_seqs]) return;
+  int lo = 0, hi = num_seqs - 1;      // sequence b: cu[b] <= tok < cu[b + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int pos = prefix[lo] + tok - cu[lo];
+  if (pos < 0 || pos >= cap) return;  // metadata past the capacity (refused in check mode)
+  const uint4 w = *reinterpret_cast<const uint4*>((is_v ? v : k) + row * kD + 8 * c);
+  uint16_t* dst = (is_v ? vc : kc) + (((int64_t)lo * num_kv_heads + hk) * cap + pos) * kD + 8 * c;
+  *reinterpret_cast<uint4*>(dst) = w;
+}
+}  // namespace
+
+hipError_t launch_cache_append(const FwdParams& p, int num_seqs, int64_t num_tokens, hipStream_t stream) {
+  const int64_t rows = num_tokens * p.num_kv_heads;
+  const int64_t blocks = (2 * rows * 16 + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(cache_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.k, p.v, p.cu, p.prefix,
+                     num_seqs, p.num_kv_heads, p.cap, rows, p.kc, p.vc);
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ T_THR = V_T + 2                     # m + 8
 T_MNEW = V_T + 3
 T_ALPHA = V_T + 4                   # rescale factor (kept to the end of the phase)
 T_NINF = V_T + 5                    # -inf
+T_VDD = V_T + 6                     # vd + R0 - 64 t (general diagonal mask)
 T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
 
 # scalar registers of the loop.  Pairs alternate with the iteration's
@@ -193,11 +194,21 @@ def softmax_ops(qh, sbase, pbase, m, l, tag):
 def mask_ops(kind, qh, sbase):
     """Scores of one query half over one tile that the causal mask hides, set
     to -inf before the phase's softmax (which then gives them weight 0 and
-    leaves the running max alone): 'd' the wave's diagonal tile (key k >
-    row q hidden, both relative to the tile / the half's first row; for half
-    0 key block 1 lies wholly above the diagonal), 'm' every key.  Register
-    layout as in softmax_ops."""
+    leaves the running max alone): 'd' a partly hidden tile that starts at
+    the wave's first row (key k > row q hidden, both relative to the tile /
+    the half's first row; for half 0 key block 1 lies wholly above the
+    diagonal), 'g' a partly hidden tile at any offset (v[T_VDD] = vd + R0 -
+    64 t, see kind_of), 'm' every key.  Register layout as in softmax_ops."""
     out = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF)]
+    if kind == 'g':
+        # any offset: key k hidden from row q when k - q > R0 - 64 t, i.e.
+        # 32 (kb - qh) + 8 (r / 4) + r % 4 > vd + R0 - 64 t (v[T_VDD])
+        for i in range(32):
+            kb, r = i // 16, i % 16
+            o = 32 * (kb - qh) + 8 * (r // 4) + r % 4
+            out += ["v_cmp_gt_i32 vcc, %d, %s" % (o, vr(T_VDD)),
+                    "v_cndmask_b32 %s, %s, %s, vcc" % (vr(sbase + i), vr(sbase + i), vr(T_NINF))]
+        return out
     if kind == 'm':
         return out + ["v_mov_b32 %s, %s" % (vr(sbase + i), vr(T_NINF)) for i in range(32)]
     diag = range(16) if qh == 0 else range(16, 32)
@@ -434,12 +445,20 @@ def tile_of(x, t, b, tmp=S_Y):
 
 
 def kind_of(t, b, dst, tmp=S_Y):
-    """dst = 0 if tile t is below the wave's diagonal tile of block b, 1 on
-    it, 2 above it (diagonal tile 2 b + wsub)."""
-    return ["s_lshl_b32 %s, %s, 1" % (sr(tmp), sr(b)),
-            "s_add_i32 %s, %s, %%[wsub]" % (sr(tmp), sr(tmp)),
+    """dst = 0 if every row of the wave in block b sees every key of tile t,
+    2 if none sees any, 1 otherwise.  The wave's first row sits at key
+    position R0 = 128 b + %[r0p] (r0p: the keys before the sequence's first
+    query, plus 64 wsub), so tiles below (R0 + 1) / 64 are wholly visible
+    and tiles above (R0 + 63) / 64 wholly hidden (one tile in between when
+    R0 is a multiple of 64, two otherwise)."""
+    return ["s_lshl_b32 %s, %s, 7" % (sr(tmp), sr(b)),
+            "s_add_i32 %s, %s, %%[r0p1]" % (sr(tmp), sr(tmp)),
+            "s_lshr_b32 %s, %s, 6" % (sr(tmp), sr(tmp)),
             "s_cmp_lt_i32 %s, %s" % (sr(t), sr(tmp)),
             "s_cselect_b32 %s, 0, 1" % sr(dst),
+            "s_lshl_b32 %s, %s, 7" % (sr(tmp), sr(b)),
+            "s_add_i32 %s, %s, %%[r0p63]" % (sr(tmp), sr(tmp)),
+            "s_lshr_b32 %s, %s, 6" % (sr(tmp), sr(tmp)),
             "s_cmp_gt_i32 %s, %s" % (sr(t), sr(tmp)),
             "s_cselect_b32 %s, 2, %s" % (sr(dst), sr(dst))]
 
@@ -626,6 +645,22 @@ def copy_part(par):
             "s_cbranch_scc0 %s" % L("nocv")] + cache_copy(par, 'v', P) + ["%s:" % L("nocv")])
 
 
+def diag_mask(qh, sbase, t, b, tag):
+    """Masks of a partly hidden tile t of block b for query half qh: the
+    'd' form when the tile starts at the wave's first row (R0 = 64 t), else
+    the general one."""
+    return ["s_lshl_b32 %s, %s, 7" % (sr(S_X), sr(b)),
+            "s_add_i32 %s, %s, %%[r0p]" % (sr(S_X), sr(S_X)),
+            "s_lshl_b32 %s, %s, 6" % (sr(S_Y), sr(t)),
+            "s_sub_i32 %s, %s, %s" % (sr(S_X), sr(S_X), sr(S_Y)),
+            "s_cmp_eq_u32 %s, 0" % sr(S_X),
+            "s_cbranch_scc0 .Lmg%s_%%=" % tag] + mask_ops('d', qh, sbase) + [
+            "s_branch .Lmd%s_%%=" % tag,
+            ".Lmg%s_%%=:" % tag,
+            "v_add_u32 %s, %s, %%[vd]" % (vr(T_VDD), sr(S_X))] + mask_ops('g', qh, sbase) + [
+            ".Lmd%s_%%=:" % tag]
+
+
 def score_mask_part(par):
     """Score phase of a tile T[g] that is not wholly visible (or of no tile:
     the pre-loop iteration): its half-1 scores are masked first."""
@@ -637,8 +672,9 @@ def score_mask_part(par):
            "s_cbranch_scc1 %s" % L("ssd"),
            "s_cmp_eq_u32 %s, 0" % KS,
            "s_cbranch_scc1 %s" % L("sgo")]
+    r = roles(par)
     out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("sgo"), "%s:" % L("ssd")]
-    out += mask_ops('d', 1, s_bank(par))
+    out += diag_mask(1, s_bank(par), r["T0"], r["B0"], "s%d" % par)
     return out
 
 
@@ -678,8 +714,9 @@ def pv_mask_part(par):
            "s_cbranch_scc1 %s" % L("psd"),
            "s_cmp_eq_u32 %s, 0" % KP,
            "s_cbranch_scc1 %s" % L("psv")]
+    r = roles(par)
     out += mask_ops('m', 0, V_SA) + ["s_branch %s" % L("psv"), "%s:" % L("psd")]
-    out += mask_ops('d', 0, V_SA)
+    out += diag_mask(0, V_SA, r["T1"], r["B1"], "p%d" % par)
     out += ["%s:" % L("psv"),
             "s_cmp_lt_i32 %s, 0" % sr(S_G),
             "s_cbranch_scc1 %s" % L("pre")]
@@ -730,7 +767,7 @@ def slow_paths(par):
     return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
-LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "wsub", "len", "gt", "wlom1", "wwid",
+LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "r0p", "r0p1", "r0p63", "len", "gt", "wlom1", "wwid",
                 "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
 LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
                 "fk6", "fk7", "vd", "cl", "coe", "coo", "qo0", "qo1"]

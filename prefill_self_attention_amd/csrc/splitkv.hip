@@ -83,17 +83,19 @@ __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int s
 }
 
 // Segments of every query block of one sequence (work items; a length-1
-// sequence's go to the decode list), and the merge entries of the blocks with
+// sequence's go to the decode list when dec_rows is set), and the merge entries of the blocks with
 // more than one segment.  Segment counts are capped at max_segs, so malformed
 // metadata cannot address outside the workspace.
-__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult, int item_mult) {
+__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult, int item_mult,
+                            bool dec_rows) {
   SeqPlan r{0, 0, 0};
+  const bool row = dec_rows && len == 1;
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-    const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
+    const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
     if (ns < 1) continue;
-    if (len == 1)
+    if (row)
       r.dec += ns;
     else
       r.items += ns;
@@ -108,7 +110,7 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int 
 __global__ __launch_bounds__(kPlanThreads)
 void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
                          int num_seqs, int num_tokens, int seg_tiles, int max_segs, int dec_mult, int item_mult,
-                         int64_t max_items, int64_t max_dec, int64_t max_merges,
+                         int dec_rows, int64_t max_items, int64_t max_dec, int64_t max_merges,
                          int32_t* __restrict__ hdr, int4* __restrict__ items,
                          int4* __restrict__ dec, int4* __restrict__ merges,
                          unsigned long long* __restrict__ counters) {
@@ -127,7 +129,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       pre = prefix[b];
       // tokens outside [0, num_tokens) would index outside the partial buffers
       len = (start >= 0 && end <= num_tokens && end > start) ? end - start : 0;
-      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult, item_mult);
+      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult, item_mult, dec_rows != 0);
     }
     const int si = wave_incl_scan(c.items, lane);
     const int sd = wave_incl_scan(c.dec, lane);
@@ -156,16 +158,17 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       // item i of head h run as step i * H + h of a grid that is a multiple of
       // H and of the 8 XCDs, the blocks reading one segment's K/V tiles then
       // run at the same time on one XCD and share its L2
+      const bool row = dec_rows && len == 1;
       const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
       const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
-      const int ns_max = block_segments(ntiles_last, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
+      const int ns_max = block_segments(ntiles_last, row, seg_tiles, max_segs, dec_mult, item_mult);
       for (int s = 0; s < ns_max; ++s)
         for (int qb = 0; qb < nqb; ++qb) {
           const int qend = min(qb * kQueryBlock + kQueryBlock, len);
           const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-          const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
+          const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
           if (s >= ns) continue;
-          if (len == 1) {
+          if (row) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
             ++off_d;
           } else {
@@ -177,7 +180,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = block_segments(ntiles, len == 1, seg_tiles, max_segs, dec_mult, item_mult);
+        const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
@@ -284,11 +287,12 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
                                int32_t num_tokens, const SplitLayout& L, int dec_seg_mult,
-                               int item_seg_mult, void* ws, hipStream_t stream) {
+                               int item_seg_mult, void* ws, hipStream_t stream, bool rows_as_items) {
   char* base = static_cast<char*>(ws);
   const int64_t max_merges = (int64_t)(L.off_lse - L.off_merges) / 16;
   hipLaunchKernelGGL(splitkv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, prefix,
-                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, item_seg_mult, L.max_items, L.max_dec_items,
+                     num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, item_seg_mult,
+                     rows_as_items ? 0 : 1, L.max_items, L.max_dec_items,
                      max_merges, reinterpret_cast<int32_t*>(base + L.off_hdr),
                      reinterpret_cast<int4*>(base + L.off_items),
                      reinterpret_cast<int4*>(base + L.off_dec),
