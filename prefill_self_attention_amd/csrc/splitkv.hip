@@ -28,7 +28,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kMinSegTiles = 16;  // 1024 keys per segment at least
 constexpr int kMaxSegs = 64;      // segments per block at most (bounds the workspace)
 constexpr int kMergeRows = 16;    // rows per merge entry (4 waves x 4 rows)
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;  // one wave per SIMD: registers for the 64-bit offsets without spilling
+static_assert(kSplitCounters <= kPlanThreads, "the plan zeroes one counter per thread");
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -104,7 +105,7 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int 
   return r;
 }
 
-// One work-group.  Sequences are taken 1024 at a time; each thread counts its
+// One work-group.  Sequences are taken 256 at a time; each thread counts its
 // sequence's items and merge entries, a work-group scan gives the offsets, and
 // the thread writes them.  hdr[0], hdr[1] receive the totals.
 __global__ __launch_bounds__(kPlanThreads)
