@@ -276,8 +276,9 @@ def gcost(g):
 
 
 def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
-    """Interleave: before the MFMA pair of fragment f wait for its reads and
-    issue fragment f+LOOKAHEAD's; load pair i = (before, after) goes around
+    """Interleave: before every fourth MFMA (fragments f, f + 1) wait for
+    their reads and issue the reads of fragments up to f + 3; load pair i =
+    (before, after) goes around
     MFMA i; the filler
     groups (softmax) fill each MFMA slot up to SLOT_BUDGET issue cycles, in
     order (raised when the rest would not fit; what is left follows the last
@@ -292,11 +293,15 @@ def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
     fi = 0
     for s, (mf, f) in enumerate(mfmas):
         used = 0
-        if s % 2 == 0:
-            pending = (issued - 1 - f) * reads_per_frag
+        if s % 4 == 0:
+            # one wait for the fragments of the next four MFMAs (f, f + 1),
+            # then the reads of fragments up to f + 3 (their slots' previous
+            # fragments, f - 2 and f - 1, have had their MFMAs issued)
+            last = min(f + 1, nfrag - 1)
+            pending = max(issued - 1 - last, 0) * reads_per_frag
             out.append("s_waitcnt lgkmcnt(%d)" % pending)
             used += 1
-            if issued < nfrag:
+            while issued < nfrag and issued <= f + 3:
                 out += frag_reads[issued]
                 used += gcost(frag_reads[issued])
                 issued += 1
