@@ -351,11 +351,18 @@ pa_status splitkv_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     int fwd_grid = 0, items_first = 0, merge_grid = 0;
     st = split_grid(head_dim, false, &fwd_grid, &items_first, &merge_grid);
     if (st != PA_OK) return st;
-    // items of about 2 x seg_tiles tiles: a 512-row chunk over an 8K-token
-    // prefix then fills the compute units with two units each
+    // items sized so that the units (item, head) number about two per
+    // compute unit (a work-group runs two); the plan launch also appends the
+    // new K/V rows to the cache
+    int cus = 0;
+    {
+      int dev = 0;
+      hipError_t e0 = hipGetDevice(&dev);
+      if (e0 == hipSuccess) cus = g_cus[dev].load(std::memory_order_relaxed);  // set by split_grid
+    }
+    const int fill = std::max(1, 2 * std::max(cus, 1) / num_heads);
     hipError_t e = pa::launch_splitkv_plan(cu_seqlens, prefix_lens, num_seqs, num_tokens, L, 1, 2, ws,
-                                           stream, /*rows_as_items=*/true);
-    if (e == hipSuccess) e = pa::launch_cache_append(p, num_seqs, num_tokens, stream);
+                                           stream, /*rows_as_items=*/true, &p, head_dim, fill);
     if (e == hipSuccess) e = pa::launch_prefill_fwd64_split(p, L.max_items, stream);
     if (e == hipSuccess) e = pa::launch_splitkv_merge(p, L, ws, head_dim, merge_grid, stream);
     if (e != hipSuccess) return hip_fail(e);

@@ -564,47 +564,5 @@ hipError_t launch_prefill_fwd64_split(const FwdParams& p, int64_t max_items, hip
   return hipGetLastError();
 }
 
-namespace {
-// Every new token's K and V row into the cache slab [B, HK, cap, D] at
-// position prefix + i, 16 bytes a thread (K then V); tokens past
-// cu[num_seqs] are left alone.
-__global__ __launch_bounds__(256) void cache_append_kernel(const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v,
-                                                           const int32_t* __restrict__ cu,
-                                                           const int32_t* __restrict__ prefix, int num_seqs,
-                                                           int num_kv_heads, int cap, int64_t rows,
-                                                           uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
-  const int64_t i = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
-  const int64_t chunks = rows * 16;  // 16-byte chunks of one matrix
-  if (i >= 2 * chunks) return;
-  const bool is_v = i >= chunks;
-  const int64_t j = is_v ? i - chunks : i;
-  const int64_t row = j >> 4;        // token * HK + hk
-  const int c = (int)(j & 15);
-  const int hk = (int)(row % num_kv_heads);
-  const int tok = (int)(row / num_kv_heads);
-  if (tok >= cu[num_seqs]) return;
-  int lo = 0, hi = num_seqs - 1;      // sequence b: cu[b] <= tok < cu[b + 1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= tok) lo = mid; else hi = mid - 1;
-  }
-  const int pos = prefix[lo] + tok - cu[lo];
-  if (pos < 0 || pos >= cap) return;  // metadata past the capacity (refused in check mode)
-  const uint4 w = *reinterpret_cast<const uint4*>((is_v ? v : k) + row * kD + 8 * c);
-  uint16_t* dst = (is_v ? vc : kc) + (((int64_t)lo * num_kv_heads + hk) * cap + pos) * kD + 8 * c;
-  *reinterpret_cast<uint4*>(dst) = w;
-}
-}  // namespace
-
-hipError_t launch_cache_append(const FwdParams& p, int num_seqs, int64_t num_tokens, hipStream_t stream) {
-  const int64_t rows = num_tokens * p.num_kv_heads;
-  const int64_t blocks = (2 * rows * 16 + 255) / 256;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(cache_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.k, p.v, p.cu, p.prefix,
-                     num_seqs, p.num_kv_heads, p.cap, rows, p.kc, p.vc);
-  return hipGetLastError();
-}
 
 }  // namespace pa

@@ -67,13 +67,12 @@ hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bo
 bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, int num_heads, int num_kv_heads);
 hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream);
 // Split-KV items of a chunked call on the 64-row kernel: keys (prefix and
-// new) from the cache slab, which launch_cache_append has filled with the
-// call's new rows first; partial results to part_o / part_lse when an item's
+// new) from the cache slab, which the plan launch has filled with the call's
+// new rows first (launch_splitkv_plan with append); partial results to part_o / part_lse when an item's
 // block has several segments, else the output.  max_items bounds the plan's
 // item count (p.hdr[0]).
 bool fwd64_split_supported(int head_dim, float scale, int max_seqlen, int num_heads, int cap);
 hipError_t launch_prefill_fwd64_split(const FwdParams& p, int64_t max_items, hipStream_t stream);
-hipError_t launch_cache_append(const FwdParams& p, int num_seqs, int64_t num_tokens, hipStream_t stream);
 // Varlen with an INT8 or an FP8 (E4M3) cache (kq, vq, ks, vs instead of kc, vc).
 hipError_t launch_prefill_fwd_fp8(const FwdParams& p, int num_seqs, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_fwd_int8(const FwdParams& p, int num_seqs, int head_dim,
@@ -103,7 +102,8 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
                                int32_t num_tokens, const SplitLayout& L, int dec_seg_mult,
                                int item_seg_mult, void* ws, hipStream_t stream,
-                               bool rows_as_items = false);
+                               bool rows_as_items = false, const FwdParams* append = nullptr,
+                               int head_dim = 0, int fill_per_head = 0);
 hipError_t launch_prefill_fwd_split(const FwdParams& p, int head_dim, bool paged, hipStream_t stream);
 hipError_t launch_splitkv_merge(const FwdParams& p, const SplitLayout& L, const void* ws,
                                 int head_dim, int grid, hipStream_t stream);

@@ -75,11 +75,13 @@ struct SeqPlan {
 // launch, long segments of both kinds measured faster (dec_mult 4: its one
 // work-group per compute unit pays a fixed cost per unit; item_mult 8: the
 // decode units keep the compute units busy while fewer, longer items run, and
-// most blocks then need no merge).  At most max_segs.  Segment s covers
+// most blocks then need no merge).  item_tiles = item_mult * seg_tiles, or
+// the fill target of the plan (see splitkv_plan_kernel).  At most max_segs.
+// Segment s covers
 // tiles [s * ntiles / ns, (s + 1) * ntiles / ns).
 __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int seg_tiles, int max_segs,
-                                              int dec_mult, int item_mult) {
-  const int target = (decode_row ? dec_mult : item_mult) * seg_tiles;
+                                              int dec_mult, int item_tiles) {
+  const int target = decode_row ? dec_mult * seg_tiles : item_tiles;
   return min((ntiles + target - 1) / target, max_segs);
 }
 
@@ -87,14 +89,14 @@ __device__ __forceinline__ int block_segments(int ntiles, bool decode_row, int s
 // sequence's go to the decode list when dec_rows is set), and the merge entries of the blocks with
 // more than one segment.  Segment counts are capped at max_segs, so malformed
 // metadata cannot address outside the workspace.
-__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult, int item_mult,
+__device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int dec_mult, int item_tiles,
                             bool dec_rows) {
   SeqPlan r{0, 0, 0};
   const bool row = dec_rows && len == 1;
   for (int q0 = 0; q0 < len; q0 += kQueryBlock) {
     const int qend = min(q0 + kQueryBlock, len);
     const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-    const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
+    const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_tiles);
     if (ns < 1) continue;
     if (row)
       r.dec += ns;
@@ -105,18 +107,83 @@ __device__ SeqPlan count_seq(int len, int pre, int seg_tiles, int max_segs, int 
   return r;
 }
 
-// One work-group.  Sequences are taken 256 at a time; each thread counts its
-// sequence's items and merge entries, a work-group scan gives the offsets, and
-// the thread writes them.  hdr[0], hdr[1] receive the totals.
+// New K/V rows for the cache, copied by the plan launch's other work-groups
+// when the attention pass reads every key from the cache.
+struct AppendArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* kc;
+  uint16_t* vc;
+  int num_kv_heads, cap, head_dim;
+  int64_t rows;  // tokens x K/V heads
+};
+
+// Chunk i (16 bytes, K rows then V rows) of every new token's K and V row
+// into the cache slab [B, HK, cap, D] at position prefix + (token - cu[b]);
+// tokens past cu[num_seqs], and positions outside the capacity, are left alone.
+__device__ __forceinline__ void append_chunk(int64_t i, const AppendArgs& a, const int32_t* __restrict__ cu,
+                                             const int32_t* __restrict__ prefix, int num_seqs) {
+  const int cpr = a.head_dim / 8;      // 16-byte chunks per row
+  const int64_t chunks = a.rows * cpr;
+  if (i >= 2 * chunks) return;
+  const bool is_v = i >= chunks;
+  const int64_t j = is_v ? i - chunks : i;
+  const int64_t row = j / cpr;         // token * HK + hk
+  const int c = (int)(j - row * cpr);
+  const int hk = (int)(row % a.num_kv_heads);
+  const int tok = (int)(row / a.num_kv_heads);
+  if (tok >= cu[num_seqs]) return;
+  int lo = 0, hi = num_seqs - 1;       // sequence lo: cu[lo] <= tok < cu[lo + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  const int pos = prefix[lo] + tok - cu[lo];
+  if (pos < 0 || pos >= a.cap) return;
+  const uint4 w = *reinterpret_cast<const uint4*>((is_v ? a.v : a.k) + row * a.head_dim + 8 * c);
+  uint16_t* dst = (is_v ? a.vc : a.kc) + (((int64_t)lo * a.num_kv_heads + hk) * a.cap + pos) * a.head_dim + 8 * c;
+  *reinterpret_cast<uint4*>(dst) = w;
+}
+
+// Work-group 0 plans.  Sequences are taken 256 at a time; each thread counts
+// its sequence's items and merge entries, a work-group scan gives the
+// offsets, and the thread writes them.  hdr[0], hdr[1] receive the totals.
+// Work-groups 1 onward (when a.rows > 0) append the new K/V rows.
 __global__ __launch_bounds__(kPlanThreads)
 void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
                          int num_seqs, int num_tokens, int seg_tiles, int max_segs, int dec_mult, int item_mult,
                          int dec_rows, int64_t max_items, int64_t max_dec, int64_t max_merges,
                          int32_t* __restrict__ hdr, int4* __restrict__ items,
                          int4* __restrict__ dec, int4* __restrict__ merges,
-                         unsigned long long* __restrict__ counters) {
+                         unsigned long long* __restrict__ counters, AppendArgs app, int fill_per_head) {
   __shared__ int wsum[3][kPlanThreads / 64];
   const int tid = __builtin_amdgcn_workitem_id_x();
+  const int wg = __builtin_amdgcn_workgroup_id_x();
+  if (wg > 0) {
+    append_chunk((int64_t)(wg - 1) * kPlanThreads + tid, app, cu, prefix, num_seqs);
+    return;
+  }
+  int item_tiles = item_mult * seg_tiles;
+  if (fill_per_head > 0) {
+    // items of about (all blocks' tiles) / fill_per_head tiles, at least 8:
+    // fill_per_head units per head fill the compute units however long the
+    // prefixes are
+    int64_t mine = 0;
+    for (int b = tid; b < num_seqs; b += kPlanThreads) {
+      const int st = cu[b], en = cu[b + 1], pre = prefix[b];
+      const int len = (st >= 0 && en <= num_tokens && en > st) ? en - st : 0;
+      for (int q0 = 0; q0 < len; q0 += kQueryBlock) mine += (pre + min(q0 + kQueryBlock, len) + kKeyTile - 1) / kKeyTile;
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    const int part = (int)min(mine, (int64_t)INT32_MAX / kPlanThreads);
+    const int s = wave_incl_scan(part, lane);
+    if (lane == 63) wsum[0][wave] = s;
+    __syncthreads();
+    int64_t total = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) total += wsum[0][w];
+    __syncthreads();  // wsum is reused below
+    item_tiles = (int)max((int64_t)8, min((total + fill_per_head - 1) / fill_per_head, (int64_t)1 << 24));
+  }
   if (tid < kSplitCounters) counters[tid] = 0;  // the attention pass hands out work through these
   const int lane = tid & 63, wave = tid >> 6;
   int64_t base_i = 0, base_d = 0, base_m = 0;
@@ -130,7 +197,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       pre = prefix[b];
       // tokens outside [0, num_tokens) would index outside the partial buffers
       len = (start >= 0 && end <= num_tokens && end > start) ? end - start : 0;
-      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult, item_mult, dec_rows != 0);
+      c = count_seq(len, pre, seg_tiles, max_segs, dec_mult, item_tiles, dec_rows != 0);
     }
     const int si = wave_incl_scan(c.items, lane);
     const int sd = wave_incl_scan(c.dec, lane);
@@ -162,12 +229,12 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
       const bool row = dec_rows && len == 1;
       const int nqb = (len + kQueryBlock - 1) / kQueryBlock;
       const int ntiles_last = (pre + len + kKeyTile - 1) / kKeyTile;  // the last block has the most
-      const int ns_max = block_segments(ntiles_last, row, seg_tiles, max_segs, dec_mult, item_mult);
+      const int ns_max = block_segments(ntiles_last, row, seg_tiles, max_segs, dec_mult, item_tiles);
       for (int s = 0; s < ns_max; ++s)
         for (int qb = 0; qb < nqb; ++qb) {
           const int qend = min(qb * kQueryBlock + kQueryBlock, len);
           const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-          const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
+          const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_tiles);
           if (s >= ns) continue;
           if (row) {
             if (off_d < max_dec) dec[off_d] = make_int4(b, s, ns, 0);
@@ -181,7 +248,7 @@ void splitkv_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restri
         const int q0 = qb * kQueryBlock;
         const int qend = min(q0 + kQueryBlock, len);
         const int ntiles = (pre + qend + kKeyTile - 1) / kKeyTile;
-        const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_mult);
+        const int ns = block_segments(ntiles, row, seg_tiles, max_segs, dec_mult, item_tiles);
         if (ns > 1)
           for (int r = q0; r < qend; r += kMergeRows, ++off_m)
             if (off_m < max_merges) merges[off_m] = make_int4(start + r, min(kMergeRows, qend - r), ns, 0);
@@ -288,17 +355,26 @@ SplitLayout split_layout(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
 
 hipError_t launch_splitkv_plan(const int32_t* cu, const int32_t* prefix, int32_t num_seqs,
                                int32_t num_tokens, const SplitLayout& L, int dec_seg_mult,
-                               int item_seg_mult, void* ws, hipStream_t stream, bool rows_as_items) {
+                               int item_seg_mult, void* ws, hipStream_t stream, bool rows_as_items,
+                               const FwdParams* append, int head_dim, int fill_per_head) {
   char* base = static_cast<char*>(ws);
   const int64_t max_merges = (int64_t)(L.off_lse - L.off_merges) / 16;
-  hipLaunchKernelGGL(splitkv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu, prefix,
+  AppendArgs app{};
+  int64_t blocks = 1;
+  if (append) {
+    app = AppendArgs{append->k, append->v, append->kc, append->vc, append->num_kv_heads, append->cap,
+                     head_dim, (int64_t)num_tokens * append->num_kv_heads};
+    blocks += (2 * app.rows * (app.head_dim / 8) + kPlanThreads - 1) / kPlanThreads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  }
+  hipLaunchKernelGGL(splitkv_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), 0, stream, cu, prefix,
                      num_seqs, num_tokens, L.seg_tiles, L.max_segs, dec_seg_mult, item_seg_mult,
                      rows_as_items ? 0 : 1, L.max_items, L.max_dec_items,
                      max_merges, reinterpret_cast<int32_t*>(base + L.off_hdr),
                      reinterpret_cast<int4*>(base + L.off_items),
                      reinterpret_cast<int4*>(base + L.off_dec),
                      reinterpret_cast<int4*>(base + L.off_merges),
-                     reinterpret_cast<unsigned long long*>(base + L.off_ctr));
+                     reinterpret_cast<unsigned long long*>(base + L.off_ctr), app, fill_per_head);
   return hipGetLastError();
 }
 
