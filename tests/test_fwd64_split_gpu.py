@@ -52,3 +52,20 @@ def test_fwd64_split_decode_row_as_item():
 @pytest.mark.parametrize("scale", [0.0, 2.0])
 def test_fwd64_split_scales(scale):
     check_case([260], [900], 2048, 4, 4, 128, 1295, "fwd64 split scale", scale=scale)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_fwd64_split_random(i):
+    """Seeded random lone chunks: lengths 2..700, prefixes 0..3000 (any offset
+    within a tile), grouped and odd head counts, three scales, capacity with
+    slack past the chunk."""
+    import numpy as np
+    from prefill_self_attention_amd import inputs as I
+    rng = np.random.default_rng(1300 + i)
+    H, HK = [(2, 1), (4, 2), (6, 3), (8, 8), (3, 3), (4, 4)][int(rng.integers(0, 6))]
+    n = int(rng.integers(2, 701))
+    pre = int(rng.integers(0, 3001))
+    cap = pre + n + int(rng.integers(0, 300))
+    scale = float([I.default_scale(128), 0.0, 0.7][int(rng.integers(0, 3))])
+    check_case([n], [pre], cap, H, HK, 128, 1400 + i, "fwd64 split random %d: len=%d prefix=%d" % (i, n, pre),
+               scale=scale)
