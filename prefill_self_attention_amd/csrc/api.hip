@@ -197,8 +197,11 @@ std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_split_occ[kMaxDevices][3][2];
 std::atomic<int> g_dec_occ[kMaxDevices][3][4][2];
 // Share of the split-KV work-groups that starts on the attention items (the
-// rest start on the decode rows' units).
-constexpr int kItemsFirstPercent = 50;
+// rest start on the decode rows' units): with streaming decode loads the
+// decode units need fewer work-groups to hold HBM busy, and about 30 % on the
+// items balanced the heaviest chunked step (too few, and the long items
+// finish last).
+constexpr int kItemsFirstPercent = 31;
 constexpr int kFuseMaxHeads = 2;
 static_assert(kFuseMaxHeads <= 2, "the mixed kernel has decode units of one and two query heads only");
 
