@@ -384,19 +384,19 @@ void prefill_fwd64_kernel(FwdParams p) {
         const f32x16_t o = get(std::integral_constant<int, 4 * qh + db>{});
 #pragma unroll
         for (int cp = 0; cp < 2; ++cp) {
-          // lane (row, hl) holds d = 32 db + 8 cc + 4 hl + [0, 4); lanes l and
-          // l^32 trade pieces so that each writes 8 consecutive d
+          // lane (row, hl) holds d = 32 db + 8 cc + 4 hl + [0, 4).  One
+          // permlane32_swap per register pair moves the upper lanes' pieces
+          // of column group 2 cp and the lower lanes' of 2 cp + 1 across, so
+          // every lane then holds 8 consecutive d: 2 cp + hl's
           const int ca = 2 * cp, cb = 2 * cp + 1;
           const uint32_t a0 = pack_bf16x2(o[4 * ca + 0] * inv, o[4 * ca + 1] * inv);
           const uint32_t a1 = pack_bf16x2(o[4 * ca + 2] * inv, o[4 * ca + 3] * inv);
           const uint32_t b0 = pack_bf16x2(o[4 * cb + 0] * inv, o[4 * cb + 1] * inv);
           const uint32_t b1 = pack_bf16x2(o[4 * cb + 2] * inv, o[4 * cb + 3] * inv);
-          const uint32_t s0 = hl ? a0 : b0, s1 = hl ? a1 : b1;
-          const auto x0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
-          const auto x1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
-          const uint32_t o0 = hl ? x0[0] : x0[1], o1 = hl ? x1[0] : x1[1];
-          const u32x4_t w = hl ? u32x4_t{o0, o1, b0, b1} : u32x4_t{a0, a1, o0, o1};
-          __builtin_amdgcn_raw_buffer_store_b128(w, orsrc, rowoff + 2 * (32 * db + 8 * (hl ? cb : ca)), 0, 0);
+          const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          const u32x4_t w = {x0[0], x1[0], x0[1], x1[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(w, orsrc, rowoff + 2 * (32 * db + 8 * (ca + hl)), 0, 0);
         }
       });
     });
