@@ -86,7 +86,7 @@ struct Fwd64Loop {
   int32_t r0p, r0p1, r0p63;  // key position of the wave's first row less 128 x block (+1, +63)
   int32_t len;        // sequence length
   int32_t gt;         // lower group's last light position (-2: none)
-  int32_t wlom1, wwid; // window of the loop entry's common iterations: (wlom1, wlom1 + 1 + wwid]
+  int32_t wlom1b, wwidb;  // bookkeeping window of the second run (lower group after the transition)
   uint32_t tileb;     // bytes of 64 K / V rows
   uint32_t nrec;      // bytes from the sequence's first K / V row to the end of its last
   uint32_t m0b;       // LDS address of the wave's first load block in its group
@@ -102,6 +102,8 @@ struct Fwd64Loop {
   uint32_t crow;      // first tile row of the lane in the cache copy
   uint32_t coe, coo;  // cache byte offsets of the copy's even / odd rows
   uint32_t qo0, qo1;  // Q byte offsets of the heavy block's rows (halves 0, 1)
+  uint32_t olo, ohi, onrec;  // output rows of this (sequence, head): base, bytes to the end of the last
+  uint32_t oo0, oo1;  // output byte offsets of the light block's rows (halves 0, 1; + 16 lane/32)
 };
 
 // Wave-uniform values for the asm statements' SGPR operands.
@@ -282,7 +284,7 @@ void prefill_fwd64_kernel(FwdParams p) {
   L.r0p1 = L.r0p + 1;
   L.r0p63 = L.r0p + 63;
   L.len = len;
-  L.gt = transition ? e_lo - 1 : -2;
+  L.gt = transition ? e_lo - 1 : -100;  // -100: never (g >= -1 meets none of gt - 1, gt, gt + 1)
   L.tileb = (uint32_t)kBN * rs;
   // keys [0, prefix + len), within the cache row's capacity (split)
   L.nrec = (uint32_t)((kSplit ? min(pfx + len, p.cap) : len) - 1) * rs + kRowBytes;
@@ -338,6 +340,15 @@ void prefill_fwd64_kernel(FwdParams p) {
     L.qo0 = (uint32_t)min(first + ql, len - 1) * rsq + 16u * hl;
     L.qo1 = (uint32_t)min(first + 32 + ql, len - 1) * rsq + 16u * hl;
   }
+  {
+    const uint16_t* ob = p.out + ((int64_t)seq_start * H + h) * kD;
+    L.olo = (uint32_t)(uintptr_t)ob;
+    L.ohi = (uint32_t)((uintptr_t)ob >> 32);
+    L.onrec = (uint32_t)(len - 1) * rsq + kRowBytes;
+    const int first = z * kBM + 64 * wsub;  // the light block's rows (the store runs rows past len out of range)
+    L.oo0 = (uint32_t)(first + ql) * rsq + 16u * hl;
+    L.oo1 = (uint32_t)(first + 32 + ql) * rsq + 16u * hl;
+  }
 
   // ---------------------------------------------------------------- prologue
   // Q of the first block's rows (rows past the sequence read its last row);
@@ -361,7 +372,7 @@ void prefill_fwd64_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- loop
   float m0 = kMInit, l0 = 0.f, m1 = kMInit, l1 = 0.f;   // halves 0 and 1
-  float m0n = kMInit, l0n = 0.f;                         // the light block's half 0 at the transition
+  float m0n = kMInit, l0n = 0.f, l1n = 0.f;              // the light block's state at the transition
 
   // store one block's finished rows (this wave's 64), column blocks
   // [D0, D1) of 32: block i of O^T from get(i), divided by the row sums
@@ -410,32 +421,29 @@ void prefill_fwd64_kernel(FwdParams p) {
   // gen_fwd64.py) for a run of positions [x0, x1) holding tiles x + off of
   // block blk: h - 1 in the run, h + 2 before its end, T[h + 1] wholly
   // visible to the wave (below (R0 + 1) / 64, see kind_of) and, when the
-  // wave copies to the cache, before the block's own tiles.
-  auto set_window = [&](int x0, int x1, int off, int blk) {
+  // wave copies to the cache, before the block's own tiles.  Encoded as
+  // (lo - 1, hi - lo), or an empty window.
+  auto window = [&](int x0, int x1, int off, int blk, int32_t& lom1, int32_t& wid) {
     int hi = min(x1 - 3, ((kBM * blk + L.r0p1) >> 6) - off - 2);
     if (L.copy) hi = min(hi, 2 * blk - off - 2);
     const int lo = x0 + 1;
-    L.wlom1 = hi < lo ? INT32_MIN : lo - 1;
-    L.wwid = hi < lo ? 0 : hi - lo;
+    lom1 = hi < lo ? INT32_MIN : lo - 1;
+    wid = hi < lo ? 0 : hi - lo;
   };
-  int g = -1;
-  for (;;) {
-    L.gstart = g;
-    if (kSplit) set_window(0, n_my, seg_t0, qb_hi);
-    else if (upper) set_window(0, n_my, 0, qb_hi);
-    else if (g < 0 && has_lo) set_window(0, e_lo, 0, z);
-    else set_window(g < 0 ? 0 : e_lo, n_my, L.jump, qb_hi);
-    g = fwd64_loop(L, m0, l0, m1, l1, m0n, l0n);
-    if (g >= n_up) break;
-    // the lower group's light block is finished (its half-0 state was moved
-    // to m0n, l0n when the heavy block's first tile started): store it and
-    // start the heavy block's half 1
-    mfma_drain();
-    store_rows(z, l0n, l1, o_get);
-    fwd64_o_zero();
-    m1 = kMInit;
-    l1 = 0.f;
-  }
+  int32_t wlom1, wwid;
+  if (kSplit) window(0, n_my, seg_t0, qb_hi, wlom1, wwid);
+  else if (upper) window(0, n_my, 0, qb_hi, wlom1, wwid);
+  else if (has_lo) window(0, e_lo, 0, z, wlom1, wwid);
+  else window(0, n_my, L.jump, qb_hi, wlom1, wwid);
+  L.wlom1b = wlom1;
+  L.wwidb = wwid;
+  if (transition) window(e_lo, n_my, L.jump, qb_hi, L.wlom1b, L.wwidb);
+  // one pass over the iterations: the lower group's light block (when a
+  // heavy part follows it) is stored, and O restarted, inside the loop
+  L.gstart = -1;
+  wlom1 = __builtin_amdgcn_readfirstlane(wlom1);  // wave-uniform: in-out SGPR operands
+  wwid = __builtin_amdgcn_readfirstlane(wwid);
+  fwd64_loop(L, m0, l0, m1, l1, m0n, l0n, l1n, wlom1, wwid);
 
   if constexpr (kSplit) {
     mfma_drain();

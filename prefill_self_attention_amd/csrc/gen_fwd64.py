@@ -57,6 +57,7 @@ T_MNEW = V_T + 3
 T_ALPHA = V_T + 4                   # rescale factor (kept to the end of the phase)
 T_NINF = V_T + 5                    # -inf
 T_VDD = V_T + 6                     # vd + R0 - 64 t (general diagonal mask)
+T_INV = (V_T + 6, V_T + 7)          # 1 / row sums of the light block's halves (its store)
 T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
 
 # scalar registers of the loop.  Pairs alternate with the iteration's
@@ -360,14 +361,65 @@ def loads(par, matrix):
     return groups
 
 
-def score_phase(par, tag):
+def light_store_groups():
+    """The lower group's finished light block, stored from O during the
+    heavy block's first score phase (O is free until that iteration's PV
+    phase): per lane 1 / (own + partner row sum) for each half, then per
+    block of 16 accumulators: read, scale, pack to bf16, one
+    v_permlane32_swap per register pair (each lane then holds 8 consecutive
+    columns: those of column group 2 cp + lane/32) and two 16-byte buffer
+    stores through the output descriptor, built in S_CB, whose range ends
+    at the sequence's last row.  Uses the V operand slots (idle in a score
+    phase) and T_INV, T_RS[0]."""
+    t = T_RS[0]
+    groups = [["s_mov_b32 %s, %%[olo]" % sr(S_CB), "s_mov_b32 %s, %%[ohi]" % sr(S_CB + 1),
+               "s_mov_b32 %s, %%[onrec]" % sr(S_CB + 2), "s_mov_b32 %s, 0x20000" % sr(S_CB + 3)]]
+    for qh, l in ((0, "%[l0n]"), (1, "%[l1n]")):
+        inv = T_INV[qh]
+        groups.append(["v_mov_b32 %s, %s" % (vr(inv), l), "v_mov_b32 %s, %s" % (vr(t), l), "s_nop 1",
+                       "v_permlane32_swap_b32 %s, %s" % (vr(inv), vr(t)), "s_nop 1",
+                       "v_add_f32 %s, %s, %s" % (vr(inv), vr(inv), vr(t)),
+                       "v_rcp_f32 %s, %s" % (vr(inv), vr(inv)), "s_nop 1"])
+    for qh in range(2):
+        for db in range(4):
+            o = A_O + 16 * (4 * qh + db)
+            groups.append(["v_accvgpr_read_b32 %s, %s" % (vr(V_VF + i), ar(o + i)) for i in range(8)])
+            groups.append(["v_accvgpr_read_b32 %s, %s" % (vr(V_VF + i), ar(o + i)) for i in range(8, 16)])
+            groups.append(["v_mul_f32 %s, %s, %s" % (vr(V_VF + i), vr(T_INV[qh]), vr(V_VF + i)) for i in range(8)])
+            groups.append(["v_mul_f32 %s, %s, %s" % (vr(V_VF + i), vr(T_INV[qh]), vr(V_VF + i)) for i in range(8, 16)])
+            groups.append(["v_cvt_pk_bf16_f32 %s, %s, %s" % (vr(V_VF + k), vr(V_VF + 2 * k), vr(V_VF + 2 * k + 1))
+                           for k in range(8)])
+            groups.append(["s_nop 1",
+                           "v_permlane32_swap_b32 %s, %s" % (vr(V_VF + 0), vr(V_VF + 2)),
+                           "v_permlane32_swap_b32 %s, %s" % (vr(V_VF + 1), vr(V_VF + 3)),
+                           "v_permlane32_swap_b32 %s, %s" % (vr(V_VF + 4), vr(V_VF + 6)),
+                           "v_permlane32_swap_b32 %s, %s" % (vr(V_VF + 5), vr(V_VF + 7)),
+                           "s_nop 1",
+                           "buffer_store_dwordx4 %s, %%[oo%d], %s, 0 offen offset:%d" % (vr(V_VF, 4), qh, sr(S_CB, 4), 64 * db),
+                           "buffer_store_dwordx4 %s, %%[oo%d], %s, 0 offen offset:%d" % (vr(V_VF + 4, 4), qh, sr(S_CB, 4), 64 * db + 32),
+                           "s_nop 1"])
+    return groups
+
+
+def o_zero_ops():
+    """O = 0 by eight MFMAs with zero operands (T_RS[0:4]) and C = 0."""
+    z = vr(T_RS[0], 4)
+    return (["v_mov_b32 %s, 0" % vr(T_RS[i]) for i in range(4)] + ["s_nop 4"] +
+            ["%s %s, %s, %s, 0" % (MFMA, ar(A_O + 16 * i, 16), z, z) for i in range(8)])
+
+
+def score_phase(par, tag, store=False):
     """Score phase of an iteration of parity par: S(T[g+1]) beside
     softmax(T[g], half 1), loads of K(T[g+2]) and V(T[g+1]) (descriptors
     S_VK, S_VV).  In the last iteration T[g+1] does not exist: its K slot
-    holds a refilled tile and the scores go unused."""
+    holds a refilled tile and the scores go unused.  store: the lower
+    group's first heavy iteration, which also stores the light block from O
+    and then zeroes O for the heavy block's first PV phase."""
     body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
             "s_mov_b32 %s, 0" % sr(S_FLAG)]
     fill = softmax_ops(1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1")
+    if store:
+        fill = interleave(fill, light_store_groups())
     k_l, v_l = loads(par, 'k'), loads(par, 'v')
     # pairs sharing an M0 stay together: K0 K1 V0 V1 K2 K3 ...
     loadg = [x for j in range(0, ROWSTEP_LOADS, 2) for x in (k_l[j], k_l[j + 1], v_l[j], v_l[j + 1])]
@@ -388,6 +440,9 @@ def score_phase(par, tag):
                                                      ar(A_Q + 4 * (8 * qh + ds), 4), src_c), f))
     body += schedule(mfmas, frag_reads, 1, fill, loadg)
     body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
+    if store:
+        # the PV MFMAs accumulate into O next
+        body += ["s_nop 2"] + o_zero_ops() + ["s_nop 7", "s_nop 7"]
     return body
 
 
@@ -506,10 +561,12 @@ def book_next(par):
         # V of T[h+1], or of T[h] when there is no T[h+1]
         ["s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, %s, %s" % (NY, T0, T1)] +
         descriptor(S_NY, S_VV, "vbl", "vbh", tmp=S_NY),
-        # out-of-line middle part: Q reload (h + 1 == gt), transition (h == gt)
+        # rare parts: Q reload (h + 1 == gt), transition (h == gt), the light
+        # block's store (h == gt + 1)
         ["s_add_i32 %s, %s, 2" % (NY, g), "s_cmp_eq_u32 %s, %%[gt]" % NY, "s_cselect_b32 %s, 1, 0" % sr(S_SPEC),
          "s_add_i32 %s, %s, 1" % (NY, g), "s_cmp_eq_u32 %s, %%[gt]" % NY,
-         "s_cselect_b32 %s, 1, %s" % (sr(S_SPEC), sr(S_SPEC))],
+         "s_cselect_b32 %s, 1, %s" % (sr(S_SPEC), sr(S_SPEC)),
+         "s_cmp_eq_u32 %s, %%[gt]" % g, "s_cselect_b32 %s, 1, %s" % (sr(S_SPEC), sr(S_SPEC))],
         # ... or a cache copy of K(T[h+1]) or V(T[h]) (tiles of the wave's own block)
         ["s_lshr_b32 %s, %s, 1" % (NY, T1), "s_cmp_eq_u32 %s, %s" % (NY, B1), "s_cselect_b32 %s, 1, 0" % NY,
          "s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, 0, %s" % (NY, NY)],
@@ -672,14 +729,20 @@ def score_mask_part(par):
     L = lambda name: lbl(name, par)
     KS = sr(roles(par)["KS"])
     out = ["s_cmp_eq_u32 %s, 0" % sr(S_CS),
-           "s_cbranch_scc1 %s" % L("sgo"),
+           "s_cbranch_scc1 %s" % L("smend"),
            "s_cmp_eq_u32 %s, 1" % KS,
            "s_cbranch_scc1 %s" % L("ssd"),
            "s_cmp_eq_u32 %s, 0" % KS,
-           "s_cbranch_scc1 %s" % L("sgo")]
+           "s_cbranch_scc1 %s" % L("smend")]
     r = roles(par)
-    out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("sgo"), "%s:" % L("ssd")]
+    out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("smend"), "%s:" % L("ssd")]
     out += diag_mask(1, s_bank(par), r["T0"], r["B0"], "s%d" % par)
+    # the lower group's first heavy iteration (g == gt + 1) takes the score
+    # phase that also stores the light block
+    out += ["%s:" % L("smend"),
+            "s_add_i32 %s, %%[gt], 1" % sr(S_X),
+            "s_cmp_eq_u32 %s, %s" % (sr(S_G), sr(S_X)),
+            "s_cbranch_scc1 %s" % L("sst")]
     return out
 
 
@@ -695,12 +758,20 @@ def middle_part(par):
            "s_add_i32 %s, %s, 1" % (sr(S_X), g),
            "s_cmp_eq_u32 %s, %%[gt]" % sr(S_X),
            "s_cbranch_scc0 %s" % L("noq")] + q_reload() + ["%s:" % L("noq")]
+    # (the half-1 state of the light block is final after this score phase:
+    # its row sum is kept for the store, and half 1 restarts with the next
+    # tile; the bookkeeping window moves to the heavy run)
     out += ["s_cmp_eq_u32 %s, %%[gt]" % g,
             "s_cbranch_scc0 %s" % L("notr"),
             "v_mov_b32 %[m0n], %[m0v]",
             "v_mov_b32 %[l0n], %[l0v]",
             "v_mov_b32 %%[m0v], %s" % MINIT,
             "v_mov_b32 %[l0v], 0",
+            "v_mov_b32 %[l1n], %[l1v]",
+            "v_mov_b32 %%[m1v], %s" % MINIT,
+            "v_mov_b32 %[l1v], 0",
+            "s_mov_b32 %[wlom1], %[wlom1b]",
+            "s_mov_b32 %[wwid], %[wwidb]",
             "%s:" % L("notr")]
     return out
 
@@ -749,7 +820,8 @@ def body(par):
     out += copy_part(par) + score_mask_part(par)
     out += ["%s:" % L("sgo")]
     out += score_phase(par, "s" + P)
-    out += ["s_or_b32 %s, %s, %s" % (sr(S_X), sr(S_SPEC), sr(S_CP)),
+    out += ["%s:" % L("sdn"),
+            "s_or_b32 %s, %s, %s" % (sr(S_X), sr(S_SPEC), sr(S_CP)),
             "s_cbranch_scc0 %s" % L("pgo")]
     out += middle_part(par) + pv_mask_part(par)
     out += ["%s:" % L("pgo")]
@@ -769,19 +841,21 @@ def slow_paths(par):
     L = lambda name: lbl(name, par)
     P = "p%d" % par
     out = ["%s:" % L("pre")] + pv_phase(par, False, "q" + P) + ["s_branch %s" % L("pdone")]
+    out += ["%s:" % L("sst")] + score_phase(par, "t" + P, store=True) + ["s_branch %s" % L("sdn")]
     return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
-LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "r0p", "r0p1", "r0p63", "len", "gt", "wlom1", "wwid",
+LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "r0p", "r0p1", "r0p63", "len", "gt",
+                "wlom1b", "wwidb", "olo", "ohi", "onrec",
                 "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
 LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
-                "fk6", "fk7", "vd", "cl", "coe", "coo", "qo0", "qo1"]
+                "fk6", "fk7", "vd", "cl", "coe", "coo", "qo0", "qo1", "oo0", "oo1"]
 
 
 def loop_text():
     """Iterations S_G = gstart .. nit-1 (gstart may be -1: the pre-loop
-    iteration), leaving after the transition iteration gt (returns gt + 1)
-    or after the last (returns nit)."""
+    iteration).  The lower group's light block is stored inside the loop
+    (the score phase of iteration gt + 1)."""
     out = ["s_mov_b32 %s, m0" % sr(S_M0SAVE),
            "s_mov_b32 %s, 0x20000" % sr(S_VK + 3),
            "s_mov_b32 %s, 0x20000" % sr(S_VV + 3),
@@ -792,24 +866,17 @@ def loop_text():
     out += [".Lentry0_%=:"] + book_entry(0) + ["s_branch .Leven_%="]
     out += [".Lodd_%=:"]
     out += body(1)
-    out += ["s_cmp_eq_u32 %s, %%[gt]" % sr(S_G),
-            "s_cbranch_scc1 .Ltrans_%=",
-            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
             "s_cmp_ge_i32 %s, %%[nit]" % sr(S_G),
             "s_cbranch_scc1 .Lend_%="]
     out += [".Leven_%=:"]
     out += body(0)
-    out += ["s_cmp_eq_u32 %s, %%[gt]" % sr(S_G),
-            "s_cbranch_scc1 .Ltrans_%=",
-            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
+    out += ["s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
             "s_cmp_ge_i32 %s, %%[nit]" % sr(S_G),
             "s_cbranch_scc0 .Lodd_%=",
             "s_branch .Lend_%="]
     out += slow_paths(1) + slow_paths(0)
-    out += [".Ltrans_%=:",
-            "s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
-            ".Lend_%=:",
-            "s_mov_b32 %%[gout], %s" % sr(S_G),
+    out += [".Lend_%=:",
             "s_mov_b32 m0, %s" % sr(S_M0SAVE)]
     return out
 
@@ -819,23 +886,23 @@ SGPR_CLOBBERS = ", ".join('"s%d"' % r for r in NUM_SGPR_FIXED)
 
 
 def loop_function():
-    lines = ["// Main loop: iterations gstart .. nit-1 of this wave (see gen_fwd64.py);",
-             "// returns the next iteration (gt + 1 after the transition iteration gt).",
-             "__device__ __forceinline__ int fwd64_loop(const Fwd64Loop& L, float& m0v, float& l0v, float& m1v,",
-             "                                          float& l1v, float& m0n, float& l0n) {",
-             "  int gout;",
+    lines = ["// Main loop: iterations gstart .. nit-1 of this wave (see gen_fwd64.py).",
+             "// wlom1, wwid: the bookkeeping window of the first run (moved to the",
+             "// second run's, wlom1b and wwidb, at the lower group's transition).",
+             "__device__ __forceinline__ void fwd64_loop(const Fwd64Loop& L, float& m0v, float& l0v, float& m1v,",
+             "                                           float& l1v, float& m0n, float& l0n, float& l1n,",
+             "                                           int32_t& wlom1, int32_t& wwid) {",
              "  asm volatile("]
     for ins in loop_text():
         lines.append('      "%s\\n"' % ins.replace('"', '\\"'))
-    outs = ['[gout] "=s"(gout)', '[m0v] "+v"(m0v)', '[l0v] "+v"(l0v)', '[m1v] "+v"(m1v)', '[l1v] "+v"(l1v)',
-            '[m0n] "+v"(m0n)', '[l0n] "+v"(l0n)']
+    outs = ['[m0v] "+v"(m0v)', '[l0v] "+v"(l0v)', '[m1v] "+v"(m1v)', '[l1v] "+v"(l1v)',
+            '[m0n] "+v"(m0n)', '[l0n] "+v"(l0n)', '[l1n] "+v"(l1n)', '[wlom1] "+s"(wlom1)', '[wwid] "+s"(wwid)']
     ins = ['[c] "s"(sgpr_f32(L.c))'] + ['[%s] "s"(sgpr_u32(L.%s))' % (n, n) for n in LOOP_SGPR_IN]
     ins += ['[qb] "s"(sgpr_ptr(L.qb))']
     ins += ['[%s] "v"(L.%s)' % (n, n) for n in LOOP_VGPR_IN]
     lines.append("      : " + ", ".join(outs))
     lines.append("      : " + ", ".join(ins))
     lines.append('      : "vcc", "scc", "memory", ' + SGPR_CLOBBERS + ", " + FIXED_CLOBBERS + ");")
-    lines.append("  return gout;")
     lines.append("}")
     return "\n".join(lines)
 
