@@ -276,22 +276,27 @@ def gcost(g):
     return sum(cost(x) for x in g)
 
 
-def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
+def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg, prefetched=False, tail=()):
     """Interleave: before every fourth MFMA (fragments f, f + 1) wait for
     their reads and issue the reads of fragments up to f + 3; load pair i =
     (before, after) goes around
     MFMA i; the filler
     groups (softmax) fill each MFMA slot up to SLOT_BUDGET issue cycles, in
     order (raised when the rest would not fit; what is left follows the last
-    MFMA)."""
+    MFMA).  The first LOOKAHEAD fragments' reads open the phase unless the
+    previous phase issued them (prefetched).  tail: reads of the next
+    phase's first fragments, issued after the last wait (no older read is
+    then outstanding)."""
     nfrag = len(frag_reads)
     out = []
-    for f in range(min(LOOKAHEAD, nfrag)):
-        out += frag_reads[f]
+    fi = 0
+    if not prefetched:
+        for f in range(min(LOOKAHEAD, nfrag)):
+            out += frag_reads[f]
     issued = min(LOOKAHEAD, nfrag)
+    last_wait = max(s for s in range(len(mfmas)) if s % 4 == 0)
     nslots = len(mfmas)
     load_at = {i: g for i, g in enumerate(loadg)}
-    fi = 0
     for s, (mf, f) in enumerate(mfmas):
         used = 0
         if s % 4 == 0:
@@ -306,6 +311,10 @@ def schedule(mfmas, frag_reads, reads_per_frag, fillers, loadg):
                 out += frag_reads[issued]
                 used += gcost(frag_reads[issued])
                 issued += 1
+            if s == last_wait:
+                for grp in tail:
+                    out += grp
+                    used += gcost(grp)
         if s in load_at:
             out += load_at[s][0]
             used += gcost(load_at[s][0])
@@ -438,11 +447,18 @@ def score_phase(par, tag, store=False):
                 src_c = "0" if ds == 0 else vr(dst, 16)
                 mfmas.append(("%s %s, %s, %s, %s" % (MFMA, vr(dst, 16), vr(slot, 4),
                                                      ar(A_Q + 4 * (8 * qh + ds), 4), src_c), f))
-    body += schedule(mfmas, frag_reads, 1, fill, loadg)
+    # the PV phase's first V fragments (V(T[g]) is in LDS since the last
+    # barrier; the V slots are idle in this phase, but the store variant
+    # uses them as temporaries until its end): the PV phase starts without
+    # waiting out a read's latency
+    hoisted = pv_frag_reads(par)[:LOOKAHEAD]
+    body += schedule(mfmas, frag_reads, 1, fill, loadg, tail=() if store else hoisted)
     body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
     if store:
         # the PV MFMAs accumulate into O next
         body += ["s_nop 2"] + o_zero_ops() + ["s_nop 7", "s_nop 7"]
+        for grp in hoisted:
+            body += grp
     return body
 
 
@@ -462,6 +478,21 @@ def interleave(main, extra):
     return out
 
 
+def pv_frag_reads(par):
+    """LDS reads of the PV phase's V fragments (V(T[g]) in V slot g % 2):
+    fragment f = 4 gg + db into V operand slot f % 4."""
+    vslot = V_OFF + par * K_SLOT_BYTES
+    out = []
+    for gg in range(4):
+        for db in range(4):
+            f = 4 * gg + db
+            slot = V_VF + 4 * (f % 4)
+            off = vslot + 128 * (db >> 1) + 4096 * gg
+            out.append(["ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot, 2), db & 1, off),
+                        "ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot + 2, 2), db & 1, off + 2048)])
+    return out
+
+
 def pv_phase(par, has_pv, tag):
     """PV phase of an iteration of parity par: O += P(T[g]) V(T[g]) (if
     has_pv) beside softmax(T[g+1], half 0) and
@@ -471,22 +502,18 @@ def pv_phase(par, has_pv, tag):
     fill = softmax_ops(0, V_SA, V_PA[1 - par], "%[m0v]", "%[l0v]", tag + "h0")
     fill = interleave(fill, book_fast(par))
     if has_pv:
-        vslot = V_OFF + par * K_SLOT_BYTES          # V(T[g]) in slot g % 2
-        frag_reads = []
+        frag_reads = pv_frag_reads(par)
         mfmas = []
         for gg in range(4):
             for db in range(4):
                 f = 4 * gg + db
                 slot = V_VF + 4 * (f % 4)
-                off = vslot + 128 * (db >> 1) + 4096 * gg
-                frag_reads.append(["ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot, 2), db & 1, off),
-                                   "ds_read_b64_tr_b16 %s, %%[vb%d] offset:%d" % (vr(slot + 2, 2), db & 1, off + 2048)])
                 for qh in range(2):
                     o = A_O + 16 * (4 * qh + db)
                     pb = (V_PA[par] if qh == 0 else V_PB) + 4 * gg
                     mfmas.append(("%s %s, %s, %s, %s" % (MFMA, ar(o, 16), vr(slot, 4), vr(pb, 4), ar(o, 16)), f))
         body += ["s_nop 1"]   # the weights were written by VALU instructions
-        body += schedule(mfmas, frag_reads, 2, fill, [])
+        body += schedule(mfmas, frag_reads, 2, fill, [], prefetched=True)
     else:
         for g in fill:
             body += g

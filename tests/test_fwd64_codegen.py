@@ -65,7 +65,16 @@ def test_schedule_keeps_every_instruction_once():
             assert sum(1 for x in body if x.startswith("buffer_load")) == 16
             pv = g.pv_phase(par, True, "t")
             assert sum(1 for x in pv if x.startswith("v_mfma")) == 32
-            assert sum(1 for x in pv if x.startswith("ds_read_b64_tr_b16")) == 32
+            # the PV phase's V fragments: its first ones read at the end of
+            # the score phase, after its last LDS wait, the rest in the phase
+            hoisted = [x for x in body if x.startswith("ds_read_b64_tr_b16")]
+            in_pv = [x for x in pv if x.startswith("ds_read_b64_tr_b16")]
+            assert sorted(hoisted + in_pv) == sorted(x for grp in g.pv_frag_reads(par) for x in grp)
+            if hoisted:
+                last_wait = max(i for i, x in enumerate(body) if x.startswith("s_waitcnt lgkmcnt"))
+                assert body.index(hoisted[0]) > last_wait
+                for variant in (body, g.score_phase(par, "u", store=True)):
+                    assert [x for x in variant if x.startswith("ds_read_b64_tr_b16")] == hoisted
 
 
 def _hipcc():
