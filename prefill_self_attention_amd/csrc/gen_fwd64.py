@@ -52,13 +52,14 @@ A_Q = 192
 
 # temporaries (v[64:79])
 T_MX0, T_MX1 = V_T + 0, V_T + 1     # row-max chains / permlane pair
+T_TS = V_T + 0                      # a half-tile's sum of weights (the max chains reuse it)
 T_THR = V_T + 2                     # m + 8
 T_MNEW = V_T + 3
 T_ALPHA = V_T + 4                   # rescale factor (kept to the end of the phase)
 T_NINF = V_T + 5                    # -inf
 T_VDD = V_T + 6                     # vd + R0 - 64 t (general diagonal mask)
 T_INV = (V_T + 6, V_T + 7)          # 1 / row sums of the light block's halves (its store)
-T_RS = list(range(V_T + 8, V_T + 16))  # O-rescale pipeline
+T_RS = list(range(V_T + 8, V_T + 16))  # weights in flight; O-rescale pipeline
 
 # scalar registers of the loop.  Pairs alternate with the iteration's
 # parity: iteration g of parity par = g % 2 reads T[g] from S_TT[par] and
@@ -115,6 +116,45 @@ def s_bank(par):
 
 
 # ------------------------------------------------------------------ softmax
+# out-of-line blocks of the loop (the exact path of the softmax), emitted
+# after the loop's other out-of-line parts
+RARE = []
+# per-lane partial sum of one half-tile's weights above which the exact path
+# runs: 2^16 (also catches inf and NaN)
+TS_LIMIT = "0x47800000"
+
+
+def p_loop(sbase, pbase, m):
+    """p = 2^(s c - m) for the 32 scores at sbase (kept intact), through the
+    rotating temporaries T_RS; P packed to bf16 pairs at pbase in the
+    B-operand order of the PV MFMAs; T_TS = sum of the unrounded p in fp32
+    (v_add: the dot-product form of the sum stalls beside the MFMAs on this
+    part).  Every exp result is read at least two instructions after the
+    exp (transcendental results need a wait state)."""
+    R = T_RS
+    groups = []
+
+    def pack(k):
+        a, b = R[(2 * k) % len(R)], R[(2 * k + 1) % len(R)]
+        out = [["v_cvt_pk_bf16_f32 %s, %s, %s" % (vr(pbase + k), vr(a), vr(b))]]
+        if k == 0:
+            out.append(["v_add_f32 %s, %s, %s" % (vr(T_TS), vr(a), vr(b))])
+        else:
+            out += [["v_add_f32 %s, %s, %s" % (vr(T_TS), vr(T_TS), vr(a))],
+                    ["v_add_f32 %s, %s, %s" % (vr(T_TS), vr(T_TS), vr(b))]]
+        return out
+    for i in range(32):
+        groups.append(["v_fma_f32 %s, %s, %%[c], -%s" % (vr(R[i % len(R)]), vr(sbase + i), m)])
+        if i >= 1:
+            groups.append(["v_exp_f32 %s, %s" % (vr(R[(i - 1) % len(R)]), vr(R[(i - 1) % len(R)]))])
+        if i >= 2 and (i - 2) % 2 == 1:
+            groups += pack((i - 2) // 2)
+    groups.append(["v_exp_f32 %s, %s" % (vr(R[31 % len(R)]), vr(R[31 % len(R)]))])
+    groups.append(["s_nop 1"])
+    groups += pack(15)
+    return groups
+
+
 def softmax_ops(qh, sbase, pbase, m, l, tag):
     """Online-softmax update of one query half over one 64-key tile.
 
@@ -126,13 +166,37 @@ def softmax_ops(qh, sbase, pbase, m, l, tag):
     B-operand order of the PV MFMAs.  m, l: the half's running max (exp2
     domain) and per-lane partial sum.
 
+    The weights of any m are exact once O and l use the same m, so the
+    common path takes p = 2^(s c - m) against the running max without
+    the tile's max, and checks the lane's sum of the tile's 32 weights: at
+    most 2^16 (no weight above it: O and l stay far from overflow) and the
+    tile is done.  Otherwise (the row's first tile, where m is still the
+    initial -1e30, or a tile whose scores pass m by more than about 11) the
+    exact path out of line takes the tile's row max as in the textbook
+    update, moves m when the max exceeds it by more than 8, sets S_FLAG and
+    rescales l (O is rescaled at the end of the phase), recomputes the
+    weights from the scores, which the common path left intact, and
+    returns.
+
     Returns a list of groups; a group's instructions are emitted together.
-    When some lane's running max moves, S_FLAG is set and l rescaled; the O
-    accumulators are rescaled at the end of the phase.
     """
+    back = ".Lsb%s_%%=" % tag
+    exact = ".Lsx%s_%%=" % tag
+    groups = p_loop(sbase, pbase, m)
+    groups.append(["v_cmp_nge_f32 vcc, %s, %s" % (TS_LIMIT, vr(T_TS)),
+                   "s_cbranch_vccnz %s" % exact,
+                   "%s:" % back,
+                   "v_add_f32 %s, %s, %s" % (l, l, vr(T_TS))])
+    RARE.append(["%s:" % exact] + [x for grp in exact_ops(sbase, m, l, tag) + p_loop(sbase, pbase, m) for x in grp]
+                + ["s_branch %s" % back])
+    return groups
+
+
+def rowmax_ops(sbase):
+    """T_MX0 = c * (row max of the tile's 32 scores and the lane partner's):
+    two v_max3 chains and one v_permlane32_swap."""
     groups = []
     live = list(range(32))
-    # row max over the live scores: two chains of v_max3, then the partner lane
     chains = [live[:len(live) // 2], live[len(live) // 2:]]
     for ci, ch in enumerate(chains):
         t = T_MX0 + ci
@@ -150,11 +214,25 @@ def softmax_ops(qh, sbase, pbase, m, l, tag):
                    "s_nop 1",
                    "v_max_f32 %s, %s, %s" % (vr(T_MX0), vr(T_MX0), vr(T_MX1)),
                    # row max in the exp2 domain (c > 0)
-                   "v_mul_f32 %s, %%[c], %s" % (vr(T_MX0), vr(T_MX0)),
-                   "v_add_f32 %s, 0x41000000, %s" % (vr(T_THR), m)])
-    # lazy rescale: the running max moves only when a lane's tile max exceeds
-    # it by more than 8 (so p stays below 2^8); then l *= alpha now and O at
-    # the end of the phase
+                   "v_mul_f32 %s, %%[c], %s" % (vr(T_MX0), vr(T_MX0))])
+    return groups
+
+
+def first_max(sbase, m):
+    """m = max(m, the tile's row max) for the first tile of a run, after its
+    masks, where m is still the initial -1e30 and O and l are zero: the
+    common path then keeps every weight of the tile at most 1.  (Past the
+    last tile the olive flag reads as a run start too; the scores are all
+    masked there and m stays.)"""
+    return [x for grp in rowmax_ops(sbase) for x in grp] + ["v_max_f32 %s, %s, %s" % (m, m, vr(T_MX0))]
+
+
+def exact_ops(sbase, m, l, tag):
+    """The row max (rowmax_ops) and the lazy move of m: only when some
+    lane's tile max exceeds it by more than 8, then l *= alpha now, O at the
+    end of the phase (S_FLAG)."""
+    groups = rowmax_ops(sbase)
+    groups.append(["v_add_f32 %s, 0x41000000, %s" % (vr(T_THR), m)])
     lbl = ".Lnr%s_%%=" % tag
     groups.append(["v_cmp_gt_f32 vcc, %s, %s" % (vr(T_MX0), vr(T_THR)),
                    "s_cbranch_vccz %s" % lbl,
@@ -166,29 +244,6 @@ def softmax_ops(qh, sbase, pbase, m, l, tag):
                    "s_nop 1",
                    "v_mul_f32 %s, %s, %s" % (l, l, vr(T_ALPHA)),
                    "%s:" % lbl])
-    # p = 2^(s c - m), in place; P packed to bf16; l += p in fp32 (v_add:
-    # the dot-product form of the sum stalls beside the MFMAs on this part).
-    # Pipelined so that every exp result is read at least two instructions
-    # after the exp (transcendental results need a wait state).
-    order = live
-
-    def pack(k):
-        return [["v_cvt_pk_bf16_f32 %s, %s, %s" % (vr(pbase + k), vr(sbase + 2 * k), vr(sbase + 2 * k + 1))],
-                ["v_add_f32 %s, %s, %s" % (l, l, vr(sbase + 2 * k))],
-                ["v_add_f32 %s, %s, %s" % (l, l, vr(sbase + 2 * k + 1))]]
-    for idx, i in enumerate(order):
-        groups.append(["v_fma_f32 %s, %s, %%[c], -%s" % (vr(sbase + i), vr(sbase + i), m)])
-        if idx >= 1:
-            j = order[idx - 1]
-            groups.append(["v_exp_f32 %s, %s" % (vr(sbase + j), vr(sbase + j))])
-        if idx >= 2 and order[idx - 2] % 2 == 1:
-            groups += pack(order[idx - 2] // 2)
-    groups.append(["v_exp_f32 %s, %s" % (vr(sbase + order[-1]), vr(sbase + order[-1]))])
-    if order[-2] % 2 == 1:
-        groups += pack(order[-2] // 2)
-    groups.append(["s_nop 1"])
-    if order[-1] % 2 == 1:
-        groups += pack(order[-1] // 2)
     return groups
 
 
@@ -379,8 +434,8 @@ def light_store_groups():
     columns: those of column group 2 cp + lane/32) and two 16-byte buffer
     stores through the output descriptor, built in S_CB, whose range ends
     at the sequence's last row.  Uses the V operand slots (idle in a score
-    phase) and T_INV, T_RS[0]."""
-    t = T_RS[0]
+    phase) and T_INV, T_MNEW (within one group)."""
+    t = T_MNEW
     groups = [["s_mov_b32 %s, %%[olo]" % sr(S_CB), "s_mov_b32 %s, %%[ohi]" % sr(S_CB + 1),
                "s_mov_b32 %s, %%[onrec]" % sr(S_CB + 2), "s_mov_b32 %s, 0x20000" % sr(S_CB + 3)]]
     for qh, l in ((0, "%[l0n]"), (1, "%[l1n]")):
@@ -600,8 +655,10 @@ def book_next(par):
         ["s_lshr_b32 %s, %s, 1" % (NZ, T0), "s_cmp_eq_u32 %s, %s" % (NZ, B0), "s_cselect_b32 %s, 1, 0" % NZ,
          "s_or_b32 %s, %s, %s" % (NY, NY, NZ), "s_cmp_eq_u32 %[copy], 0",
          "s_cselect_b32 %s, 0, %s" % (NY, NY), "s_or_b32 %s, %s, %s" % (sr(S_SPEC), sr(S_SPEC), NY)],
-        # variant codes: masks needed (and for the PV phase, its products)
-        ["s_mov_b32 %s, %s" % (sr(S_CS), KS), "s_mov_b32 %s, %s" % (sr(S_CP), KP)],
+        # variant codes: masks needed (and for the PV phase, its products),
+        # + 8 for the first tile of a run (its max starts the running max)
+        ["s_cmp_eq_u32 %s, 0" % sr(r["OS"]), "s_cselect_b32 %s, 8, 0" % NY, "s_or_b32 %s, %s, %s" % (sr(S_CS), KS, NY),
+         "s_cmp_eq_u32 %s, 0" % OP, "s_cselect_b32 %s, 8, 0" % NY, "s_or_b32 %s, %s, %s" % (sr(S_CP), KP, NY)],
     ]
 
 
@@ -764,9 +821,13 @@ def score_mask_part(par):
     r = roles(par)
     out += mask_ops('m', 1, s_bank(par)) + ["s_branch %s" % L("smend"), "%s:" % L("ssd")]
     out += diag_mask(1, s_bank(par), r["T0"], r["B0"], "s%d" % par)
+    # the first tile of a run starts the running max of half 1
+    out += ["%s:" % L("smend"),
+            "s_cmp_eq_u32 %s, 0" % sr(r["OS"]),
+            "s_cbranch_scc0 %s" % L("snf")] + first_max(s_bank(par), "%[m1v]") + ["%s:" % L("snf")]
     # the lower group's first heavy iteration (g == gt + 1) takes the score
     # phase that also stores the light block
-    out += ["%s:" % L("smend"),
+    out += [
             "s_add_i32 %s, %%[gt], 1" % sr(S_X),
             "s_cmp_eq_u32 %s, %s" % (sr(S_G), sr(S_X)),
             "s_cbranch_scc1 %s" % L("sst")]
@@ -820,7 +881,10 @@ def pv_mask_part(par):
     r = roles(par)
     out += mask_ops('m', 0, V_SA) + ["s_branch %s" % L("psv"), "%s:" % L("psd")]
     out += diag_mask(0, V_SA, r["T1"], r["B1"], "p%d" % par)
+    # the first tile of a run starts the running max of half 0
     out += ["%s:" % L("psv"),
+            "s_cmp_eq_u32 %s, 0" % sr(r["OP"]),
+            "s_cbranch_scc0 %s" % L("pnf")] + first_max(V_SA, "%[m0v]") + ["%s:" % L("pnf"),
             "s_cmp_lt_i32 %s, 0" % sr(S_G),
             "s_cbranch_scc1 %s" % L("pre")]
     return out
@@ -883,6 +947,7 @@ def loop_text():
     """Iterations S_G = gstart .. nit-1 (gstart may be -1: the pre-loop
     iteration).  The lower group's light block is stored inside the loop
     (the score phase of iteration gt + 1)."""
+    RARE.clear()
     out = ["s_mov_b32 %s, m0" % sr(S_M0SAVE),
            "s_mov_b32 %s, 0x20000" % sr(S_VK + 3),
            "s_mov_b32 %s, 0x20000" % sr(S_VV + 3),
@@ -903,6 +968,8 @@ def loop_text():
             "s_cbranch_scc0 .Lodd_%=",
             "s_branch .Lend_%="]
     out += slow_paths(1) + slow_paths(0)
+    for blk in RARE:
+        out += blk
     out += [".Lend_%=:",
             "s_mov_b32 m0, %s" % sr(S_M0SAVE)]
     return out
