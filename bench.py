@@ -22,8 +22,12 @@ before the timed region.  Prints one JSON line.
 Context fields (not part of value): cold and warm (median and p99 per
 launch: cold after a 1 GiB fill that evicts L2 and the Infinity Cache before
 every launch, warm back to back), measured_mfma_peak (the bf16 matrix-core
-rate measured in-process by a small MFMA-loop kernel, and value as a
-percentage of it), hbm_copy_measured (a plain 1 GiB device copy),
+rate measured in-process by a small MFMA-loop kernel with random operands,
+and with constant ones, each with its shader clock, and value as a
+percentage of the random-operand rate), kernel_clock (the shader clock over
+the attention kernel's loop and its phase times, from a measurement build
+with per-wave clock stamps) with mfma_peak_at_kernel_clock (the published
+dense rate scaled to that clock), hbm_copy_measured (a plain 1 GiB device copy),
 gemm_bf16_context (a large hipBLASLt bf16 GEMM at the run's clock; it and
 the MFMA peak run before the attention's warm-up, so the timed steps start
 at the clock the matrix cores sustain, not while it ramps up from idle),
@@ -115,37 +119,107 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
 def measured_mfma_peak(blocks=2048, iters=4000, reps=5):
-    """The bf16 MFMA rate measured on this part at the run's clock: the
-    probe library's back-to-back v_mfma_f32_32x32x16_bf16 loop (8
-    independent accumulators per wave, 4 waves per work-group, 8 work-groups
-    per CU), best of a few launches."""
+    """The bf16 MFMA rate measured on this part: the probe library's
+    back-to-back v_mfma_f32_32x32x16_bf16 loop (8 independent accumulators
+    per wave, 4 waves per work-group, 8 work-groups per CU), best of a few
+    launches, with random operands (the power real data draws; the part then
+    runs a lower shader clock) and with constant ones, each with the median
+    shader clock of its work-groups (s_memtime cycles over s_memrealtime
+    time)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "prefill_self_attention_amd", "libpa_mfma_peak.so")
     lib = ctypes.CDLL(path)
-    lib.pa_mfma_peak_run.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pa_mfma_peak_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
     lib.pa_mfma_peak_run.restype = ctypes.c_int
     lib.pa_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.pa_mfma_peak_flops.restype = ctypes.c_double
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    best = None
-    for r in range(reps + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        if lib.pa_mfma_peak_run(ctypes.c_void_p(out.data_ptr()), blocks, iters, sp) != 0:
-            raise RuntimeError("mfma peak probe failed to launch")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        if r > 0 and (best is None or ms < best):
-            best = ms
-    tflops = lib.pa_mfma_peak_flops(blocks, iters) / (best * 1e-3) / 1e12
-    return {"tflops": round(tflops, 1), "pct_of_published_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 1),
-            "kernel": "v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wave, %d work-groups of 4 waves" % blocks,
-            "launch_ms": round(best, 3)}
+
+    def run(random_operands):
+        best = None
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if lib.pa_mfma_peak_run(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clk.data_ptr()), blocks, iters,
+                                    random_operands, sp) != 0:
+                raise RuntimeError("mfma peak probe failed to launch")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if r > 0 and (best is None or ms < best[0]):
+                c = clk.view(blocks, 4).cpu()
+                mhz = _median(((c[:, 3] - c[:, 2]).double() / ((c[:, 1] - c[:, 0]).double() / 100.0)).tolist())
+                best = (ms, mhz)
+        tflops = lib.pa_mfma_peak_flops(blocks, iters) / (best[0] * 1e-3) / 1e12
+        return {"tflops": round(tflops, 1), "pct_of_published_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 1),
+                "shader_clock_mhz": round(best[1]), "launch_ms": round(best[0], 3)}
+
+    rnd = run(1)
+    const = run(0)
+    return dict(rnd, operands="random bf16 in [-1, 1), four register sets cycled",
+                kernel="v_mfma_f32_32x32x16_bf16, 8 independent accumulators per wave, %d work-groups of 4 waves"
+                % blocks, constant_operands=const)
+
+
+def kernel_clock(args_fn, n_launch=30):
+    """Shader clock and phase times of the 64-row kernel on this workload:
+    the measurement build of the library (libprefill_attn_clock.so, the same
+    sources with per-wave clock stamps) runs the same varlen call
+    (args_fn() -> the ctypes arguments of prefill_attn_varlen_gqa) n_launch
+    times back to back; from the last launch's stamps: the median (and
+    per-XCD) shader clock over each wave's loop, and the median prologue,
+    loop and epilogue times and the span from the first wave's start to the
+    last wave's end."""
+    import ctypes
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "prefill_self_attention_amd", "libprefill_attn_clock.so")
+    lib = ctypes.CDLL(path)
+    f = lib.prefill_attn_varlen_gqa
+    p_, i32 = ctypes.c_void_p, ctypes.c_int32
+    f.argtypes = [p_, p_, p_, p_, i32, i32, i32, i32, i32, p_, p_, p_, ctypes.c_float, p_]
+    f.restype = ctypes.c_int
+    lib.pa_fwd64_clock_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    lib.pa_fwd64_clock_stamps.restype = ctypes.c_int
+    for _ in range(n_launch):
+        if f(*args_fn()) != 0:
+            raise RuntimeError("clock-stamp build: launch failed")
+    torch.cuda.synchronize()
+    n = 1 << 16
+    buf = np.zeros(8 * n, dtype=np.uint64)
+    if lib.pa_fwd64_clock_stamps(ctypes.c_void_p(buf.ctypes.data), n) != 0:
+        raise RuntimeError("clock-stamp build: copy failed")
+    st = buf.reshape(n, 8).astype(np.int64)
+    idx = np.nonzero(st[:, 0])[0]
+    st = st[idx]
+    if len(st) == 0:
+        return None
+    real = (st[:, :4] - st[:, 0].min()) / 100.0          # microseconds
+    cyc = st[:, 4:]
+    loop_us = real[:, 2] - real[:, 1]
+    mhz = (cyc[:, 2] - cyc[:, 1]) / np.maximum(loop_us, 1e-3)
+    xcd = (idx // 4) % 8
+    return {"waves": int(len(st)),
+            "loop_shader_clock_mhz": {"median": round(float(np.median(mhz))), "min": round(float(mhz.min())),
+                                      "max": round(float(mhz.max())),
+                                      "per_xcd_median": [round(float(np.median(mhz[xcd == x]))) for x in range(8)]},
+            "median_us": {"prologue": round(float(np.median(real[:, 1] - real[:, 0])), 2),
+                          "loop": round(float(np.median(loop_us)), 2),
+                          "epilogue": round(float(np.median(real[:, 3] - real[:, 2])), 2)},
+            "loop_us_min_max": [round(float(loop_us.min()), 2), round(float(loop_us.max()), 2)],
+            "span_first_start_to_last_end_us": round(float(real[:, 3].max()), 2),
+            "library": "libprefill_attn_clock.so (measurement build, per-wave s_memtime / s_memrealtime stamps)"}
 
 
 def read_traffic():
@@ -633,6 +707,14 @@ def main():
 
     msf8 = timed_steps(step_fp8, args.steps, args.warmup)
 
+    # the shader clock the kernel runs at, from the measurement build
+    clock = None
+    if D == 128 and args.workload == "single_T2048_H32_D128":
+        import ctypes
+        clock = kernel_clock(lambda: (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), cu.data_ptr(), len(w.lengths),
+                                      max_seqlen, H, HK, D, kc.data_ptr(), vc.data_ptr(), out.data_ptr(),
+                                      ctypes.c_float(w.scale), None))
+
     # cold: every launch after a 1 GiB fill that evicts L2 and the Infinity Cache
     cold_ms = cold_launch_times(step, min(args.steps, 100))
     # the HBM copy rate this part sustains (a plain 1 GiB device-to-device
@@ -671,6 +753,13 @@ def main():
                  "p99": round(launch_ms[min(len(launch_ms) - 1, int(math.ceil(0.99 * len(launch_ms))) - 1)] * 1e3, 2),
                  "mean_back_to_back": round(ms_per_step * 1e3, 2)},
         "measured_mfma_peak": dict(peak, value_pct_of_it=round(100.0 * value / peak["tflops"], 1)),
+        # the kernel's own shader clock, and the published dense rate scaled
+        # to it (2.5 PFLOP/s at 2.4 GHz)
+        "kernel_clock": clock,
+        "mfma_peak_at_kernel_clock": None if clock is None else {
+            "tflops": round(PEAK_BF16_TFLOPS * clock["loop_shader_clock_mhz"]["median"] / 2400.0, 1),
+            "value_pct_of_it": round(100.0 * value / (PEAK_BF16_TFLOPS * clock["loop_shader_clock_mhz"]["median"]
+                                                      / 2400.0), 1)},
         "kernel_source_sha256": kernel_sha(),
         # cache bytes written per step over the fused step's time: the write's
         # share of the step's HBM traffic, not a bandwidth of its own

@@ -1,6 +1,8 @@
-"""Build libprefill_attn.so (HIP, gfx950) in-tree with hipcc, and the small
-libpa_mfma_peak.so (a matrix-core rate probe the benchmark reports beside
-the attention rate).
+"""Build libprefill_attn.so (HIP, gfx950) in-tree with hipcc, and two
+measurement libraries the benchmark reports beside the attention rate: the
+small libpa_mfma_peak.so (a matrix-core rate probe) and
+libprefill_attn_clock.so (the same sources built with PA_CLOCK_STAMPS: the
+64-row kernel records per-wave clock stamps; never loaded by the product).
 
 Run as ``python -m prefill_self_attention_amd.build`` or call ``build()``.
 Prints a warning for every kernel that uses scratch (private) memory.
@@ -23,6 +25,7 @@ LIB = os.path.join(HERE, "libprefill_attn.so")
 SOURCES = ["api.hip", "prefill_fwd.hip", "splitkv.hip", "fwd64.hip"]
 PEAK_LIB = os.path.join(HERE, "libpa_mfma_peak.so")
 PEAK_SOURCES = ["mfma_peak.hip"]
+CLOCK_LIB = os.path.join(HERE, "libprefill_attn_clock.so")
 ARCH = "gfx950"
 
 
@@ -45,7 +48,7 @@ def scratch_kernels(remarks: str):
     return found
 
 
-def _compile(sources, lib, verbose):
+def _start(sources, lib, verbose, defines=()):
     tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            # no NaN canonicalisation around max/min (inputs are finite by contract)
@@ -54,14 +57,21 @@ def _compile(sources, lib, verbose):
            "-Wno-unused-command-line-argument",
            "-Rpass-analysis=kernel-resource-usage",
            "-I", INCLUDE, "-I", CSRC]
+    cmd += ["-D" + d for d in defines]
     cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(line for line in res.stdout.splitlines()
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return proc, tmp, lib
+
+
+def _finish(job, verbose):
+    proc, tmp, lib = job
+    stdout, _ = proc.communicate()
+    out = "\n".join(line for line in stdout.splitlines()
                     if "packed-fp32-ops" not in line)
-    if res.returncode != 0:
+    if proc.returncode != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + out)
@@ -85,8 +95,18 @@ def _compile(sources, lib, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    _compile(PEAK_SOURCES, PEAK_LIB, verbose)
-    return _compile(SOURCES, LIB, verbose)
+    """Compiles the three libraries at once (separate hipcc processes)."""
+    jobs = [_start(SOURCES, LIB, verbose), _start(PEAK_SOURCES, PEAK_LIB, verbose),
+            _start(SOURCES, CLOCK_LIB, verbose, defines=("PA_CLOCK_STAMPS",))]
+    errors = []
+    for job in jobs:
+        try:
+            _finish(job, verbose)
+        except RuntimeError as e:
+            errors.append(str(e))
+    if errors:
+        raise RuntimeError("\n".join(errors))
+    return LIB
 
 
 if __name__ == "__main__":

@@ -158,6 +158,27 @@ __device__ __forceinline__ void end_interval() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Clock stamps, in the measurement build of the library only (built with
+// PA_CLOCK_STAMPS beside the product library): every wave of the varlen
+// kernel records (s_memrealtime, a fixed 100 MHz counter; s_memtime, shader
+// clock cycles) at its start, after the prologue, after the loop and at its
+// end, in g_fwd64_stamps[8 * (4 * work-group + wave) + i]:
+// i = 0..3 the real times, 4..7 the cycle counts.
+#ifdef PA_CLOCK_STAMPS
+constexpr bool kStamps = true;
+constexpr int64_t kStampWaves = 1 << 16;
+__device__ uint64_t g_fwd64_stamps[8 * kStampWaves];
+#else
+constexpr bool kStamps = false;
+#endif
+struct Stamp {
+  uint64_t real, cycles;
+};
+__device__ __forceinline__ Stamp stamp() {
+  if constexpr (kStamps) return {__builtin_amdgcn_s_memrealtime(), __builtin_amdgcn_s_memtime()};
+  return {0, 0};
+}
+
 // kSplit = false: varlen (keys from k, v; block pairs).  kSplit = true:
 // split-KV items of a chunked call (keys from the cache, which already holds
 // the call's new rows; each group of two waves takes its own unit (item,
@@ -167,6 +188,7 @@ template <bool kSplit>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_fwd64_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  const Stamp st0 = stamp();
   claim_registers();
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -369,6 +391,7 @@ void prefill_fwd64_kernel(FwdParams p) {
           (__attribute__((address_space(3))) void*)(lds + group * kGroupBytes + 1024 * (2 * i + wsub)), 16, fk[i], 0, 0, 0);
   }
   end_interval();
+  const Stamp st1 = stamp();
 
   // ---------------------------------------------------------------- loop
   float m0 = kMInit, l0 = 0.f, m1 = kMInit, l1 = 0.f;   // halves 0 and 1
@@ -444,6 +467,7 @@ void prefill_fwd64_kernel(FwdParams p) {
   wlom1 = __builtin_amdgcn_readfirstlane(wlom1);  // wave-uniform: in-out SGPR operands
   wwid = __builtin_amdgcn_readfirstlane(wwid);
   fwd64_loop(L, m0, l0, m1, l1, m0n, l0n, l1n, wlom1, wwid);
+  const Stamp st2 = stamp();
 
   if constexpr (kSplit) {
     mfma_drain();
@@ -535,9 +559,30 @@ void prefill_fwd64_kernel(FwdParams p) {
     store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
   else
     store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
+#ifdef PA_CLOCK_STAMPS
+  const Stamp st3 = stamp();
+  const int64_t w = 4 * (int64_t)__builtin_amdgcn_workgroup_id_x() + wave;
+  if (lane < 8 && w < kStampWaves) {
+    const Stamp& x = (lane & 3) == 0 ? st0 : (lane & 3) == 1 ? st1 : (lane & 3) == 2 ? st2 : st3;
+    g_fwd64_stamps[8 * w + lane] = lane < 4 ? x.real : x.cycles;
+  }
+#else
+  (void)st0;
+  (void)st1;
+  (void)st2;
+#endif
 }
 
 }  // namespace
+
+#ifdef PA_CLOCK_STAMPS
+// Copies the stamps of the last varlen launch (8 uint64 per wave, waves
+// 4 w + i of work-group w) to host memory; n_waves <= 65536.
+extern "C" int pa_fwd64_clock_stamps(uint64_t* host, int64_t n_waves) {
+  if (!host || n_waves <= 0 || n_waves > kStampWaves) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_fwd64_stamps), 8 * sizeof(uint64_t) * n_waves);
+}
+#endif
 
 bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, int num_heads, int num_kv_heads) {
   // lane offsets within a sequence are 32-bit: rows of q and of k / v
