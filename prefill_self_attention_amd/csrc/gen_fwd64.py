@@ -425,6 +425,20 @@ def loads(par, matrix):
     return groups
 
 
+# of the iteration's 16 loads, the last PV_LOADS go out in the PV phase
+# (before its bookkeeping moves the load descriptors on): the four waves
+# then issue half as many loads at once, and the score phase half as many
+# issue slots (8 of 16 measured best; all 16 in the PV phase is slower)
+PV_LOADS = 8
+
+
+def load_groups(par):
+    """The iteration's load groups, pairs sharing an M0 together: K0 K1 V0 V1
+    K2 K3 ..."""
+    k_l, v_l = loads(par, 'k'), loads(par, 'v')
+    return [x for j in range(0, ROWSTEP_LOADS, 2) for x in (k_l[j], k_l[j + 1], v_l[j], v_l[j + 1])]
+
+
 def light_store_groups():
     """The lower group's finished light block, stored from O during the
     heavy block's first score phase (O is free until that iteration's PV
@@ -484,9 +498,7 @@ def score_phase(par, tag, store=False):
     fill = softmax_ops(1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1")
     if store:
         fill = interleave(fill, light_store_groups())
-    k_l, v_l = loads(par, 'k'), loads(par, 'v')
-    # pairs sharing an M0 stay together: K0 K1 V0 V1 K2 K3 ...
-    loadg = [x for j in range(0, ROWSTEP_LOADS, 2) for x in (k_l[j], k_l[j + 1], v_l[j], v_l[j + 1])]
+    loadg = load_groups(par)[:len(load_groups(par)) - PV_LOADS]
     kslot = (1 - par) * K_SLOT_BYTES          # K(T[g+1]) in slot (g+1) % 2
     nb = s_bank(1 - par)                      # half-1 scores of T[g+1]
     frag_reads = []
@@ -568,8 +580,21 @@ def pv_phase(par, has_pv, tag):
                     pb = (V_PA[par] if qh == 0 else V_PB) + 4 * gg
                     mfmas.append(("%s %s, %s, %s, %s" % (MFMA, ar(o, 16), vr(slot, 4), vr(pb, 4), ar(o, 16)), f))
         body += ["s_nop 1"]   # the weights were written by VALU instructions
-        body += schedule(mfmas, frag_reads, 2, fill, [], prefetched=True)
+        lg = load_groups(par)
+        pv_loads = lg[len(lg) - PV_LOADS:] if PV_LOADS else []
+        sched = schedule(mfmas, frag_reads, 2, fill, pv_loads, prefetched=True)
+        if pv_loads:
+            # the loads read the descriptors before book_fast moves them on
+            last_load = max(i for i, x in enumerate(sched) if x.startswith("buffer_load"))
+            first_move = min(i for i, x in enumerate(sched) if x.startswith("s_add_u32 %s" % sr(S_VK))
+                             or x.startswith("s_add_u32 %s" % sr(S_VV)))
+            assert last_load < first_move, (last_load, first_move)
+        body += sched
     else:
+        # (the pre-loop iteration: its PV-phase loads before the bookkeeping)
+        lg = load_groups(par)
+        for before, after in (lg[len(lg) - PV_LOADS:] if PV_LOADS else []):
+            body += before + ["s_nop 0"] + after
         for g in fill:
             body += g
     body += o_rescale(0, after_mfma=has_pv, tag=tag, olive=roles(par)["OP"])

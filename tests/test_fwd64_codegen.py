@@ -62,9 +62,17 @@ def test_schedule_keeps_every_instruction_once():
                 if not ins.startswith("s_nop"):
                     assert body.count(ins) >= flat.count(ins), ins
             assert sum(1 for x in body if x.startswith("v_mfma")) == 32
-            assert sum(1 for x in body if x.startswith("buffer_load")) == 16
             pv = g.pv_phase(par, True, "t")
             assert sum(1 for x in pv if x.startswith("v_mfma")) == 32
+            # the iteration's 16 loads: split between the two phases, each
+            # load exactly once, and the PV-less phase of the pre-loop
+            # iteration issues the PV phase's share too
+            loads = sorted(x for x in body + pv if x.startswith("buffer_load"))
+            want = sorted(x for pair in g.load_groups(par) for x in pair[1])
+            assert loads == want and len(loads) == 16
+            pre = g.pv_phase(par, False, "t")
+            assert sorted(x for x in pre if x.startswith("buffer_load")) == \
+                sorted(x for x in pv if x.startswith("buffer_load"))
             # the PV phase's V fragments: its first ones read at the end of
             # the score phase, after its last LDS wait, the rest in the phase
             hoisted = [x for x in body if x.startswith("ds_read_b64_tr_b16")]
