@@ -29,14 +29,19 @@
 //    instruction, so the matrix cores and the vector ALU work at the same
 //    time in one wave; the next tiles' global-to-LDS loads are spread between
 //    the MFMAs as well.
-//  * The softmax is the one of prefill_fwd.hip (exp2 domain, lazy rescale by
-//    more than 2^8, causal masking on the diagonal tile only); the running
-//    sum adds the bf16-rounded weights that the PV product uses.
+//  * The softmax works in the exp2 domain with a lazily moved running max,
+//    as prefill_fwd.hip's does, but the common path takes a tile's weights
+//    against the running max without the tile's own max (any max gives the
+//    same O / l when O and l share it) and checks their sum; the first tile
+//    of a run starts the running max, and a sum past its bound takes the
+//    exact update out of line.  Causal masking on the diagonal tiles only;
+//    the running sum adds the fp32 weights.
 //  * Work split as in prefill_fwd.hip: a work-group takes the block pair
 //    (z, n-1-z) of one (sequence, head); two waves (the upper group) walk the
-//    heavy block's first tiles, the other two the light block and then the
-//    heavy block's remaining tiles, and the heavy block's two partial states
-//    are merged through LDS at the end.  Each group keeps its K and V tiles
+//    heavy block's first tiles, the other two the light block (stored
+//    inside the loop, during the heavy block's first score phase) and then
+//    the heavy block's remaining tiles, and the heavy block's two partial
+//    states are merged through LDS at the end.  Each group keeps its K and V tiles
 //    in LDS rings of two (64 KB per group).
 //  * Tiles that hold a block's own tokens are copied from LDS to the cache
 //    with 16-byte streaming stores, every token once.

@@ -26,13 +26,17 @@ kernel never uses them outside these statements):
 
 Iteration g of the loop (T[g]: the g-th key tile of the wave's group):
 score phase: S(T[g+1]) = K Q^T on 32 MFMAs (both query halves share each K
-fragment read from LDS) beside the softmax of T[g] for rows 32..63, plus the
-loads of K(T[g+2]) and V(T[g+1]); cache copies of the tiles' own rows; PV
-phase: O^T += V^T P^T for T[g] on 32 MFMAs (both halves share each V
-fragment) beside the softmax of T[g+1] for rows 0..31; then a barrier.  The
-VALU work is spread over the MFMA slots by an issue-cost model measured on
-this part (an MFMA every 32 cycles leaves about 19 cycles of issue for other
-instructions of the same wave).
+fragment read from LDS) beside the softmax of T[g] for rows 32..63 and half
+of the loads of K(T[g+2]) and V(T[g+1]), ending with the reads of the PV
+phase's first V fragments; PV phase: O^T += V^T P^T for T[g] on 32 MFMAs
+(both halves share each V fragment) beside the softmax of T[g+1] for rows
+0..31, the other half of the loads and the next iteration's bookkeeping;
+then a barrier.  What only some iterations need (masks, cache copies of the
+tiles' own rows, the first tile of a run, the lower group's switch from the
+light to the heavy block) sits behind one guard branch before each phase.
+The VALU work is spread over the MFMA slots by an issue-cost model measured
+on this part (an MFMA every 32 cycles leaves about 19 cycles of issue for
+other instructions of the same wave).
 """
 from __future__ import annotations
 
