@@ -533,6 +533,20 @@ def score_phase(par, tag, store=False):
     return body
 
 
+def score_phase_last(par, tag):
+    """Score phase of the group's last iteration: no T[g+1] to score and no
+    tile to load, only the softmax of T[g] for rows 32..63 and, at the end,
+    the reads of the PV phase's first V fragments."""
+    body = ["v_mov_b32 %s, 0xff800000" % vr(T_NINF),
+            "s_mov_b32 %s, 0" % sr(S_FLAG)]
+    for grp in softmax_ops(1, s_bank(par), V_PB, "%[m1v]", "%[l1v]", tag + "h1"):
+        body += grp
+    body += o_rescale(1, after_mfma=False, tag=tag, olive=roles(par)["OS"])
+    for grp in pv_frag_reads(par)[:LOOKAHEAD]:
+        body += grp
+    return body
+
+
 def interleave(main, extra):
     """The groups of main with those of extra spread evenly among them."""
     if not main:
@@ -685,8 +699,10 @@ def book_next(par):
          "s_or_b32 %s, %s, %s" % (NY, NY, NZ), "s_cmp_eq_u32 %[copy], 0",
          "s_cselect_b32 %s, 0, %s" % (NY, NY), "s_or_b32 %s, %s, %s" % (sr(S_SPEC), sr(S_SPEC), NY)],
         # variant codes: masks needed (and for the PV phase, its products),
-        # + 8 for the first tile of a run (its max starts the running max)
+        # + 8 for the first tile of a run (its max starts the running max);
+        # the score phase + 16 when there is no T[h+1] to score
         ["s_cmp_eq_u32 %s, 0" % sr(r["OS"]), "s_cselect_b32 %s, 8, 0" % NY, "s_or_b32 %s, %s, %s" % (sr(S_CS), KS, NY),
+         "s_cmp_eq_u32 %s, 3" % KP, "s_cselect_b32 %s, 16, 0" % NY, "s_or_b32 %s, %s, %s" % (sr(S_CS), sr(S_CS), NY),
          "s_cmp_eq_u32 %s, 0" % OP, "s_cselect_b32 %s, 8, 0" % NY, "s_or_b32 %s, %s, %s" % (sr(S_CP), KP, NY)],
     ]
 
@@ -855,11 +871,14 @@ def score_mask_part(par):
             "s_cmp_eq_u32 %s, 0" % sr(r["OS"]),
             "s_cbranch_scc0 %s" % L("snf")] + first_max(s_bank(par), "%[m1v]") + ["%s:" % L("snf")]
     # the lower group's first heavy iteration (g == gt + 1) takes the score
-    # phase that also stores the light block
+    # phase that also stores the light block; the group's last iteration
+    # (no T[g+1]) the one without score products and loads
     out += [
             "s_add_i32 %s, %%[gt], 1" % sr(S_X),
             "s_cmp_eq_u32 %s, %s" % (sr(S_G), sr(S_X)),
-            "s_cbranch_scc1 %s" % L("sst")]
+            "s_cbranch_scc1 %s" % L("sst"),
+            "s_cmp_eq_u32 %s, 3" % sr(r["KP"]),
+            "s_cbranch_scc1 %s" % L("snm")]
     return out
 
 
@@ -962,6 +981,7 @@ def slow_paths(par):
     P = "p%d" % par
     out = ["%s:" % L("pre")] + pv_phase(par, False, "q" + P) + ["s_branch %s" % L("pdone")]
     out += ["%s:" % L("sst")] + score_phase(par, "t" + P, store=True) + ["s_branch %s" % L("sdn")]
+    out += ["%s:" % L("snm")] + score_phase_last(par, "u" + P) + ["s_branch %s" % L("sdn")]
     return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
