@@ -547,6 +547,23 @@ def score_phase_last(par, tag):
     return body
 
 
+def pv_phase_last(par):
+    """PV phase of the group's last iteration: the products of T[g] alone
+    (there is no T[g+1] to take the softmax of, no tile to load and no next
+    iteration to keep books for)."""
+    frag_reads = pv_frag_reads(par)
+    mfmas = []
+    for gg in range(4):
+        for db in range(4):
+            f = 4 * gg + db
+            slot = V_VF + 4 * (f % 4)
+            for qh in range(2):
+                o = A_O + 16 * (4 * qh + db)
+                pb = (V_PA[par] if qh == 0 else V_PB) + 4 * gg
+                mfmas.append(("%s %s, %s, %s, %s" % (MFMA, ar(o, 16), vr(slot, 4), vr(pb, 4), ar(o, 16)), f))
+    return ["s_nop 1"] + schedule(mfmas, frag_reads, 2, [], [], prefetched=True)
+
+
 def interleave(main, extra):
     """The groups of main with those of extra spread evenly among them."""
     if not main:
@@ -921,6 +938,9 @@ def pv_mask_part(par):
     KP = sr(roles(par)["KP"])
     out = ["s_cmp_eq_u32 %s, 0" % sr(S_CP),
            "s_cbranch_scc1 %s" % L("pgo"),
+           # the group's last iteration: no T[g+1], so no softmax and no loads
+           "s_cmp_eq_u32 %s, 3" % KP,
+           "s_cbranch_scc1 %s" % L("pnm"),
            "s_nop 7", "s_nop 7", "s_nop 7",
            "s_cmp_eq_u32 %s, 1" % KP,
            "s_cbranch_scc1 %s" % L("psd"),
@@ -982,6 +1002,7 @@ def slow_paths(par):
     out = ["%s:" % L("pre")] + pv_phase(par, False, "q" + P) + ["s_branch %s" % L("pdone")]
     out += ["%s:" % L("sst")] + score_phase(par, "t" + P, store=True) + ["s_branch %s" % L("sdn")]
     out += ["%s:" % L("snm")] + score_phase_last(par, "u" + P) + ["s_branch %s" % L("sdn")]
+    out += ["%s:" % L("pnm")] + pv_phase_last(par) + ["s_branch %s" % L("pdone")]
     return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
