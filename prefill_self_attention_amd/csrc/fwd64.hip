@@ -82,13 +82,12 @@ constexpr float kMInit = -1.0e30f;
 // Operands of the main loop (see gen_fwd64.py): wave-uniform values first.
 struct Fwd64Loop {
   float c;            // |scale| * log2(e) > 0
-  int32_t gstart;     // first iteration to run (-1: the pre-loop iteration)
   int32_t nit;        // iterations of the work-group (the upper group's tiles)
   int32_t nmy;        // tiles of this wave's group
   int32_t elo;        // tiles of the first run (lower group: the light block)
   int32_t jump;       // tile index minus position in the second run
   int32_t blk0, blk1; // query block of the first / second run
-  int32_t r0p, r0p1, r0p63;  // key position of the wave's first row less 128 x block (+1, +63)
+  int32_t r0p;        // key position of the wave's first row less 128 x block
   int32_t len;        // sequence length
   int32_t gt;         // lower group's last light position (-2: none)
   int32_t wlom1b, wwidb;  // bookkeeping window of the second run (lower group after the transition)
@@ -308,8 +307,6 @@ void prefill_fwd64_kernel(FwdParams p) {
   L.blk0 = (upper || !has_lo) ? qb_hi : z;
   L.blk1 = qb_hi;
   L.r0p = pfx + 64 * wsub;
-  L.r0p1 = L.r0p + 1;
-  L.r0p63 = L.r0p + 63;
   L.len = len;
   L.gt = transition ? e_lo - 1 : -100;  // -100: never (g >= -1 meets none of gt - 1, gt, gt + 1)
   L.tileb = (uint32_t)kBN * rs;
@@ -452,7 +449,7 @@ void prefill_fwd64_kernel(FwdParams p) {
   // wave copies to the cache, before the block's own tiles.  Encoded as
   // (lo - 1, hi - lo), or an empty window.
   auto window = [&](int x0, int x1, int off, int blk, int32_t& lom1, int32_t& wid) {
-    int hi = min(x1 - 3, ((kBM * blk + L.r0p1) >> 6) - off - 2);
+    int hi = min(x1 - 3, ((kBM * blk + L.r0p + 1) >> 6) - off - 2);
     if (L.copy) hi = min(hi, 2 * blk - off - 2);
     const int lo = x0 + 1;
     lom1 = hi < lo ? INT32_MIN : lo - 1;
@@ -468,7 +465,6 @@ void prefill_fwd64_kernel(FwdParams p) {
   if (transition) window(e_lo, n_my, L.jump, qb_hi, L.wlom1b, L.wwidb);
   // one pass over the iterations: the lower group's light block (when a
   // heavy part follows it) is stored, and O restarted, inside the loop
-  L.gstart = -1;
   wlom1 = __builtin_amdgcn_readfirstlane(wlom1);  // wave-uniform: in-out SGPR operands
   wwid = __builtin_amdgcn_readfirstlane(wwid);
   fwd64_loop(L, m0, l0, m1, l1, m0n, l0n, l1n, wlom1, wwid);

@@ -654,12 +654,12 @@ def kind_of(t, b, dst, tmp=S_Y):
     and tiles above (R0 + 63) / 64 wholly hidden (one tile in between when
     R0 is a multiple of 64, two otherwise)."""
     return ["s_lshl_b32 %s, %s, 7" % (sr(tmp), sr(b)),
-            "s_add_i32 %s, %s, %%[r0p1]" % (sr(tmp), sr(tmp)),
-            "s_lshr_b32 %s, %s, 6" % (sr(tmp), sr(tmp)),
-            "s_cmp_lt_i32 %s, %s" % (sr(t), sr(tmp)),
+            "s_add_i32 %s, %s, %%[r0p]" % (sr(tmp), sr(tmp)),
+            "s_add_i32 %s, %s, 1" % (sr(tmp), sr(tmp)),         # R0 + 1
+            "s_lshr_b32 %s, %s, 6" % (sr(dst), sr(tmp)),
+            "s_cmp_lt_i32 %s, %s" % (sr(t), sr(dst)),
             "s_cselect_b32 %s, 0, 1" % sr(dst),
-            "s_lshl_b32 %s, %s, 7" % (sr(tmp), sr(b)),
-            "s_add_i32 %s, %s, %%[r0p63]" % (sr(tmp), sr(tmp)),
+            "s_add_i32 %s, %s, 62" % (sr(tmp), sr(tmp)),        # R0 + 63
             "s_lshr_b32 %s, %s, 6" % (sr(tmp), sr(tmp)),
             "s_cmp_gt_i32 %s, %s" % (sr(t), sr(tmp)),
             "s_cselect_b32 %s, 2, %s" % (sr(dst), sr(dst))]
@@ -1006,7 +1006,7 @@ def slow_paths(par):
     return out + book_slow(par, "p" + P) + book_slow(par, "q" + P)
 
 
-LOOP_SGPR_IN = ["gstart", "nit", "nmy", "elo", "jump", "blk0", "blk1", "r0p", "r0p1", "r0p63", "len", "gt",
+LOOP_SGPR_IN = ["nit", "nmy", "elo", "jump", "blk0", "blk1", "r0p", "len", "gt",
                 "wlom1b", "wwidb", "olo", "ohi", "onrec",
                 "tileb", "nrec", "m0b", "kbl", "kbh", "vbl", "vbh", "copy", "kcl", "kch", "vcl", "vch"]
 LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "fk3", "fk4", "fk5",
@@ -1014,18 +1014,15 @@ LOOP_VGPR_IN = ["kb0", "kb1", "kb2", "kb3", "vb0", "vb1", "fk0", "fk1", "fk2", "
 
 
 def loop_text():
-    """Iterations S_G = gstart .. nit-1 (gstart may be -1: the pre-loop
-    iteration).  The lower group's light block is stored inside the loop
-    (the score phase of iteration gt + 1)."""
+    """Iterations S_G = -1 (the pre-loop iteration: the scores of T[0]) ..
+    nit-1.  The lower group's light block is stored inside the loop (the
+    score phase of iteration gt + 1)."""
     RARE.clear()
     out = ["s_mov_b32 %s, m0" % sr(S_M0SAVE),
            "s_mov_b32 %s, 0x20000" % sr(S_VK + 3),
            "s_mov_b32 %s, 0x20000" % sr(S_VV + 3),
-           "s_mov_b32 %s, %%[gstart]" % sr(S_G),
-           "s_bitcmp1_b32 %s, 0" % sr(S_G),
-           "s_cbranch_scc0 .Lentry0_%="]
-    out += book_entry(1) + ["s_branch .Lodd_%="]
-    out += [".Lentry0_%=:"] + book_entry(0) + ["s_branch .Leven_%="]
+           "s_mov_b32 %s, -1" % sr(S_G)]
+    out += book_entry(1)    # -1 is odd
     out += [".Lodd_%=:"]
     out += body(1)
     out += ["s_add_i32 %s, %s, 1" % (sr(S_G), sr(S_G)),
@@ -1050,7 +1047,7 @@ SGPR_CLOBBERS = ", ".join('"s%d"' % r for r in NUM_SGPR_FIXED)
 
 
 def loop_function():
-    lines = ["// Main loop: iterations gstart .. nit-1 of this wave (see gen_fwd64.py).",
+    lines = ["// Main loop: iterations -1 .. nit-1 of this wave (see gen_fwd64.py).",
              "// wlom1, wwid: the bookkeeping window of the first run (moved to the",
              "// second run's, wlom1b and wwidb, at the lower group's transition).",
              "__device__ __forceinline__ void fwd64_loop(const Fwd64Loop& L, float& m0v, float& l0v, float& m1v,",
