@@ -174,10 +174,11 @@ def softmax_ops(qh, sbase, pbase, m, l, tag):
     common path takes p = 2^(s c - m) against the running max without
     the tile's max, and checks the lane's sum of the tile's 32 weights: at
     most 2^16 (no weight above it: O and l stay far from overflow) and the
-    tile is done.  Otherwise (the row's first tile, where m is still the
-    initial -1e30, or a tile whose scores pass m by more than about 11) the
-    exact path out of line takes the tile's row max as in the textbook
-    update, moves m when the max exceeds it by more than 8, sets S_FLAG and
+    tile is done.  The first tile of a run has its row max taken before the
+    phase (first_max, in the block that masks it), so the sum passes the
+    bound only where a tile's scores pass m by more than about 11 (or m is
+    still the initial -1e30); then the exact path out of line takes the
+    tile's row max as in the textbook update, moves m when the max exceeds it by more than 8, sets S_FLAG and
     rescales l (O is rescaled at the end of the phase), recomputes the
     weights from the scores, which the common path left intact, and
     returns.
