@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "quant_rows.h"
 #include "prefill_attn.h"
 
 namespace {
@@ -174,15 +175,20 @@ pa_status run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int
   p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * 1.4426950408889634, 0x1p-100);
   p.neg_q = scale < 0.f ? 1 : 0;
   hipError_t e;
+  const bool rows64 =
+      pa::fwd64_supported(head_dim, prefix != nullptr, scale, max_seqlen, num_heads, num_kv_heads) && fwd64_enabled();
   if (qc) {
     p.kq = static_cast<int8_t*>(qc->kq);
     p.vq = static_cast<int8_t*>(qc->vq);
     p.ks = qc->ks;
     p.vs = qc->vs;
-    e = qc->fp8 ? pa::launch_prefill_fwd_fp8(p, num_seqs, head_dim, stream)
-                : pa::launch_prefill_fwd_int8(p, num_seqs, head_dim, stream);
-  } else if (pa::fwd64_supported(head_dim, prefix != nullptr, scale, max_seqlen, num_heads, num_kv_heads) && fwd64_enabled()) {
-    e = pa::launch_prefill_fwd64(p, num_seqs, stream);
+    if (rows64)
+      e = pa::launch_prefill_fwd64(p, num_seqs, qc->fp8 ? pa::qrow::kCacheFp8 : pa::qrow::kCacheInt8, stream);
+    else
+      e = qc->fp8 ? pa::launch_prefill_fwd_fp8(p, num_seqs, head_dim, stream)
+                  : pa::launch_prefill_fwd_int8(p, num_seqs, head_dim, stream);
+  } else if (rows64) {
+    e = pa::launch_prefill_fwd64(p, num_seqs, pa::qrow::kCacheBf16, stream);
   } else {
     e = pa::launch_prefill_fwd(p, num_seqs, head_dim, prefix != nullptr, stream);
   }

@@ -46,14 +46,18 @@
 //  * Tiles that hold a block's own tokens are copied from LDS to the cache
 //    with 16-byte streaming stores, every token once.
 //
-// Runs for varlen calls with head_dim 128, a bf16 cache and a non-negative
-// scale; api.hip sends every other case to prefill_fwd_kernel.
+// Runs for varlen calls with head_dim 128 and a non-negative scale; api.hip
+// sends every other case to prefill_fwd_kernel.  With an INT8 or FP8 cache the
+// loop copies nothing: after the output rows each wave quantises its share of
+// the work-group's own rows, read again from k and v (quant_rows.h holds the
+// rule, shared with prefill_fwd_kernel, so the codes and scales are the same).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
 
 #include "launch.h"
+#include "quant_rows.h"
 
 namespace pa {
 namespace {
@@ -183,14 +187,59 @@ __device__ __forceinline__ Stamp stamp() {
   return {0, 0};
 }
 
+// The INT8 or FP8 cache rows of query block blk that wave `wave` writes: its
+// 32 rows 32 wave .. 32 wave + 31 of the block, 16 lanes per row with 8
+// values each, K and V read again from k and v (the loop has just read them,
+// so they come from L2 or the Infinity Cache).  Rows past the sequence read
+// its last row, so that every lane takes part in the row maximum, and store
+// nothing.
+template <int kCache>
+__device__ __forceinline__ void quantize_block_rows(const uint16_t* kin, const uint16_t* vin, int64_t row_stride,
+                                                    int8_t* kq, int8_t* vq, float* ks, float* vs,
+                                                    int64_t cache_base, int blk, int len, int wave, int lane) {
+  const int ch = lane & 15;
+  const int r0 = blk * kBM + 32 * wave + (lane >> 4);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    qrow::u32x4_t kr[4], vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = min(r0 + 16 * half + 4 * i, len - 1);
+      kr[i] = *reinterpret_cast<const qrow::u32x4_t*>(kin + row * row_stride + 8 * ch);
+      vr[i] = *reinterpret_cast<const qrow::u32x4_t*>(vin + row * row_stride + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 16 * half + 4 * i;
+      const float ka = qrow::group_max<16>(qrow::absmax8(kr[i]));
+      const float va = qrow::group_max<16>(qrow::absmax8(vr[i]));
+      if (row < len) {
+        const int64_t dst = cache_base + (int64_t)row * kD + 8 * ch;
+        if constexpr (kCache == qrow::kCacheInt8) {
+          __builtin_nontemporal_store(qrow::quantize8(kr[i], ka), (qrow::u32x2_t*)(kq + dst));
+          __builtin_nontemporal_store(qrow::quantize8(vr[i], va), (qrow::u32x2_t*)(vq + dst));
+        } else {
+          __builtin_nontemporal_store(qrow::quantize_fp8(kr[i], ka), (qrow::u32x2_t*)(kq + dst));
+          __builtin_nontemporal_store(qrow::quantize_fp8(vr[i], va), (qrow::u32x2_t*)(vq + dst));
+        }
+        if (ch == 0) {
+          ks[cache_base / kD + row] = kCache == qrow::kCacheInt8 ? qrow::int8_scale(ka) : qrow::fp8_scale(ka);
+          vs[cache_base / kD + row] = kCache == qrow::kCacheInt8 ? qrow::int8_scale(va) : qrow::fp8_scale(va);
+        }
+      }
+    }
+  }
+}
+
 // kSplit = false: varlen (keys from k, v; block pairs).  kSplit = true:
 // split-KV items of a chunked call (keys from the cache, which already holds
 // the call's new rows; each group of two waves takes its own unit (item,
 // head) and writes a partial result when the item's block has several
-// segments).
-template <bool kSplit>
+// segments).  kCache: the varlen cache format (bf16, INT8 or FP8).
+template <bool kSplit, int kCache>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_fwd64_kernel(FwdParams p) {
+  static_assert(!kSplit || kCache == qrow::kCacheBf16, "the split-KV items write no cache");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   const Stamp st0 = stamp();
   claim_registers();
@@ -317,13 +366,24 @@ void prefill_fwd64_kernel(FwdParams p) {
   L.kbh = (uint32_t)((uintptr_t)kin >> 32);
   L.vbl = (uint32_t)(uintptr_t)vin;
   L.vbh = (uint32_t)((uintptr_t)vin >> 32);
-  L.copy = writes_cache ? 1u : 0u;
+  L.copy = writes_cache && kCache == qrow::kCacheBf16 ? 1u : 0u;
   uint16_t* kc = kSplit ? p.kc : p.kc + cache_base;  // the copy (varlen only) writes these
   uint16_t* vc = kSplit ? p.vc : p.vc + cache_base;
-  L.kcl = (uint32_t)(uintptr_t)kc;
-  L.kch = (uint32_t)((uintptr_t)kc >> 32);
-  L.vcl = (uint32_t)(uintptr_t)vc;
-  L.vch = (uint32_t)((uintptr_t)vc >> 32);
+  if constexpr (kCache == qrow::kCacheBf16) {
+    L.kcl = (uint32_t)(uintptr_t)kc;
+    L.kch = (uint32_t)((uintptr_t)kc >> 32);
+    L.vcl = (uint32_t)(uintptr_t)vc;
+    L.vch = (uint32_t)((uintptr_t)vc >> 32);
+  } else {
+    // the loop copies nothing (copy = 0), so these carry what the
+    // quantisation after the loop needs: the rows' cache offset, whether
+    // this head writes them, and the light block (-1: none).  As operands of
+    // the loop they are held across it at no cost in registers.
+    L.kcl = (uint32_t)cache_base;
+    L.kch = (uint32_t)((uint64_t)cache_base >> 32);
+    L.vcl = writes_cache ? 1u : 0u;
+    L.vch = has_lo ? (uint32_t)z : ~0u;
+  }
   L.qb = p.q + ((int64_t)seq_start * H + h) * kD;
   L.kb0 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 0 + hl);
   L.kb1 = gbase + ql * kRowBytes + 16 * chunk_slot(ql, 2 + hl);
@@ -511,10 +571,37 @@ void prefill_fwd64_kernel(FwdParams p) {
   // lower group holds the heavy block's remaining tiles (n_lo > e_lo) or
   // only the light block; the upper group the heavy block's first tiles
   const bool merge = n_lo > e_lo;
+  // the quantised cache rows of the work-group's blocks (the heavy block, and
+  // the light one when it has its own), after the output rows
+  auto quantize_own = [&]() __attribute__((always_inline)) {
+    if constexpr (kCache != qrow::kCacheBf16) {
+      if (sgpr_u32(L.vcl) != 0) {
+        // Everything comes from the loop's own operands (held across it
+        // anyway) and from the kernel arguments read again here, through a
+        // pointer the compiler cannot trace back to the prologue: nothing more
+        // stays in scalar registers across the loop.
+        const FwdParams* kp = (const FwdParams*)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kp));
+        const auto u64 = [](uint32_t lo, uint32_t hi) { return (uint64_t)sgpr_u32(hi) << 32 | sgpr_u32(lo); };
+        const uint16_t* kq_in = reinterpret_cast<const uint16_t*>(u64(L.kbl, L.kbh));
+        const uint16_t* vq_in = reinterpret_cast<const uint16_t*>(u64(L.vbl, L.vbh));
+        const int64_t stride = sgpr_u32(L.tileb) / (2 * kBN);  // elements between keys
+        const int64_t cbase = (int64_t)u64(L.kcl, L.kch);
+        const int n = (int)sgpr_u32(L.len);
+        const int light = (int)sgpr_u32(L.vch);
+        quantize_block_rows<kCache>(kq_in, vq_in, stride, kp->kq, kp->vq, kp->ks, kp->vs, cbase, (int)sgpr_u32(L.blk1),
+                                    n, wave, lane);
+        if (light >= 0)
+          quantize_block_rows<kCache>(kq_in, vq_in, stride, kp->kq, kp->vq, kp->ks, kp->vs, cbase, light, n, wave,
+                                      lane);
+      }
+    }
+  };
   mfma_drain();
   if (!merge) {
     if (upper) store_rows(qb_hi, l0, l1, o_get);
     else if (n_lo > 0) store_rows(z, l0, l1, o_get);
+    quantize_own();
     return;
   }
   // the two waves holding the same rows (upper and lower, same wsub) each
@@ -560,6 +647,7 @@ void prefill_fwd64_kernel(FwdParams p) {
     store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
   else
     store_cols(qb_hi, la0, la1, merged, std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
+  quantize_own();
 #ifdef PA_CLOCK_STAMPS
   const Stamp st3 = stamp();
   const int64_t w = 4 * (int64_t)__builtin_amdgcn_workgroup_id_x() + wave;
@@ -591,14 +679,29 @@ bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, in
   return head_dim == 128 && !chunked && scale >= 0.f && (int64_t)max_seqlen * row_bytes < ((int64_t)1 << 31);
 }
 
-hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream) {
+hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, int cache_format, hipStream_t stream) {
   FwdParams q = p;
   q.num_seqs = num_seqs;
   // units per XCD (8 XCDs), each with grid_z block pairs
   const int64_t per_xcd = ((int64_t)p.num_heads * num_seqs + 7) / 8;
   const int64_t grid = 8 * per_xcd * p.grid_z;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_fwd64_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
+  switch (cache_format) {
+    case qrow::kCacheBf16:
+      hipLaunchKernelGGL((prefill_fwd64_kernel<false, qrow::kCacheBf16>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, q);
+      break;
+    case qrow::kCacheInt8:
+      hipLaunchKernelGGL((prefill_fwd64_kernel<false, qrow::kCacheInt8>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, q);
+      break;
+    case qrow::kCacheFp8:
+      hipLaunchKernelGGL((prefill_fwd64_kernel<false, qrow::kCacheFp8>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, q);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -614,7 +717,7 @@ hipError_t launch_prefill_fwd64_split(const FwdParams& p, int64_t max_items, hip
   const int64_t grid = (max_items * p.num_heads + 1) / 2;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_fwd64_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_fwd64_kernel<true, qrow::kCacheBf16>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -62,10 +62,11 @@ int fwd_grid_blocks(int max_seqlen);
 // Enqueue the fused attention + cache-write kernel; returns hipGetLastError().
 hipError_t launch_prefill_fwd(const FwdParams& p, int num_seqs, int head_dim, bool chunked,
                               hipStream_t stream);
-// Varlen, head_dim 128, bf16 cache, scale >= 0: the 64-row-per-wave kernel
-// (fwd64.hip), same grid and contract as launch_prefill_fwd.
+// Varlen, head_dim 128, scale >= 0: the 64-row-per-wave kernel (fwd64.hip),
+// same contract as launch_prefill_fwd (cache_format 0) and as
+// launch_prefill_fwd_int8 / _fp8 (1, 2: p.kq, p.vq, p.ks, p.vs).
 bool fwd64_supported(int head_dim, bool chunked, float scale, int max_seqlen, int num_heads, int num_kv_heads);
-hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, hipStream_t stream);
+hipError_t launch_prefill_fwd64(const FwdParams& p, int num_seqs, int cache_format, hipStream_t stream);
 // Split-KV items of a chunked call on the 64-row kernel: keys (prefix and
 // new) from the cache slab, which the plan launch has filled with the call's
 // new rows first (launch_splitkv_plan with append); partial results to part_o / part_lse when an item's

@@ -90,11 +90,12 @@ def test_fp8_varlen_ragged(H, HK, D):
     check_codes(k, v, cu, kq, vq, ks, vs, "fp8 varlen")
 
 
-def test_fp8_special_rows():
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_special_rows(D):
     """Zero rows (codes keep the sign of x * 0), rows below 2^-100, a wide
     dynamic range reaching the E4M3 subnormals, exact midpoints (amax = 448
     gives scale 1, and values halfway between neighbouring E4M3 codes)."""
-    H, D = 2, 64
+    H = 2
     lengths = [40, 25]
     N = sum(lengths)
     g = I.generator(810)
@@ -107,9 +108,10 @@ def test_fp8_special_rows():
     gen = torch.Generator().manual_seed(811)
     k[6, 0] = (torch.randn(D, generator=gen) * torch.logspace(-30, 6, D)).to(torch.bfloat16)
     # midpoints between neighbouring codes, all exact in bf16 (at most 5
-    # significant bits); 448 first so the scale is exactly 1
+    # significant bits); 448 first so the scale is exactly 1; codes 0x28 ..
+    # 0x7d, again from 0x28 when D - 1 passes them (0x7e is 448, 0x7f NaN)
     mids = [448.0] + [(oracle.e4m3_decode(c) + oracle.e4m3_decode(c + 1)) / 2 * (-1) ** c
-                      for c in range(0x28, 0x28 + D - 1)]
+                      for c in (0x28 + i % 0x55 for i in range(D - 1))]
     ties = torch.tensor(mids)
     k[7, 0] = ties.to(torch.bfloat16)
     v[8, 1] = (-ties).to(torch.bfloat16)

@@ -90,10 +90,11 @@ def test_int8_varlen_ragged(H, HK, D):
     check_codes(k, v, cu, kq, vq, ks, vs, "int8 varlen")
 
 
-def test_int8_special_rows():
+@pytest.mark.parametrize("D", [64, 128])
+def test_int8_special_rows(D):
     """Zero rows, rows below 2^-100, wide dynamic range, exact ties (amax =
     127/64 so 127/amax = 64 and odd multiples of 1/128 land on .5)."""
-    H, D = 2, 64
+    H = 2
     lengths = [40, 25]
     N = sum(lengths)
     g = I.generator(710)
