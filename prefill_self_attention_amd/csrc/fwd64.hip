@@ -99,8 +99,10 @@ struct Fwd64Loop {
   uint32_t nrec;      // bytes from the sequence's first K / V row to the end of its last
   uint32_t m0b;       // LDS address of the wave's first load block in its group
   uint32_t kbl, kbh, vbl, vbh;  // first K / V row of the sequence (this K/V head)
-  uint32_t copy;      // 1: this query head writes the K/V head's cache rows
-  uint32_t kcl, kch, vcl, vch;  // the sequence's cache rows of this K/V head
+  uint32_t copy;      // 1: the loop copies this K/V head's rows to a bf16 cache
+  uint32_t kcl, kch, vcl, vch;  // bf16 cache: the sequence's cache rows of this K/V head; INT8 / FP8 cache (the
+                                // loop copies nothing): the rows' cache offset (kcl, kch), whether this head
+                                // writes them (vcl) and the light block or -1 (vch), for the quantisation
   const uint16_t* qb; // first Q row of the sequence (this head)
   uint32_t kb0, kb1, kb2, kb3;  // LDS read bases of the score operand
   uint32_t vb0, vb1;            // LDS read bases of the PV operand
