@@ -879,16 +879,18 @@ void prefill_fwd_kernel(FwdParams p) {
     // Batching 与算子排布" §3; untitled page www.zwxr.cn/news/300951 §1.2].
     const int len = p.cu[b + 1] - p.cu[b];
     if (len == 1) {
-      if (z == 0) {
+      // in the last z-layer: every layer before it holds only multi-row
+      // sequences' pairs, so those are all dispatched before any decode unit
+      if (z == p.grid_z - 1) {
         float* const red = reinterpret_cast<float*>(fwd_lds<D, kChunked, false, kCache, false, 0>());
         static_assert(dec::red_floats<D, 1, kWaves>() * 4 <= Cfg<D>::kLdsBytes, "decode reduction exceeds LDS");
         dec::decode_unit<D, 1, false, kWaves>(p, (int64_t)h, make_int4(b, 0, 1, 0), red, nullptr, nullptr);
       }
       return;
     }
-    // pairs in reverse order: the last z-layer holds only the longest
+    // pairs in reverse order: the first z-layer holds only the longest
     // sequences' pairs, so the chunk's long blocks are dispatched first and
-    // the decode rows fill the compute units behind them
+    // the decode rows (last layer) fill the compute units behind them
     z = p.grid_z - 1 - z;
   }
   fwd_item<D, kChunked, false, kCache>(p, h, b, z, 0, 1);
